@@ -1,0 +1,481 @@
+// C ABI of the MoE layer: argument validation, workspace carving, the chunk
+// loop and the GEMV/GEMM dispatch.  Host code only; it enqueues kernels on the
+// caller's stream and never allocates device memory, synchronises or reads
+// device data (the optional kernel-timing mode aside, which only records
+// events and synchronises inside moe_profile_read).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr int kDefaultTileRows = 64;
+constexpr int kDefaultGemvMaxRows = 4;
+constexpr int kMaxRowsDecode = 8;
+
+moe_status validate_desc(const moe_layer_desc* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARGUMENT, "desc is null");
+  if (d->group_size != 64) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "group_size must be 64 (got %d)", d->group_size);
+  if (d->hidden <= 0 || d->hidden % 64 || d->hidden > 8192)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "hidden must be a positive multiple of 64 <= 8192 (got %d)", d->hidden);
+  if (d->inter <= 0 || d->inter % 64 || d->inter > 4096)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "inter must be a positive multiple of 64 <= 4096 (got %d)", d->inter);
+  if (d->shared_inter < 0 || d->shared_inter % 64 || d->shared_inter > 4096)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "shared_inter must be 0 or a multiple of 64 <= 4096 (got %d)", d->shared_inter);
+  if (d->n_experts < 1 || d->n_experts > 512)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "n_experts must be in 1..512 (got %d)", d->n_experts);
+  if (d->top_k < 1 || d->top_k > 16) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k must be in 1..16 (got %d)", d->top_k);
+  if (d->top_k > d->n_experts)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "top_k (%d) exceeds n_experts (%d)", d->top_k, d->n_experts);
+  if (d->gemv_max_rows < -1 || d->gemv_max_rows > kMaxRowsDecode)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "gemv_max_rows must be in -1..8 (got %d)", d->gemv_max_rows);
+  if (d->max_chunk < 1 || d->max_chunk > 8192)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "max_chunk must be in 1..8192 (got %d)", d->max_chunk);
+  const int bm = d->tile_rows;
+  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "tile_rows must be 0, 16, 32, 64 or 128 (got %d)", bm);
+  return MOE_OK;
+}
+
+int tile_rows(const moe_layer_desc* d) { return d->tile_rows ? d->tile_rows : kDefaultTileRows; }
+int imax(const moe_layer_desc* d) { return d->inter > d->shared_inter ? d->inter : d->shared_inter; }
+
+int64_t max_tiles_for(const moe_layer_desc* d, int64_t T) {
+  if (T <= 0) return 1;
+  const int64_t BM = tile_rows(d), k = d->top_k, E = d->n_experts;
+  const int64_t tk = T * k;
+  return (tk + BM - 1) / BM + (E < tk ? E : tk) + (d->shared_inter > 0 ? (T + BM - 1) / BM : 0);
+}
+
+struct Blob {
+  int64_t expert_bytes, gateup_bytes, shared_base, shared_gateup_bytes, total;
+};
+
+Blob blob_geom(const moe_layer_desc* d) {
+  const int64_t H = d->hidden, I = d->inter, Is = d->shared_inter, E = d->n_experts;
+  Blob b;
+  b.gateup_bytes = (I / 32) * (H / 64) * 2 * kBlockBytes;
+  b.expert_bytes = b.gateup_bytes + (H / 32) * (I / 64) * kBlockBytes;
+  b.shared_base = E * b.expert_bytes;
+  b.shared_gateup_bytes = (Is / 32) * (H / 64) * 2 * kBlockBytes;
+  b.total = b.shared_base + (Is ? b.shared_gateup_bytes + (H / 32) * (Is / 64) * kBlockBytes : 0);
+  return b;
+}
+
+struct Ws {
+  size_t logits, xsum, ids, tw, counts, offsets, sorted, tiles, n_tiles, active, n_active, hbuf, hsum;
+  size_t total;
+};
+
+size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+
+Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
+  const int64_t E = d->n_experts, k = d->top_k, H = d->hidden, Im = imax(d);
+  const int64_t rows = Tc * k + Tc;
+  Ws w;
+  size_t o = 0;
+  w.logits = o; o += al(Tc * E * 4);
+  w.xsum = o; o += al(Tc * (H / 64) * 4);
+  w.ids = o; o += al(Tc * k * 4);
+  w.tw = o; o += al(Tc * k * 4);
+  w.counts = o; o += al(E * 4);
+  w.offsets = o; o += al((E + 1) * 4);
+  w.sorted = o; o += al(Tc * k * 4);
+  w.tiles = o; o += al(max_tiles_for(d, Tc) * 3 * 4);
+  w.n_tiles = o; o += al(4);
+  w.active = o; o += al(E * 4);
+  w.n_active = o; o += al(4);
+  w.hbuf = o; o += al(rows * Im * 2);
+  w.hsum = o; o += al(rows * (Im / 32) * 4);
+  w.total = o;
+  return w;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+// ---- device check -------------------------------------------------------
+std::mutex g_dev_mu;
+int g_dev_ok[64];  // 0 = unknown, 1 = gfx950, -1 = other
+
+moe_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_dev_ok[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  if (g_dev_ok[dev] != 1) return fail(MOE_ERR_DEVICE_UNSUPPORTED, "device %d is not gfx950", dev);
+  return MOE_OK;
+}
+
+// ---- kernel timing (measurement mode) ----------------------------------------
+constexpr int kNumKernels = 7;
+struct Pending {
+  int kid;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+double g_prof_ms[kNumKernels];
+int g_prof_n[kNumKernels];
+
+hipEvent_t get_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch `fn` (returning hipError_t), bracketed by events when timing is on.
+template <class F>
+moe_status timed(int kid, hipStream_t s, const char* what, F fn) {
+  Pending p{kid, nullptr, nullptr};
+  if (g_prof_on && kid >= 0) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    p.a = get_event();
+    p.b = get_event();
+    if (p.a) (void)hipEventRecord(p.a, s);
+  }
+  hipError_t e = fn();
+  if (g_prof_on && kid >= 0 && p.a && p.b) {
+    (void)hipEventRecord(p.b, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_pending.push_back(p);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+#define TRY(x)                     \
+  do {                             \
+    moe_status _s = (x);           \
+    if (_s != MOE_OK) return _s;   \
+  } while (0)
+
+LayerArgs layer_args(const moe_layer_desc* d, const void* packed) {
+  const Blob b = blob_geom(d);
+  LayerArgs L;
+  L.blob = static_cast<const uint8_t*>(packed);
+  L.H = d->hidden;
+  L.E = d->n_experts;
+  L.k = d->top_k;
+  L.I = d->inter;
+  L.Is = d->shared_inter;
+  L.expert_bytes = b.expert_bytes;
+  L.gateup_bytes = b.gateup_bytes;
+  L.shared_base = b.shared_base;
+  L.shared_gateup_bytes = b.shared_gateup_bytes;
+  return L;
+}
+
+struct RouteOut {
+  int32_t *ids, *counts, *offsets, *sorted, *tiles, *n_tiles, *active, *n_active;
+  float *tw, *logits, *xsum;
+};
+
+moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const float* wr,
+                     const float* bias, const RouteOut& o, hipStream_t s) {
+  const int E = d->n_experts, k = d->top_k, H = d->hidden;
+  TRY(timed(0, s, "router logits", [&] { return launch_logits(x, T, H, wr, bias, E, o.logits, o.xsum, s); }));
+  TRY(timed(1, s, "top-k", [&] { return launch_topk(o.logits, T, E, k, o.ids, o.tw, s); }));
+  TRY(timed(2, s, "routing metadata", [&] {
+    return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, o.counts, o.offsets,
+                       o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, s);
+  }));
+  return MOE_OK;
+}
+
+RouteOut ws_route(void* ws, const Ws& w) {
+  RouteOut o;
+  o.logits = at<float>(ws, w.logits);
+  o.xsum = at<float>(ws, w.xsum);
+  o.ids = at<int32_t>(ws, w.ids);
+  o.tw = at<float>(ws, w.tw);
+  o.counts = at<int32_t>(ws, w.counts);
+  o.offsets = at<int32_t>(ws, w.offsets);
+  o.sorted = at<int32_t>(ws, w.sorted);
+  o.tiles = at<int32_t>(ws, w.tiles);
+  o.n_tiles = at<int32_t>(ws, w.n_tiles);
+  o.active = at<int32_t>(ws, w.active);
+  o.n_active = at<int32_t>(ws, w.n_active);
+  return o;
+}
+
+ChunkArgs chunk_args(const moe_layer_desc* d, const uint16_t* x, int Tc, const RouteOut& o, void* ws,
+                     const Ws& w, float* y) {
+  ChunkArgs C;
+  C.x = x;
+  C.T = Tc;
+  C.Tk = Tc * d->top_k;
+  C.xsum = o.xsum;
+  C.ids = o.ids;
+  C.tw = o.tw;
+  C.counts = o.counts;
+  C.offsets = o.offsets;
+  C.sorted = o.sorted;
+  C.tiles = o.tiles;
+  C.n_tiles = o.n_tiles;
+  C.active = o.active;
+  C.n_active = o.n_active;
+  C.hbuf = at<uint16_t>(ws, w.hbuf);
+  C.hsum = at<float>(ws, w.hsum);
+  C.y = y;
+  C.Imax = imax(d);
+  return C;
+}
+
+moe_status forward_checks(const moe_layer_desc* d, const void* packed, const float* wr,
+                          const uint16_t* x, int32_t T, const float* y, const void* ws,
+                          size_t ws_bytes) {
+  TRY(validate_desc(d));
+  if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %d)", T);
+  if (T == 0) return MOE_OK;
+  if (!packed || !wr || !x || !y || !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  const int64_t Tc = T < d->max_chunk ? T : d->max_chunk;
+  const size_t need = ws_layout(d, Tc).total;
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", ws_bytes, need);
+  return MOE_OK;
+}
+
+moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_t* x, int Tc,
+                      const float* wr, const float* bias, float* y, void* ws, const Ws& w, hipStream_t s) {
+  const RouteOut o = ws_route(ws, w);
+  TRY(run_route(d, x, Tc, wr, bias, o, s));
+  const ChunkArgs C = chunk_args(d, x, Tc, o, ws, w, y);
+  const int mt = (int)max_tiles_for(d, Tc);
+  TRY(timed(-1, s, "zero y", [&] { return launch_fill_zero(y, (int64_t)Tc * d->hidden, s); }));
+  TRY(timed(3, s, "gate/up GEMM", [&] { return launch_gateup_gemm(L, C, mt, s); }));
+  TRY(timed(4, s, "down GEMM", [&] { return launch_down_gemm(L, C, mt, s); }));
+  return MOE_OK;
+}
+
+// The grouped GEMM path over T tokens, max_chunk tokens at a time; the
+// workspace is carved for one chunk and reused (launches are stream-ordered).
+moe_status prefill_loop(const moe_layer_desc* d, const void* packed, const float* wr, const float* bias,
+                        const uint16_t* x, int T, float* y, void* ws, hipStream_t s) {
+  const LayerArgs L = layer_args(d, packed);
+  const int chunk = d->max_chunk;
+  const Ws w = ws_layout(d, T < chunk ? T : chunk);
+  for (int c0 = 0; c0 < T; c0 += chunk) {
+    const int Tc = T - c0 < chunk ? T - c0 : chunk;
+    TRY(gemm_chunk(d, L, x + (int64_t)c0 * d->hidden, Tc, wr, bias, y + (int64_t)c0 * d->hidden, ws, w, s));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_packed_bytes(const moe_layer_desc* desc, size_t* bytes) {
+  TRY(validate_desc(desc));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is null");
+  *bytes = (size_t)blob_geom(desc).total;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_bytes(const moe_layer_desc* desc, int32_t max_tokens, size_t* bytes) {
+  TRY(validate_desc(desc));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is null");
+  if (max_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "max_tokens must be >= 0");
+  const int64_t Tc = max_tokens < desc->max_chunk ? max_tokens : desc->max_chunk;
+  *bytes = ws_layout(desc, Tc > 0 ? Tc : 1).total;
+  return MOE_OK;
+}
+
+moe_status moe_max_tiles(const moe_layer_desc* desc, int32_t T, int32_t* n) {
+  TRY(validate_desc(desc));
+  if (!n) return fail(MOE_ERR_INVALID_ARGUMENT, "n is null");
+  if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0");
+  *n = (int32_t)max_tiles_for(desc, T);
+  return MOE_OK;
+}
+
+int32_t moe_default_gemv_max_rows(void) { return kDefaultGemvMaxRows; }
+
+moe_status moe_pack_weights(const moe_layer_desc* desc, moe_qmatrix gate, moe_qmatrix up,
+                            moe_qmatrix down, moe_qmatrix sh_gate, moe_qmatrix sh_up,
+                            moe_qmatrix sh_down, void* packed, size_t packed_bytes, void* stream) {
+  TRY(validate_desc(desc));
+  const Blob b = blob_geom(desc);
+  auto bad = [](const moe_qmatrix& m) { return !m.codes || !m.scales || !m.biases; };
+  if (!packed || bad(gate) || bad(up) || bad(down))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (desc->shared_inter > 0 && (bad(sh_gate) || bad(sh_up) || bad(sh_down)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null shared-expert pointer");
+  if (packed_bytes < (size_t)b.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "packed buffer %zu bytes < required %lld", packed_bytes,
+                (long long)b.total);
+  TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = desc->hidden, I = desc->inter, Is = desc->shared_inter, E = desc->n_experts;
+  uint8_t* dst = static_cast<uint8_t*>(packed);
+  auto pack = [&](const moe_qmatrix& m, int M, int N, int K, int64_t base, int64_t stride_m,
+                  int64_t stride_nb, int64_t stride_g) -> moe_status {
+    PackArgs P{m.codes, m.scales, m.biases, dst, M, N, K, base, stride_m, stride_nb, stride_g};
+    hipError_t e = launch_pack(P, s);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
+    return MOE_OK;
+  };
+  const int64_t gu_nb = (int64_t)(H / 64) * 2 * kBlockBytes, gu_g = 2 * kBlockBytes;
+  TRY(pack(gate, E, I, H, 0, b.expert_bytes, gu_nb, gu_g));
+  TRY(pack(up, E, I, H, kBlockBytes, b.expert_bytes, gu_nb, gu_g));
+  TRY(pack(down, E, H, I, b.gateup_bytes, b.expert_bytes, (int64_t)(I / 64) * kBlockBytes, kBlockBytes));
+  if (Is > 0) {
+    TRY(pack(sh_gate, 1, Is, H, b.shared_base, 0, gu_nb, gu_g));
+    TRY(pack(sh_up, 1, Is, H, b.shared_base + kBlockBytes, 0, gu_nb, gu_g));
+    TRY(pack(sh_down, 1, H, Is, b.shared_base + b.shared_gateup_bytes, 0,
+             (int64_t)(Is / 64) * kBlockBytes, kBlockBytes));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_layer_desc* desc, const uint16_t* x, int32_t T, const float* router_w,
+                     const float* logit_bias, const moe_routing* out, void* ws, size_t ws_bytes,
+                     void* stream) {
+  TRY(validate_desc(desc));
+  if (T < 0 || T > desc->max_chunk)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "T must be in 0..max_chunk (got %d)", T);
+  if (T == 0) return MOE_OK;
+  if (!x || !router_w || !out || !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!out->topk_ids || !out->topk_weights || !out->expert_counts || !out->expert_offsets ||
+      !out->sorted_assign || !out->tile_map || !out->n_tiles)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null routing output pointer");
+  const Ws w = ws_layout(desc, T);
+  if (ws_bytes < w.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", ws_bytes, w.total);
+  TRY(check_device());
+  RouteOut o = ws_route(ws, w);
+  o.ids = out->topk_ids;
+  o.tw = out->topk_weights;
+  o.counts = out->expert_counts;
+  o.offsets = out->expert_offsets;
+  o.sorted = out->sorted_assign;
+  o.tiles = out->tile_map;
+  o.n_tiles = out->n_tiles;
+  return run_route(desc, x, T, router_w, logit_bias, o, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_forward_prefill(const moe_layer_desc* desc, const void* packed, const float* router_w,
+                               const float* logit_bias, const uint16_t* x, int32_t T, float* y, void* ws,
+                               size_t ws_bytes, void* stream) {
+  TRY(forward_checks(desc, packed, router_w, x, T, y, ws, ws_bytes));
+  if (T == 0) return MOE_OK;
+  TRY(check_device());
+  return prefill_loop(desc, packed, router_w, logit_bias, x, T, y, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, const float* router_w,
+                              const float* logit_bias, const uint16_t* x, int32_t T, float* y, void* ws,
+                              size_t ws_bytes, void* stream) {
+  TRY(forward_checks(desc, packed, router_w, x, T, y, ws, ws_bytes));
+  if (T == 0) return MOE_OK;
+  if (T > kMaxRowsDecode) return fail(MOE_ERR_INVALID_ARGUMENT, "decode takes 1..8 rows (got %d)", T);
+  TRY(check_device());
+  const int R = desc->gemv_max_rows < 0 ? kDefaultGemvMaxRows : desc->gemv_max_rows;
+  const bool gemv = T <= R && T <= desc->max_chunk && (int64_t)T * desc->hidden <= 32768;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!gemv) return prefill_loop(desc, packed, router_w, logit_bias, x, T, y, ws, s);
+  const LayerArgs L = layer_args(desc, packed);
+  const Ws w = ws_layout(desc, T);
+  const RouteOut o = ws_route(ws, w);
+  TRY(run_route(desc, x, T, router_w, logit_bias, o, s));
+  const ChunkArgs C = chunk_args(desc, x, T, o, ws, w, y);
+  TRY(timed(5, s, "gate/up GEMV", [&] { return launch_gemv_gateup(L, C, s); }));
+  TRY(timed(6, s, "down GEMV", [&] { return launch_gemv_down(L, C, s); }));
+  return MOE_OK;
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_DEVICE_UNSUPPORTED: return "MOE_ERR_DEVICE_UNSUPPORTED";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_profile_enable(int32_t on) {
+  g_prof_on = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& p : g_pending) {
+    (void)hipEventSynchronize(p.b);
+    g_event_pool.push_back(p.a);
+    g_event_pool.push_back(p.b);
+  }
+  g_pending.clear();
+  for (int i = 0; i < kNumKernels; i++) {
+    g_prof_ms[i] = 0.0;
+    g_prof_n[i] = 0;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(int32_t kernel_id, double* total_ms, int32_t* launches) {
+  if (kernel_id < 0 || kernel_id >= kNumKernels || !total_ms || !launches)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "bad profile query");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& p : g_pending) {
+    hipError_t e = hipEventSynchronize(p.b);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, p.a, p.b);
+    g_prof_ms[p.kid] += ms;
+    g_prof_n[p.kid] += 1;
+    g_event_pool.push_back(p.a);
+    g_event_pool.push_back(p.b);
+  }
+  g_pending.clear();
+  *total_ms = g_prof_ms[kernel_id];
+  *launches = g_prof_n[kernel_id];
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Device-side definitions shared by the MoE kernels (gfx950 / CDNA4).
+//
+// Packed weight blob.  The canonical format is the pages' 4-bit group-affine
+// one ("Optimizing on-device inference for Apple Silicon", section
+// "Dequantise weights during matrix multiplication": 4-bit codes, one bf16
+// scale and one bf16 bias per 64 weights).  The blob holds the same bytes
+// (0.5625 B per parameter) rearranged into blocks of 32 output rows x 64
+// input columns (one quantisation group):
+//
+//   block = 1024 B of codes + 128 B of (scale, bias)        = 1152 B
+//   codes: 64 lanes x 16 B.  Lane l holds row (l % 32) and the 32 columns
+//          [32*(l/32), 32*(l/32)+32) of the group as 4 dwords; dword c covers
+//          columns 8c..8c+7 of that range with the even columns' codes in
+//          nibbles 0..3 and the odd columns' codes in nibbles 4..7.
+//   scale/bias: 32 dwords, dword r = scale bits | bias bits << 16 for row r.
+//
+// A dword d of codes expands to four bf16 pairs with one AND-OR each:
+//   ((d >> 4i) & 0x000F000F) | 0x43004300 = (bf16(128 + q[2i]), bf16(128 + q[2i+1]))
+// because bf16 0x4300 is 128.0 and the 7 mantissa bits of [128, 256) step by 1.
+// The dot product with the codes then carries an offset 128 * sum(x) that the
+// kernels remove with the group's per-row activation sum:
+//   sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k.
+//
+// Per expert the blob stores gate and up interleaved per (row block, group),
+// then down:
+//   gate/up block (nb, g, which) at ((nb * H/64 + g) * 2 + which) * 1152
+//   down block (nb, g)           at gateup_bytes + (nb * I/64 + g) * 1152
+// Routed experts follow each other with stride expert_bytes; the shared expert
+// (width Is) follows the last routed expert.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 64;
+constexpr int kBlockRows = 32;
+constexpr int kCodeBytes = 1024;
+constexpr int kBlockBytes = 1152;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Blob geometry and per-chunk pointers passed by value to every kernel.
+struct LayerArgs {
+  const uint8_t* blob;
+  int H, E, k, I, Is;
+  int64_t expert_bytes;         // routed expert stride
+  int64_t gateup_bytes;         // routed gate/up region
+  int64_t shared_base;          // byte offset of the shared expert
+  int64_t shared_gateup_bytes;  // shared gate/up region
+};
+
+struct ChunkArgs {
+  const uint16_t* x;      // [T][H] bf16
+  int T;                  // tokens in this chunk
+  int Tk;                 // T * k: first hbuf row of the shared expert
+  const float* xsum;      // [T][H/64] per-group activation sums
+  const int32_t* ids;     // [T][k]
+  const float* tw;        // [T][k]
+  const int32_t* counts;  // [E]
+  const int32_t* offsets; // [E+1]
+  const int32_t* sorted;  // [T*k]
+  const int32_t* tiles;   // [..][3]
+  const int32_t* n_tiles; // [1]
+  const int32_t* active;  // [E] experts with rows, increasing
+  const int32_t* n_active;// [1]
+  uint16_t* hbuf;         // [T*k + T][Imax] bf16
+  float* hsum;            // [T*k + T][Imax/32] sums of bf16(h) over 32-column halves of a group
+  float* y;               // [T][H]
+  int Imax;               // row stride of hbuf
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Four bf16 pairs (128 + code) from one packed dword.
+__device__ __forceinline__ void expand_codes(uint32_t d, uint32_t out[4]) {
+  out[0] = (d & 0x000F000Fu) | 0x43004300u;
+  out[1] = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
+  out[2] = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
+  out[3] = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint4 v = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Expert weight base pointer and widths.
+__device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e) {
+  return L.blob + (e == L.E ? L.shared_base : (int64_t)e * L.expert_bytes);
+}
+
+}  // namespace moe

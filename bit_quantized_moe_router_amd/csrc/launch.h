@@ -1,0 +1,34 @@
+// Host-side launchers of the MoE kernels (one per kernel family).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct PackArgs {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  uint8_t* dst;
+  int M, N, K;
+  int64_t dst_base;
+  int64_t stride_m;
+  int64_t stride_nb;
+  int64_t stride_g;
+};
+
+hipError_t launch_pack(const PackArgs& P, hipStream_t s);
+hipError_t launch_logits(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
+                         float* logits, float* xsum, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* tw,
+                       hipStream_t s);
+hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
+                       int32_t* n_tiles, int32_t* active, int32_t* n_active, hipStream_t s);
+hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s);
+hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);
+hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);
+
+}  // namespace moe

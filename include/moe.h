@@ -1,0 +1,197 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) 4-bit group-affine MoE FFN layer.
+ *
+ * The layer (the "Optimizing on-device inference for Apple Silicon" page):
+ *   - a router scores E experts per token and keeps the top k; one shared
+ *     expert processes every token (section "Qwen creates three different
+ *     workload shapes");
+ *   - each expert is a SwiGLU FFN whose weights are 4-bit integer codes, every
+ *     64 consecutive weights along the input dimension sharing one bf16 scale
+ *     and one bf16 bias that rebuild the weight as w = s*q + b (section
+ *     "Dequantise weights during matrix multiplication");
+ *   - routing runs on the GPU as top-k, histogram, prefix scan, scatter and a
+ *     block map, with no CPU round trip inside the layer (section "Keep
+ *     expert routing on the GPU");
+ *   - prefill uses a grouped matrix-matrix product over the routed rows;
+ *     single-row decode uses a row-parallel matrix-vector product (sections
+ *     "Apple silicon provides different paths for different workloads" and
+ *     "Optimise the one-row weight path");
+ *   - long prompts are processed in bounded chunks (section "Bound temporary
+ *     memory with prompt chunking").
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers unless stated otherwise, and are
+ *     owned by the caller.  The library allocates no memory in any call and
+ *     never reads device memory on the host.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on `stream` and returns; no call synchronises.
+ *   - Argument and shape errors are reported before anything is enqueued, so a
+ *     failed call leaves no partial work.  A failed kernel launch returns
+ *     MOE_ERR_HIP; faults during execution surface at the caller's next
+ *     synchronisation.  moe_last_error() gives a thread-local message for the
+ *     last failure.
+ *   - T = 0 is a valid no-op returning MOE_OK.
+ *   - Calls on different streams are safe given distinct workspaces and
+ *     outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad count, k > E, ... */
+    MOE_ERR_UNSUPPORTED_SHAPE = 2,  /* H or I not a multiple of 64, group != 64, sizes over limits */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes or packed_bytes below the required size */
+    MOE_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_DEVICE_UNSUPPORTED = 5  /* the current device is not gfx950 */
+} moe_status;
+
+/*
+ * Layer description.  Limits: hidden and inter multiples of 64 (the group
+ * size; the pages' format cannot quantise a width that is not a multiple of
+ * the group, cf. the Laya page's quantisation section), hidden <= 8192,
+ * inter <= 4096, shared_inter a multiple of 64 or 0, 1 <= top_k <= 16,
+ * top_k <= n_experts <= 512.
+ */
+typedef struct {
+    int32_t hidden;        /* H: model width, the input of gate/up and the output of down */
+    int32_t n_experts;     /* E: routed experts */
+    int32_t top_k;         /* k: experts kept per token */
+    int32_t inter;         /* I: routed expert intermediate width */
+    int32_t shared_inter;  /* Is: shared expert intermediate width, 0 = no shared expert */
+    int32_t group_size;    /* must be 64 */
+    int32_t gemv_max_rows; /* R*: moe_forward_decode uses the row-parallel GEMV path for
+                              T <= R* and the grouped GEMM path above; -1 = library default;
+                              0 = always GEMM; at most 8 */
+    int32_t max_chunk;     /* tokens per prefill chunk (1..8192); routing metadata is per chunk */
+    int32_t tile_rows;     /* BM: rows per tile of the block map; 0 = library default (64);
+                              one of 16, 32, 64, 128 */
+} moe_layer_desc;
+
+/*
+ * One quantised matrix stack in the canonical format (device pointers):
+ *   codes  [M][N][K/2]  uint8, two codes per byte, the even k in the low nibble
+ *   scales [M][N][K/64] bf16 bits
+ *   biases [M][N][K/64] bf16 bits
+ * with M = E for routed matrices and M = 1 for the shared expert; gate and up
+ * have N = inter (or shared_inter), K = hidden; down has N = hidden, K = inter.
+ */
+typedef struct {
+    const uint8_t *codes;
+    const uint16_t *scales;
+    const uint16_t *biases;
+} moe_qmatrix;
+
+/*
+ * Routing outputs for one chunk of T tokens (device pointers, caller-owned):
+ *   topk_ids       [T][k]  int32, experts in order of decreasing logit
+ *   topk_weights   [T][k]  float, softmax over the k selected logits
+ *   expert_counts  [E]     int32, assignments per expert (histogram)
+ *   expert_offsets [E+1]   int32, exclusive prefix scan of the counts
+ *   sorted_assign  [T*k]   int32, flat assignment ids t*k+j grouped by expert,
+ *                          increasing inside each expert (stable scatter)
+ *   tile_map       [moe_max_tiles][3] int32, (expert, first row inside the
+ *                          expert's segment, rows) per BM-row tile, experts in
+ *                          increasing order, then the shared expert's tiles as
+ *                          expert E over the tokens
+ *   n_tiles        [1]     int32, the number of valid tile_map entries
+ */
+typedef struct {
+    int32_t *topk_ids;
+    float *topk_weights;
+    int32_t *expert_counts;
+    int32_t *expert_offsets;
+    int32_t *sorted_assign;
+    int32_t *tile_map;
+    int32_t *n_tiles;
+} moe_routing;
+
+/* Size in bytes of the packed weight blob for `desc` (host output). */
+moe_status moe_packed_bytes(const moe_layer_desc *desc, size_t *bytes);
+
+/* Workspace bytes needed by moe_route / moe_forward_* for up to max_tokens per call (host output). */
+moe_status moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens, size_t *bytes);
+
+/* Number of tile_map entries moe_route may write for a chunk of T tokens (host output). */
+moe_status moe_max_tiles(const moe_layer_desc *desc, int32_t T, int32_t *n);
+
+/*
+ * Repack canonical quantised weights into the library's blob (device, size
+ * moe_packed_bytes).  The blob is opaque and valid only for the desc that
+ * made it.  It stores exactly the canonical codes, scales and biases (0.5625
+ * bytes per parameter), rearranged so that one 64-lane wave reads a 32-row x
+ * 64-column group with one 16-byte load per lane.  sh_* are ignored when
+ * shared_inter == 0.  One-time preparation; not part of the forward path.
+ */
+moe_status moe_pack_weights(const moe_layer_desc *desc, moe_qmatrix gate, moe_qmatrix up,
+                            moe_qmatrix down, moe_qmatrix sh_gate, moe_qmatrix sh_up,
+                            moe_qmatrix sh_down, void *packed, size_t packed_bytes, void *stream);
+
+/*
+ * Route one chunk of T <= max_chunk tokens: router logits
+ * fp32(sum_h x[t,h]*Wr[e,h] accumulated in float64) + logit_bias[e], top-k,
+ * softmax weights, then histogram, prefix scan, stable scatter and block map,
+ * all on the GPU.
+ *   x          [T][H] bf16
+ *   router_w   [E][H] float
+ *   logit_bias [E] float or NULL
+ *   ws         workspace of at least moe_workspace_bytes(desc, T) bytes
+ */
+moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
+                     const float *router_w, const float *logit_bias, const moe_routing *out,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Full layer over T tokens with the grouped dequantising GEMM path, chunk by
+ * chunk (max_chunk tokens each):
+ *   y[t] = sum_j topk_weights[t,j] * FFN_{topk_ids[t,j]}(x[t]) + FFN_shared(x[t])
+ * with FFN(x) = Wd (silu(Wg x) * (Wu x)).
+ *   packed  blob from moe_pack_weights
+ *   y       [T][H] float (written, not accumulated)
+ *   ws      at least moe_workspace_bytes(desc, min(T, max_chunk)) bytes
+ */
+moe_status moe_forward_prefill(const moe_layer_desc *desc, const void *packed,
+                               const float *router_w, const float *logit_bias,
+                               const uint16_t *x, int32_t T, float *y,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Same layer for a few rows (1 <= T <= 8): the row-parallel GEMV path when
+ * T <= gemv_max_rows, otherwise the grouped GEMM path of moe_forward_prefill.
+ */
+moe_status moe_forward_decode(const moe_layer_desc *desc, const void *packed,
+                              const float *router_w, const float *logit_bias,
+                              const uint16_t *x, int32_t T, float *y,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* Default R* of the library (host output). */
+int32_t moe_default_gemv_max_rows(void);
+
+const char *moe_status_str(moe_status s);
+const char *moe_last_error(void);
+
+/*
+ * Kernel timing for measurement tools.  While enabled, the library records a
+ * HIP event pair around every launch of the kernels named below, on the
+ * launch stream.  moe_profile_read synchronises on those events, returns the
+ * summed duration (ms) and launch count of kernel `kernel_id` since the last
+ * reset, and never runs on the forward path.  Not thread-safe.
+ *   0 = router logits, 1 = top-k, 2 = routing metadata, 3 = gate/up grouped
+ *   GEMM, 4 = down grouped GEMM, 5 = gate/up GEMV, 6 = down GEMV
+ */
+moe_status moe_profile_enable(int32_t on);
+moe_status moe_profile_reset(void);
+moe_status moe_profile_read(int32_t kernel_id, double *total_ms, int32_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: routing indices, counts, offsets, permutation and block map bit-exact;
+routing weights within 1e-5; layer outputs within relative L2 <= 5e-3 and
+max-abs <= 2e-2 * RMS(reference) of the float64 oracle.
+"""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from oracle import oracle as orc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 5e-3
+MAXABS_RMS = 2e-2
+W_TOL = 1e-5
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def M():
+    _need_gpu()
+    from bit_quantized_moe_router_amd import layer as L
+    return L
+
+
+_LAYERS = {}
+
+
+def get_layer(M, case, **kw):
+    key = (case["cfg"]["H"], case["cfg"]["E"], case["cfg"]["I"], case["cfg"]["Is"], case["cfg"]["wseed"],
+           case["k"], tuple(sorted(kw.items())))
+    if key not in _LAYERS:
+        _LAYERS[key] = M.MoELayer(case["w"], case["k"], max_tokens=kw.pop("max_tokens", 2048), **kw)
+    return _LAYERS[key]
+
+
+def dev(M, a):
+    return None if a is None else M.to_dev(a, "cuda")
+
+
+def check_close(y, ref, label):
+    y = np.asarray(y, np.float64)
+    err = y - ref
+    rel = np.linalg.norm(err) / np.linalg.norm(ref)
+    rms = np.sqrt(np.mean(ref ** 2))
+    maxabs = np.abs(err).max()
+    print(f"[parity] {label}: rel_l2={rel:.3e} max_abs/rms={maxabs / rms:.3e}", flush=True)
+    assert np.all(np.isfinite(y)), label
+    assert rel <= REL_L2, (label, rel)
+    assert maxabs <= MAXABS_RMS * rms, (label, maxabs / rms)
+
+
+def check_route(r_gpu, r_ref, label):
+    g = {k: v.cpu().numpy() for k, v in r_gpu.items()}
+    assert np.array_equal(g["topk_ids"], r_ref["topk_ids"]), label
+    assert np.array_equal(g["expert_counts"], r_ref["counts"]), label
+    assert np.array_equal(g["expert_offsets"], r_ref["offsets"]), label
+    assert np.array_equal(g["sorted_assign"], r_ref["sorted_assign"]), label
+    n = int(g["n_tiles"][0])
+    assert n == r_ref["n_tiles"], label
+    assert np.array_equal(g["tile_map"][:n], r_ref["tiles"]), label
+    dw = np.abs(g["topk_weights"].astype(np.float64) - r_ref["topk_weights"]).max()
+    assert dw <= W_TOL, (label, dw)
+    print(f"[route] {label}: bit-exact, max|dw|={dw:.2e}", flush=True)
+
+
+# ---- packer -------------------------------------------------------------------
+
+def unpack_matrix(blob, base, N, K, stride_nb, stride_g, stride_blk=1152):
+    """Inverse of the documented blob layout, written from the layout description."""
+    NBn, G = N // 32, K // 64
+    idx = (base + np.arange(NBn)[:, None, None] * stride_nb + np.arange(G)[None, :, None] * stride_g
+           + np.arange(1152)[None, None, :])
+    blk = blob[idx]  # [NBn][G][1152]
+    d = np.ascontiguousarray(blk[..., :1024]).view(np.uint32).reshape(NBn, G, 2, 32, 4)
+    nib = (d[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 15  # [NBn][G][h][row][c][p]
+    koff = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+    q = np.empty((NBn, 32, G, 2, 4, 8), np.uint8)
+    q[..., koff] = nib.transpose(0, 3, 1, 2, 4, 5)
+    q = q.reshape(N, K)
+    sb = np.ascontiguousarray(blk[..., 1024:]).view(np.uint32).reshape(NBn, G, 32).transpose(0, 2, 1).reshape(N, G)
+    return q, (sb & 0xFFFF).astype(np.uint16), (sb >> 16).astype(np.uint16)
+
+
+def canon_q(codes):
+    q = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), np.uint8)
+    q[..., 0::2] = codes & 15
+    q[..., 1::2] = codes >> 4
+    return q
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_pack_roundtrip(M, name):
+    case = mi.make_case(name)
+    w = case["w"]
+    lay = get_layer(M, case)
+    blob = lay.packed.cpu().numpy()
+    H, E, I, Is = w["H"], w["E"], w["I"], w["Is"]
+    gu = (I // 32) * (H // 64) * 2 * 1152
+    ex = gu + (H // 32) * (I // 64) * 1152
+    assert blob.size == E * ex + 3 * H * Is * 9 // 16
+    experts = range(E) if E <= 16 else [0, 1, 77, E - 1]
+    for e in experts:
+        for which, m in ((0, "gate"), (1, "up")):
+            q, s, b = unpack_matrix(blob, e * ex + which * 1152, I, H, (H // 64) * 2 * 1152, 2 * 1152)
+            assert np.array_equal(q, canon_q(w[m]["codes"][e])), (e, m)
+            assert np.array_equal(s, w[m]["scales"][e]) and np.array_equal(b, w[m]["biases"][e])
+        q, s, b = unpack_matrix(blob, e * ex + gu, H, I, (I // 64) * 1152, 1152)
+        assert np.array_equal(q, canon_q(w["down"]["codes"][e]))
+        assert np.array_equal(s, w["down"]["scales"][e]) and np.array_equal(b, w["down"]["biases"][e])
+    sgu = (Is // 32) * (H // 64) * 2 * 1152
+    q, s, b = unpack_matrix(blob, E * ex + 1152, Is, H, (H // 64) * 2 * 1152, 2 * 1152)
+    assert np.array_equal(q, canon_q(w["sh_up"]["codes"][0]))
+    q, s, b = unpack_matrix(blob, E * ex + sgu, H, Is, (Is // 64) * 1152, 1152)
+    assert np.array_equal(q, canon_q(w["sh_down"]["codes"][0])) and np.array_equal(b, w["sh_down"]["biases"][0])
+
+
+# ---- routing ------------------------------------------------------------------
+
+ROUTE_CASES = ["tiny", "decode", "smallrow2", "smallrow5", "smallrow8", "prefill512", "prefill4096"]
+
+
+@pytest.mark.parametrize("name", ROUTE_CASES)
+def test_route_bitexact(M, name):
+    case = mi.make_case(name)
+    lay = get_layer(M, case)
+    BM = lay.desc.tile_rows or 64
+    x, bias = case["x"], case["bias"]
+    for c0 in range(0, case["T"], mi.CHUNK):
+        xc = x[c0:c0 + mi.CHUNK]
+        r = lay.route(dev(M, xc), dev(M, bias))
+        torch.cuda.synchronize()
+        ref = orc.route(xc, case["w"]["router_w"], bias, case["k"], BM)
+        check_route(r, ref, f"{name}[{c0}:]")
+
+
+@pytest.mark.parametrize("bm", [16, 32, 128])
+def test_route_tile_rows(M, bm):
+    case = mi.make_case("prefill512")
+    lay = get_layer(M, case, tile_rows=bm)
+    r = lay.route(dev(M, case["x"]), None)
+    torch.cuda.synchronize()
+    check_route(r, orc.route(case["x"], case["w"]["router_w"], None, case["k"], bm), f"prefill512 BM={bm}")
+
+
+# ---- full layer -----------------------------------------------------------------
+
+def oracle_rows(case, tokens=None, chunk=mi.CHUNK):
+    y, _ = orc.forward(case["w"], case["k"], case["x"], case["bias"], chunk, 64, tokens=tokens)
+    return y
+
+
+@pytest.mark.parametrize("bm,chunk", [(0, 2048), (16, 2048), (32, 16), (128, 64), (64, 7)])
+def test_tiny_prefill_all_rows(M, bm, chunk):
+    case = mi.make_case("tiny")
+    lay = get_layer(M, case, tile_rows=bm, max_chunk=chunk)
+    y = lay.forward_prefill(dev(M, case["x"]), dev(M, case["bias"]))
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), oracle_rows(case), f"tiny prefill BM={bm} chunk={chunk}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("gemv", [8, 0])
+def test_tiny_decode_both_paths(M, T, gemv):
+    case = mi.make_case("tiny")
+    lay = get_layer(M, case, gemv_max_rows=gemv)
+    x = case["x"][:T]
+    y = lay.forward_decode(dev(M, x), None)
+    torch.cuda.synchronize()
+    sub = dict(case, x=x, T=T)
+    check_close(y.cpu().numpy(), oracle_rows(sub), f"tiny decode T={T} gemv_max_rows={gemv}")
+
+
+def test_decode_T1(M):
+    case = mi.make_case("decode")
+    lay = get_layer(M, case)
+    y = lay.forward_decode(dev(M, case["x"]), None)
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), oracle_rows(case), "decode T=1 (GEMV)")
+
+
+@pytest.mark.parametrize("T", mi.SMALLROW_TS)
+@pytest.mark.parametrize("gemv", [8, 0])
+def test_smallrow_both_paths(M, T, gemv):
+    case = mi.make_case(f"smallrow{T}")
+    lay = get_layer(M, case, gemv_max_rows=gemv)
+    y = lay.forward_decode(dev(M, case["x"]), None)
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), oracle_rows(case), f"smallrow T={T} gemv_max_rows={gemv}")
+
+
+def _sample_tokens(case, n, seed):
+    """Seeded sample that also holds tokens routed to the most loaded expert of each chunk."""
+    rng = np.random.default_rng(seed)
+    T = case["T"]
+    toks = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    toks.update([0, T - 1])
+    return np.array(sorted(toks), np.int32)
+
+
+@pytest.mark.parametrize("name", ["prefill512", "prefill4096"])
+def test_prefill_sampled_rows(M, name):
+    case = mi.make_case(name)
+    lay = get_layer(M, case)
+    y = lay.forward_prefill(dev(M, case["x"]), dev(M, case["bias"]))
+    torch.cuda.synchronize()
+    yn = y.cpu().numpy()
+    assert np.all(np.isfinite(yn))
+    toks = _sample_tokens(case, 40, seed=7)
+    check_close(yn[toks], oracle_rows(case, toks), f"{name} sampled {len(toks)} rows")
+
+
+# ---- edge cases -------------------------------------------------------------------
+
+EDGE = [
+    # T, H, E, k, I, Is, seed, zipf, chunk, bm
+    (37, 128, 8, 3, 64, 128, 21, 22, 16, 16),   # ragged chunks, zipf bias, Is != I
+    (9, 192, 1, 1, 128, 0, 31, None, 64, 32),   # one expert, no shared expert
+    (50, 256, 32, 8, 192, 64, 51, 52, 2048, 64),  # k=8 of 32, I not a multiple of 128
+    (5, 64, 4, 4, 64, 64, 61, None, 2, 16),     # k == E, tiny chunks
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,I,Is,seed,zipf,chunk,bm", EDGE)
+def test_edge_layers(M, T, H, E, k, I, Is, seed, zipf, chunk, bm):
+    case = mi.small_layer(T, H, E, k, I, Is, seed, zipf)
+    lay = M.MoELayer(case["w"], k, max_tokens=T, max_chunk=chunk, tile_rows=bm)
+    y = lay.forward_prefill(dev(M, case["x"]), dev(M, case["bias"]))
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), oracle_rows(case, chunk=chunk), f"edge {case['name']} prefill")
+    if T <= 8:
+        for gemv in (8, 0):
+            lay.set_desc(gemv_max_rows=gemv)
+            y = lay.forward_decode(dev(M, case["x"]), dev(M, case["bias"]))
+            torch.cuda.synchronize()
+            check_close(y.cpu().numpy(), oracle_rows(case, chunk=chunk), f"edge {case['name']} decode {gemv}")
+    # routing of the first chunk
+    xc = case["x"][:chunk]
+    r = lay.route(dev(M, xc), dev(M, case["bias"]))
+    torch.cuda.synchronize()
+    check_route(r, orc.route(xc, case["w"]["router_w"], case["bias"], k, bm), f"edge {case['name']}")
+
+
+def test_zero_tokens_is_noop(M):
+    case = mi.make_case("tiny")
+    lay = get_layer(M, case)
+    y = torch.full((4, case["cfg"]["H"]), 7.0, device="cuda")
+    x = dev(M, case["x"][:0])
+    from bit_quantized_moe_router_amd import moe_forward_prefill
+    moe_forward_prefill(lay.desc, lay.packed, lay.router_w, None, x, 0, y, lay.ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
