@@ -1,0 +1,200 @@
+"""Benchmark of the MoE layer on one MI355X.
+
+One step = one full layer call (routing, grouped gate/up GEMM + SwiGLU, down
+GEMM + combine) over the 4096-token prefill workload (two chunks of 2048;
+H=2048, 256 experts top-8 + shared, I=512, 4-bit group-64 weights, Zipf(1.1)
+logit bias).  Inputs are resident in HBM before the timed region.  Weight
+copies rotate every step (4 distinct packed blobs, 1.8 GB > the 256 MB
+Infinity Cache) so each step reads its weights from HBM, as consecutive layers
+of a model would.
+
+Also reported on the same line: the T=1 decode layer (GEMV path) in
+microseconds per layer, kernel-level roofline fractions from HIP events
+recorded around the dominant kernels on the launch stream, and the CPU
+oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--copies", type=int, default=4, help="distinct weight blobs rotated per step")
+    p.add_argument("--decode-steps", type=int, default=200)
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(case, budget_s):
+    """The oracle as it stands on one host core: routing of one 2048-token chunk,
+    then the layer output of as many of its tokens as fit the time budget."""
+    from oracle import oracle as orc
+
+    x = case["x"][:2048]
+    t0 = time.perf_counter()
+    r = orc.route(x, case["w"]["router_w"], case["bias"], case["k"], 64)
+    t_route = time.perf_counter() - t0
+    n, t_ffn = 0, 0.0
+    step = 4
+    while t_ffn < max(1.0, budget_s - t_route) and n + step <= 2048:
+        toks = np.arange(n, n + step, dtype=np.int32)
+        t1 = time.perf_counter()
+        orc.ffn_tokens(case["w"], case["k"], x, r["topk_ids"], r["topk_weights"], toks)
+        t_ffn += time.perf_counter() - t1
+        n += step
+    per_tok = t_route / 2048 + t_ffn / n
+    return {"value": round(1.0 / per_tok, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"routing of one 2048-token chunk ({t_route:.2f} s) + layer output of its first {n} "
+                      f"tokens ({t_ffn:.2f} s), single-threaded C, float64"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import moe_inputs as mi
+    import bit_quantized_moe_router_amd as moe
+    from bit_quantized_moe_router_amd.layer import MoELayer, to_dev
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = mi.make_case("prefill4096")
+    w, k, T, H = case["w"], case["k"], case["T"], case["cfg"]["H"]
+    I, Is, E = w["I"], w["Is"], w["E"]
+    layers = [MoELayer(w, k, device=dev, max_tokens=2048)]
+    for _ in range(a.copies - 1):
+        lay = MoELayer.__new__(MoELayer)
+        lay.__dict__.update(layers[0].__dict__)
+        lay.packed = layers[0].packed.clone()
+        lay.router_w = layers[0].router_w.clone()
+        lay.ws = torch.empty_like(layers[0].ws)
+        layers.append(lay)
+    x = to_dev(case["x"], dev)
+    bias = to_dev(case["bias"], dev)
+    ys = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in layers]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        lay = layers[i % len(layers)]
+        lay.forward_prefill(x, bias, ys[i % len(layers)])
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, kernel events recorded by the library on this stream.
+    moe.moe_profile_reset()
+    moe.moe_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t_wall = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    moe.moe_profile_enable(False)
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / a.steps
+    kern = {}
+    for kid, name in moe.KERNEL_NAMES.items():
+        tot, n = moe.moe_profile_read(kid)
+        if n:
+            kern[name] = {"avg_us": round(1000.0 * tot / n, 3), "launches": n}
+
+    # Dominant kernel: gate/up grouped GEMM, one launch per 2048-token chunk.
+    Tc = 2048
+    flop_gateup = 2.0 * (Tc * k + Tc) * H * (2 * I)
+    g = kern["k_gateup_gemm"]
+    achieved = flop_gateup / (g["avg_us"] * 1e-6) / 1e12
+    flop_down = 2.0 * (Tc * k + Tc) * I * H
+    d = kern["k_down_gemm"]
+    down_tf = flop_down / (d["avg_us"] * 1e-6) / 1e12
+
+    # Decode T=1 (GEMV path) on the same layer copies.
+    dcase = mi.make_case("decode")
+    xd = to_dev(dcase["x"], dev)
+    yd = torch.empty((1, H), dtype=torch.float32, device=dev)
+    for lay in layers:
+        lay.set_desc(gemv_max_rows=-1)
+    for i in range(10):
+        layers[i % len(layers)].forward_decode(xd, None, yd)
+    torch.cuda.synchronize()
+    moe.moe_profile_reset()
+    moe.moe_profile_enable(True)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for i in range(a.decode_steps):
+        layers[i % len(layers)].forward_decode(xd, None, yd)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(False)
+    dec_us = 1000.0 * d0.elapsed_time(d1) / a.decode_steps
+    dkern = {}
+    for kid, name in moe.KERNEL_NAMES.items():
+        tot, n = moe.moe_profile_read(kid)
+        if n:
+            dkern[name] = {"avg_us": round(1000.0 * tot / n, 3), "launches": n}
+    blk = 1152
+    gu_bytes = 9 * (I // 32) * (H // 64) * 2 * blk          # 8 routed + shared, gate and up, packed
+    dn_bytes = 9 * (H // 32) * (I // 64) * blk
+    gemv_gu = dkern.get("k_gemv_gateup")
+    gemv_dn = dkern.get("k_gemv_down")
+    dec_roof = {
+        "gateup_gemv_GBs": round(gu_bytes / (gemv_gu["avg_us"] * 1e-6) / 1e9, 1) if gemv_gu else None,
+        "down_gemv_GBs": round(dn_bytes / (gemv_dn["avg_us"] * 1e-6) / 1e9, 1) if gemv_dn else None,
+        "peak_GBs": PEAK_HBM_GBS,
+    }
+
+    rec = {
+        "metric": "MoE-layer tok/s @T=4096 prefill; µs/layer @T=1 decode; % HBM/MFMA roofline",
+        "value": round(T / (ms_per_step / 1000.0), 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "MoE layer prefill T=4096 in 2x2048-token chunks, H=2048, E=256 top-8 + 1 shared, "
+                               "I=Is=512, SwiGLU, 4-bit codes g64 bf16 scale/bias, Zipf(1.1) logit bias",
+                   "weight_copies_rotated": a.copies, "wall_s_timed": round(t_wall, 4)},
+        "roofline": {"bound": "mfma", "kernel": "k_gateup_gemm", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flop_per_launch": flop_gateup, "avg_us": g["avg_us"]},
+        "kernels_us": kern,
+        "down_gemm_tflops": round(down_tf, 2),
+        "decode": {"us_per_layer": round(dec_us, 3), "T": 1, "kernels_us": dkern, "roofline": dec_roof},
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(case, a.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -91,7 +91,8 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(LayerArgs L, ChunkArgs C) {
             du = dot2_bf16(qu[4 * c + i], xw[i], du);
           }
         }
-        const float xs = C.xsum[(int64_t)tok[j] * G + g];
+        // The group's activation sum covers both lane halves: fold it in once.
+        const float xs = h == 0 ? C.xsum[(int64_t)tok[j] * G + g] : 0.f;
         accg[j] = fmaf(sg, dg, fmaf(bpg, xs, accg[j]));
         accu[j] = fmaf(su, du, fmaf(bpu, xs, accu[j]));
       }
@@ -191,8 +192,8 @@ __global__ __launch_bounds__(256) void k_gemv_down(LayerArgs L, ChunkArgs C) {
           d = dot2_bf16(q[4 * c + 2], hv.z, d);
           d = dot2_bf16(q[4 * c + 3], hv.w, d);
         }
-        const float* hsp = C.hsum + irow * hsw + 2 * g;
-        const float v = w * fmaf(s, d, bp * (hsp[0] + hsp[1]));
+        // hsum holds 32-column sums, so this lane half's own columns.
+        const float v = w * fmaf(s, d, bp * C.hsum[irow * hsw + 2 * g + h]);
 #pragma unroll
         for (int tt = 0; tt < kGemvMaxRows; tt++)
           if (tt == t) acc[tt] += v;

@@ -246,7 +246,8 @@ def test_edge_layers(M, T, H, E, k, I, Is, seed, zipf, chunk, bm):
     xc = case["x"][:chunk]
     r = lay.route(dev(M, xc), dev(M, case["bias"]))
     torch.cuda.synchronize()
-    check_route(r, orc.route(xc, case["w"]["router_w"], case["bias"], k, bm), f"edge {case['name']}")
+    ref = orc.route(xc, case["w"]["router_w"], case["bias"], k, bm, with_shared=Is > 0)
+    check_route(r, ref, f"edge {case['name']}")
 
 
 def test_zero_tokens_is_noop(M):
