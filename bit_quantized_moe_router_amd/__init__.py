@@ -18,7 +18,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED_SH
 
 # Kernel ids of moe_profile_read.
 K_LOGITS, K_TOPK, K_META, K_GATEUP_GEMM, K_DOWN_GEMM, K_GATEUP_GEMV, K_DOWN_GEMV = range(7)
-KERNEL_NAMES = {K_LOGITS: "k_logits", K_TOPK: "k_topk", K_META: "k_meta",
+KERNEL_NAMES = {K_LOGITS: "k_screen|k_logits_small", K_TOPK: "k_route_exact", K_META: "k_meta|k_topk_meta",
                 K_GATEUP_GEMM: "k_gateup_gemm", K_DOWN_GEMM: "k_down_gemm",
                 K_GATEUP_GEMV: "k_gemv_gateup", K_DOWN_GEMV: "k_gemv_down"}
 
@@ -157,8 +157,9 @@ def moe_forward_decode(desc, packed, router_w, logit_bias, x, T, y, ws, stream=N
                                     _stream(stream)))
 
 
-def moe_profile_enable(on: bool):
-    _check(lib().moe_profile_enable(1 if on else 0))
+def moe_profile_enable(mask: int):
+    """Bit i set = record events around kernel id i (0 = off)."""
+    _check(lib().moe_profile_enable(int(mask)))
 
 
 def moe_profile_reset():

@@ -32,7 +32,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
   return s;
 }
 
-constexpr int kDefaultTileRows = 64;
+constexpr int kDefaultTileRows = 256;
 constexpr int kDefaultGemvMaxRows = 4;
 constexpr int kMaxRowsDecode = 8;
 
@@ -55,8 +55,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->max_chunk < 1 || d->max_chunk > 8192)
     return fail(MOE_ERR_INVALID_ARGUMENT, "max_chunk must be in 1..8192 (got %d)", d->max_chunk);
   const int bm = d->tile_rows;
-  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "tile_rows must be 0, 16, 32, 64 or 128 (got %d)", bm);
+  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "tile_rows must be 0, 16, 32, 64, 128 or 256 (got %d)", bm);
   return MOE_OK;
 }
 
@@ -86,7 +86,7 @@ Blob blob_geom(const moe_layer_desc* d) {
 }
 
 struct Ws {
-  size_t logits, xsum, ids, tw, counts, offsets, sorted, tiles, n_tiles, active, n_active, hbuf, hsum;
+  size_t logits, wnorm, xsum, x16, ids, tw, counts, offsets, sorted, tiles, n_tiles, active, n_active, hbuf, hsum;
   size_t total;
 };
 
@@ -98,7 +98,9 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   Ws w;
   size_t o = 0;
   w.logits = o; o += al(Tc * E * 4);
+  w.wnorm = o; o += al(E * 4);
   w.xsum = o; o += al(Tc * (H / 64) * 4);
+  w.x16 = o; o += al(Tc * H * 2);
   w.ids = o; o += al(Tc * k * 4);
   w.tw = o; o += al(Tc * k * 4);
   w.counts = o; o += al(E * 4);
@@ -146,7 +148,7 @@ struct Pending {
   hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+uint32_t g_prof_mask = 0;  // bit i: time kernel id i
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_event_pool;
 double g_prof_ms[kNumKernels];
@@ -167,14 +169,15 @@ hipEvent_t get_event() {
 template <class F>
 moe_status timed(int kid, hipStream_t s, const char* what, F fn) {
   Pending p{kid, nullptr, nullptr};
-  if (g_prof_on && kid >= 0) {
+  const bool on = kid >= 0 && ((g_prof_mask >> kid) & 1u);
+  if (on) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     p.a = get_event();
     p.b = get_event();
     if (p.a) (void)hipEventRecord(p.a, s);
   }
   hipError_t e = fn();
-  if (g_prof_on && kid >= 0 && p.a && p.b) {
+  if (on && p.a && p.b) {
     (void)hipEventRecord(p.b, s);
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_pending.push_back(p);
@@ -207,14 +210,27 @@ LayerArgs layer_args(const moe_layer_desc* d, const void* packed) {
 
 struct RouteOut {
   int32_t *ids, *counts, *offsets, *sorted, *tiles, *n_tiles, *active, *n_active;
-  float *tw, *logits, *xsum;
+  float *tw, *logits, *wnorm, *xsum;
+  uint16_t* x16;
 };
 
 moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const float* wr,
                      const float* bias, const RouteOut& o, hipStream_t s) {
   const int E = d->n_experts, k = d->top_k, H = d->hidden;
-  TRY(timed(0, s, "router logits", [&] { return launch_logits(x, T, H, wr, bias, E, o.logits, o.xsum, s); }));
-  TRY(timed(1, s, "top-k", [&] { return launch_topk(o.logits, T, E, k, o.ids, o.tw, s); }));
+  bool two = false;
+  TRY(timed(0, s, "router logits", [&] {
+    return launch_route_logits(x, T, H, wr, bias, E, k, o.logits, o.wnorm, o.ids, o.tw, o.xsum, o.x16, s, &two);
+  }));
+  if (!two) {
+    // Few tokens: exact logits are already there; top-k + metadata in one launch.
+    return timed(2, s, "top-k + routing metadata", [&] {
+      return launch_topk_meta(o.logits, T, E, k, o.ids, o.tw, tile_rows(d), d->shared_inter > 0 ? 1 : 0,
+                              o.counts, o.offsets, o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, s);
+    });
+  }
+  TRY(timed(1, s, "top-k", [&] {
+    return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wnorm, o.ids, o.tw, o.xsum, o.x16, s);
+  }));
   TRY(timed(2, s, "routing metadata", [&] {
     return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, o.counts, o.offsets,
                        o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, s);
@@ -225,7 +241,9 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
 RouteOut ws_route(void* ws, const Ws& w) {
   RouteOut o;
   o.logits = at<float>(ws, w.logits);
+  o.wnorm = at<float>(ws, w.wnorm);
   o.xsum = at<float>(ws, w.xsum);
+  o.x16 = at<uint16_t>(ws, w.x16);
   o.ids = at<int32_t>(ws, w.ids);
   o.tw = at<float>(ws, w.tw);
   o.counts = at<int32_t>(ws, w.counts);
@@ -242,6 +260,7 @@ ChunkArgs chunk_args(const moe_layer_desc* d, const uint16_t* x, int Tc, const R
                      const Ws& w, float* y) {
   ChunkArgs C;
   C.x = x;
+  C.x16 = o.x16;
   C.T = Tc;
   C.Tk = Tc * d->top_k;
   C.xsum = o.xsum;
@@ -438,8 +457,8 @@ const char* moe_status_str(moe_status s) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-moe_status moe_profile_enable(int32_t on) {
-  g_prof_on = on != 0;
+moe_status moe_profile_enable(int32_t mask) {
+  g_prof_mask = (uint32_t)mask;
   return MOE_OK;
 }
 

@@ -56,6 +56,7 @@ struct LayerArgs {
 
 struct ChunkArgs {
   const uint16_t* x;      // [T][H] bf16
+  const uint16_t* x16;    // [T][H] fp16(x / 256), operand of the grouped GEMM
   int T;                  // tokens in this chunk
   int Tk;                 // T * k: first hbuf row of the shared expert
   const float* xsum;      // [T][H/64] per-group activation sums
@@ -68,8 +69,8 @@ struct ChunkArgs {
   const int32_t* n_tiles; // [1]
   const int32_t* active;  // [E] experts with rows, increasing
   const int32_t* n_active;// [1]
-  uint16_t* hbuf;         // [T*k + T][Imax] bf16
-  float* hsum;            // [T*k + T][Imax/32] sums of bf16(h) over 32-column halves of a group
+  uint16_t* hbuf;         // [T*k + T][Imax]: fp16(h / 256) on the GEMM path, bf16 h on the GEMV path
+  float* hsum;            // [T*k + T][Imax/32] GEMV path: sums of bf16(h) over 32-column halves of a group
   float* y;               // [T][H]
   int Imax;               // row stride of hbuf
 };

@@ -1,232 +1,266 @@
 // Grouped expert GEMMs for prefill ("Optimizing on-device inference for Apple
-// Silicon", sections "Dequantise weights during matrix multiplication" and
-// "Reduce intermediate and state traffic"):
-//   gate/up: per tile of routed rows, h = silu(x Wg^T) * (x Wu^T) -> bf16
+// Silicon", sections "Dequantise weights during matrix multiplication",
+// "Match tile size to expert load" and "Reduce intermediate and state
+// traffic"):
+//   gate/up: per tile of routed rows, h = silu(x Wg^T) * (x Wu^T)
 //   down:    y[token] += routing weight * (h Wd^T), the shared expert with 1
-// Weights stay 4-bit in HBM.  Each wave expands its 16-byte code slice per
-// group straight into bf16 MFMA operands (128 + q, exact), multiplies with
-// v_mfma_f32_32x32x16_bf16 into a per-group fp32 partial P, and folds the
-// group's affine parameters in fp32:  acc += s * P + (b - 128 s) * sum(x).
-// The full-precision weights are never materialised, in HBM or in LDS.
 //
-// Workgroup: 256 threads = 4 waves over a 64-row slab x 64 output columns,
-// wave (wm, wn) owning rows 32*wm.. and columns 32*wn.. of the slab.  The tile
-// map (expert, first row, rows) comes from the routing kernels; surplus
-// workgroups (beyond n_tiles, read on the device) exit at once.
+// Workgroup = 8 waves over a tile of up to 256 rows of one expert x 256 weight
+// columns (gate/up: 128 intermediate columns of gate and the same 128 of up;
+// down: 256 output columns).  Wave (wm, wn) owns rows 64*wm.. and half the
+// columns: 2 x 4 blocks of v_mfma_f32_32x32x16_f16, fp32 accumulation.
+//
+// Weights stay 4-bit in HBM.  Per 64-wide K group the workgroup reads the
+// packed codes of its 8 blocks of 32 columns (one 16-byte load per thread,
+// one block per wave), rebuilds w = s*q + b in fp32, rounds it to fp16 and
+// writes it to LDS in MFMA operand order (block, k-step, lane), so that every
+// wave reads its B operands with conflict-free 16-byte LDS reads.  The LDS
+// tile is double buffered: the weights of group g+1 are rebuilt while the
+// MFMAs of group g run.  The full-precision weights never reach HBM.
+//
+// Operand precision: the pages rebuild weights in bf16; here the operands are
+// fp16 (11 significant bits instead of 8), which cuts the rounding error of
+// the rebuilt weights eightfold.  Activations enter as fp16(x / 256) (written
+// by the routing kernels) and the intermediate as fp16(h / 256); the power-of-
+// two scale is exact and keeps any bf16-sized value inside the fp16 range, and
+// the epilogues multiply it back.
+//
+// Activations go from memory straight to registers (gathered token rows for
+// gate/up, contiguous rows of the expert's segment for down), one group ahead,
+// in two register sets that alternate between even and odd groups.  Rows
+// beyond the tile's valid count reuse a valid row's address and are never
+// stored; a wave whose 64 rows are all beyond the count skips its MFMAs.
+// Workgroups beyond n_tiles (read on the device) exit.
 //
 // MFMA 32x32x16 operand layout (wave64): lane l supplies row (A) / column (B)
 // l % 32 and eight consecutive k-slots 8*(l/32)..+7; the result holds column
-// l % 32 and rows 8*(i/4) + 4*(l/32) + i%4 in accumulator i.  The kernels map
-// k-slot j of MFMA c for lane half h to input column 32h + 8c + j of the
-// group, for A and B alike, which is also the order the packer stores codes
-// in; any consistent mapping gives the same product.
+// l % 32 and rows 8*(i/4) + 4*(l/32) + i%4 in accumulator i.  k-slot j of MFMA
+// c for lane half h carries input column 32h + 8c + j of the group, for A and
+// B alike, which is the order the packer stores codes in.
+//
+// Workgroup ids are mapped so that the column tiles of one row tile run on the
+// same XCD back to back (dispatch is round-robin over the 8 XCDs), which
+// keeps the tile's activation rows in that XCD's L2.
 #include "launch.h"
 
 namespace moe {
 
-constexpr int kSlab = 64;
-constexpr int kAStride = 72;  // bf16 per LDS row of the A slab (64 + 8 pad)
+constexpr int kTileRows = 256;
+constexpr int kWaves = 8;
+constexpr int kBlocks = 8;                           // 32-column weight blocks per tile
+constexpr int kBufBytes = kBlocks * kCodeBytes * 4;  // fp16 tile of one group: 8 x 4 x 64 x 16 B
+constexpr int kSmem = 2 * kBufBytes + kTileRows * 8; // + token / weight per row
 
-// Stage one 64-row x 64-column bf16 slab of A into LDS; rows with src == null are zero.
-__device__ __forceinline__ void stage_a(uint16_t* As, const uint16_t* const* rowsrc, int col0) {
-  for (int i = threadIdx.x; i < kSlab * 8; i += 256) {
-    const int r = i >> 3, part = i & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    const uint16_t* p = rowsrc[r];
-    if (p) v = *reinterpret_cast<const uint4*>(p + col0 + part * 8);
-    *reinterpret_cast<uint4*>(As + r * kAStride + part * 8) = v;
-  }
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// 8 codes of one packed dword -> 8 fp16 weights w = s*q + b (round to nearest
+// even), in k order, as four dwords of fp16 pairs.
+__device__ __forceinline__ uint4 dequant8(uint32_t d, float s, float b) {
+  uint32_t e = d & 0x0F0F0F0Fu;         // bytes: q0 q4 q1 q5
+  uint32_t o = (d >> 4) & 0x0F0F0F0Fu;  // bytes: q2 q6 q3 q7
+  asm("" : "+v"(e), "+v"(o));            // keep the masks; bytes convert with v_cvt_f32_ubyteN
+  const float w0 = fmaf((float)(e & 0xFFu), s, b), w1 = fmaf((float)((e >> 16) & 0xFFu), s, b);
+  const float w2 = fmaf((float)(o & 0xFFu), s, b), w3 = fmaf((float)((o >> 16) & 0xFFu), s, b);
+  const float w4 = fmaf((float)((e >> 8) & 0xFFu), s, b), w5 = fmaf((float)(e >> 24), s, b);
+  const float w6 = fmaf((float)((o >> 8) & 0xFFu), s, b), w7 = fmaf((float)(o >> 24), s, b);
+  f16x2_t p0 = {(_Float16)w0, (_Float16)w1}, p1 = {(_Float16)w2, (_Float16)w3};
+  f16x2_t p2 = {(_Float16)w4, (_Float16)w5}, p3 = {(_Float16)w6, (_Float16)w7};
+  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
 }
 
-__device__ __forceinline__ bf16x8_t a_frag(const uint16_t* As, int row, int h, int c) {
-  return *reinterpret_cast<const bf16x8_t*>(As + row * kAStride + h * 32 + c * 8);
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// One group (64 k) of one 32x32 output block: P = A(32x64) * (128 + Q)(64x32).
-__device__ __forceinline__ f32x16_t group_mma(const uint16_t* As, int arow, int h, uint4 codes) {
-  f32x16_t p = {};
-  const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
-#pragma unroll
-  for (int c = 0; c < 4; c++) {
-    uint32_t b[4];
-    expand_codes(cw[c], b);
-    p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag(As, arow, h, c), as_bf16x8(b[0], b[1], b[2], b[3]),
-                                               p, 0, 0, 0);
-  }
-  return p;
-}
-
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_gateup_gemm(LayerArgs L, ChunkArgs C) {
-  const int tile = blockIdx.x;
+template <bool kGateUp>
+__global__ __launch_bounds__(kWaves * 64) void k_expert_gemm(LayerArgs L, ChunkArgs C, int n_ct) {
+  // ---- workgroup -> (tile, column tile), XCD-aware ----
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, m = lin >> 3;
+  const int tile = (m / n_ct) * 8 + xcd, ct = m % n_ct;
   if (tile >= *C.n_tiles) return;
   const int e = C.tiles[3 * tile], r0 = C.tiles[3 * tile + 1], rows = C.tiles[3 * tile + 2];
   const bool shared = e == L.E;
   const int Iw = shared ? L.Is : L.I;
-  const int ct = blockIdx.y;
-  if (ct * 64 >= Iw) return;
+  if (Iw == 0) return;
+  const int H = L.H;
+  // gate/up: columns = intermediate (32-row blocks of gate and up); down: output columns.
+  const int ncols = kGateUp ? Iw : H;
+  const int K = kGateUp ? H : Iw;
+  const int G = K / kGroup;
+  const int cb0 = ct * (kGateUp ? 4 : 8);  // first 32-column block of this column tile
+  if (cb0 * 32 >= ncols) return;
+  const int nvb = min(kGateUp ? 4 : 8, ncols / 32 - cb0);  // valid 32-column blocks (gate/up: per matrix)
 
-  const int H = L.H, G = H / kGroup;
-  const uint8_t* wbase = expert_base(L, e);
+  const uint8_t* ebase = expert_base(L, e);
+  const uint8_t* wbase = kGateUp ? ebase : ebase + (shared ? L.shared_gateup_bytes : L.gateup_bytes);
   const int seg = shared ? 0 : C.offsets[e];
-  const int outbase = shared ? C.Tk + r0 : seg + r0;
+  const int rowbase = shared ? C.Tk + r0 : seg + r0;  // hbuf row of the tile's first row
 
-  extern __shared__ float smem[];
-  float* Xs = smem;                                                      // [64][G]
-  uint16_t* As = reinterpret_cast<uint16_t*>(Xs + kSlab * G);            // [64][72]
-  const uint16_t** rowsrc = reinterpret_cast<const uint16_t**>(As + kSlab * kAStride);  // [64]
-  int* tok = reinterpret_cast<int*>(rowsrc + kSlab);                     // [64]
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* bt = smem;                                       // [2][blk][c][lane] x 16 B
+  int* tok = reinterpret_cast<int*>(smem + 2 * kBufBytes);  // [256]
+  float* wt = reinterpret_cast<float*>(tok + kTileRows);    // [256]
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, col = lane & 31;
-  const int nb = ct * 2 + wn;  // 32-row block of gate/up
-  const int arow = wm * 32 + col;
 
-  for (int slab = 0; slab < rows; slab += kSlab) {
-    const int srows = min(kSlab, rows - slab);
-    __syncthreads();
-    if (threadIdx.x < kSlab) {
-      const int r = threadIdx.x;
-      int t = -1;
-      if (r < srows) t = shared ? r0 + slab + r : C.sorted[seg + r0 + slab + r] / L.k;
-      tok[r] = t;
-      rowsrc[r] = t >= 0 ? C.x + (int64_t)t * H : nullptr;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kSlab * G; i += 256) {
-      const int r = i / G, g = i - r * G;
-      Xs[i] = tok[r] >= 0 ? C.xsum[(int64_t)tok[r] * G + g] : 0.f;
-    }
-
-    f32x16_t accg = {}, accu = {};
-    for (int g = 0; g < G; g++) {
-      const uint8_t* blk = wbase + ((int64_t)(nb * G + g) * 2) * kBlockBytes;
-      const uint4 cg = *reinterpret_cast<const uint4*>(blk + lane * 16);
-      const uint4 cu = *reinterpret_cast<const uint4*>(blk + kBlockBytes + lane * 16);
-      const uint32_t sbg = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
-      const uint32_t sbu = *reinterpret_cast<const uint32_t*>(blk + kBlockBytes + kCodeBytes + col * 4);
-      __syncthreads();
-      stage_a(As, rowsrc, g * kGroup);
-      __syncthreads();
-      const f32x16_t pg = group_mma(As, arow, h, cg);
-      const f32x16_t pu = group_mma(As, arow, h, cu);
-      const float sg = bf16_bits_to_f32(sbg & 0xFFFFu), bg = bf16_bits_to_f32(sbg >> 16);
-      const float su = bf16_bits_to_f32(sbu & 0xFFFFu), bu = bf16_bits_to_f32(sbu >> 16);
-      const float bpg = bg - 128.f * sg, bpu = bu - 128.f * su;
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int r = wm * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-        const float xsr = Xs[r * G + g];
-        accg[i] = fmaf(sg, pg[i], fmaf(bpg, xsr, accg[i]));
-        accu[i] = fmaf(su, pu[i], fmaf(bpu, xsr, accu[i]));
+  // Row metadata: token (and routing weight for down).
+  if (tid < kTileRows) {
+    int t = 0;
+    float w = 0.f;
+    if (tid < rows) {
+      if (shared) {
+        t = r0 + tid;
+        w = 1.f;
+      } else {
+        const int a = C.sorted[seg + r0 + tid];
+        t = a / L.k;
+        w = C.tw[a];
       }
     }
+    tok[tid] = t;
+    wt[tid] = w;
+  }
 
-    // SwiGLU, bf16 store, and the 32-column sums of bf16(h) for the down GEMM.
-    const int hsw = C.Imax / 32;
+  // ---- weight block rebuilt by this wave: LDS block `wave`, lane `lane` ----
+  // gate/up: LDS blocks 0..3 are gate, 4..7 up, column block cb0 + (wave & 3);
+  // down: column block cb0 + wave.
+  const int qj = kGateUp ? (wave & 3) : wave;
+  const bool qvalid = qj < nvb;  // wave-uniform
+  const int qjc = qvalid ? qj : nvb - 1;  // invalid blocks read a valid block and store nothing
+  const uint8_t* qsrc = kGateUp ? wbase + ((int64_t)(cb0 + qjc) * G * 2 + (wave >> 2)) * kBlockBytes
+                                : wbase + (int64_t)(cb0 + qjc) * G * kBlockBytes;
+  const int64_t qstride = kGateUp ? 2 * kBlockBytes : kBlockBytes;
+  uint4* qdst0 = reinterpret_cast<uint4*>(bt) + wave * 4 * 64 + lane;
+
+  __syncthreads();  // tok / wt visible
+
+  // ---- A operand pointers: rows 64*wm + 32*f + col, lane half h ----
+  const uint16_t* aptr[2];
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int r = wm * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-      const uint16_t hb = f32_to_bf16_rne(silu_mul(accg[i], accu[i]));
-      float hs = bf16_bits_to_f32(hb);
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) hs += __shfl_xor(hs, off);
-      if (r < srows) {
-        const int64_t orow = outbase + slab + r;
-        C.hbuf[orow * C.Imax + nb * 32 + col] = hb;
-        if (col == 0) C.hsum[orow * hsw + nb] = hs;
-      }
+  for (int f = 0; f < 2; f++) {
+    const int r = wm * 64 + f * 32 + col;
+    const int rr = r < rows ? r : 0;
+    if (kGateUp) {
+      aptr[f] = C.x16 + (int64_t)tok[rr] * H + h * 32;
+    } else {
+      aptr[f] = C.hbuf + (int64_t)(rowbase + rr) * C.Imax + h * 32;
     }
   }
-}
+  const bool wave_active = __builtin_amdgcn_readfirstlane(wm * 64 < rows ? 1 : 0) != 0;
+  // Wave's weight blocks in the LDS tile.
+  int wblk[4];
+#pragma unroll
+  for (int b = 0; b < 4; b++) wblk[b] = kGateUp ? (b >> 1) * 4 + 2 * wn + (b & 1) : 4 * wn + b;
 
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_down_gemm(LayerArgs L, ChunkArgs C) {
-  const int tile = blockIdx.x;
-  if (tile >= *C.n_tiles) return;
-  const int e = C.tiles[3 * tile], r0 = C.tiles[3 * tile + 1], rows = C.tiles[3 * tile + 2];
-  const bool shared = e == L.E;
-  const int Kw = shared ? L.Is : L.I;
-  if (Kw == 0) return;
-  const int H = L.H;
-  const int ct = blockIdx.y;
-  const int Gk = Kw / kGroup;
-  const uint8_t* wbase = expert_base(L, e) + (shared ? L.shared_gateup_bytes : L.gateup_bytes);
-  const int seg = shared ? 0 : C.offsets[e];
-  const int inbase = shared ? C.Tk + r0 : seg + r0;
-  const int hsw = C.Imax / 32;
+  auto load_a = [&](int g, uint4 (&dst)[2][4]) {
+    const int gg = g < G ? g : G - 1;  // past the end: a valid, unused group
+#pragma unroll
+    for (int f = 0; f < 2; f++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) dst[f][c] = *reinterpret_cast<const uint4*>(aptr[f] + gg * kGroup + c * 8);
+  };
+  auto load_q = [&](int g, uint4& code, uint32_t& sb) {
+    const int gg = g < G ? g : G - 1;
+    const uint8_t* blk = qsrc + gg * qstride;
+    code = *reinterpret_cast<const uint4*>(blk + lane * 16);
+    sb = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
+  };
+  auto dequant_store = [&](int buf, const uint4& code, uint32_t sb) {
+    const float s = bf16_bits_to_f32(sb & 0xFFFFu), b = bf16_bits_to_f32(sb >> 16);
+    uint4* dst = qdst0 + buf * (kBufBytes / 16);
+    dst[0 * 64] = dequant8(code.x, s, b);
+    dst[1 * 64] = dequant8(code.y, s, b);
+    dst[2 * 64] = dequant8(code.z, s, b);
+    dst[3 * 64] = dequant8(code.w, s, b);
+  };
 
-  extern __shared__ float smem[];
-  float* Hs = smem;                                                      // [64][Gk]
-  uint16_t* As = reinterpret_cast<uint16_t*>(Hs + kSlab * Gk);           // [64][72]
-  const uint16_t** rowsrc = reinterpret_cast<const uint16_t**>(As + kSlab * kAStride);
-  int* tok = reinterpret_cast<int*>(rowsrc + kSlab);
-  float* wt = reinterpret_cast<float*>(tok + kSlab);
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int f = 0; f < 2; f++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) acc[f][b] = f32x16_t{};
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5, col = lane & 31;
-  const int nb = ct * 2 + wn;  // 32-row block of down (output columns)
-  const int arow = wm * 32 + col;
+  auto mma_group = [&](int buf, const uint4 (&a)[2][4]) {
+    const uint4* bsrc = reinterpret_cast<const uint4*>(bt + buf * kBufBytes);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      f16x8_t bv[4];
+#pragma unroll
+      for (int b = 0; b < 4; b++) bv[b] = __builtin_bit_cast(f16x8_t, bsrc[(wblk[b] * 4 + c) * 64 + lane]);
+#pragma unroll
+      for (int f = 0; f < 2; f++) {
+        const f16x8_t av = __builtin_bit_cast(f16x8_t, a[f][c]);
+#pragma unroll
+        for (int b = 0; b < 4; b++) acc[f][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[b], acc[f][b], 0, 0, 0);
+      }
+    }
+  };
 
-  for (int slab = 0; slab < rows; slab += kSlab) {
-    const int srows = min(kSlab, rows - slab);
+  // Prologue: group 0 weights into buffer 0; A of group 0; codes of group 1.
+  uint4 a0[2][4], a1[2][4];
+  uint4 qc0, qc1;
+  uint32_t qs0, qs1;
+  load_q(0, qc0, qs0);
+  load_a(0, a0);
+  if (qvalid) dequant_store(0, qc0, qs0);
+  load_q(1, qc1, qs1);
+  __syncthreads();
+
+  // Two groups per iteration; register sets and LDS buffers alternate.
+  for (int g = 0; g < G; g += 2) {
+    // even group g: A in a0, weights in buffer 0, codes of g+1 in qc1.
+    load_a(g + 1, a1);
+    if (qvalid && g + 1 < G) dequant_store(1, qc1, qs1);
+    load_q(g + 2, qc0, qs0);
+    if (wave_active) mma_group(0, a0);
     __syncthreads();
-    if (threadIdx.x < kSlab) {
-      const int r = threadIdx.x;
-      int t = -1;
-      float w = 0.f;
-      const uint16_t* src = nullptr;
-      if (r < srows) {
-        const int64_t irow = inbase + slab + r;
-        if (shared) {
-          t = r0 + slab + r;
-          w = 1.f;
-        } else {
-          const int a = C.sorted[irow];
-          t = a / L.k;
-          w = C.tw[a];
+    if (g + 1 >= G) break;
+    // odd group g+1: A in a1, weights in buffer 1, codes of g+2 in qc0.
+    load_a(g + 2, a0);
+    if (qvalid && g + 2 < G) dequant_store(0, qc0, qs0);
+    load_q(g + 3, qc1, qs1);
+    if (wave_active) mma_group(1, a1);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  // ---- epilogue: undo the 2^-8 activation scale ----
+  if (kGateUp) {
+#pragma unroll
+    for (int f = 0; f < 2; f++) {
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        if (2 * wn + j >= nvb) continue;
+        const int icol = (cb0 + 2 * wn + j) * 32 + col;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int r = wm * 64 + f * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (r < rows) {
+            const float hv = silu_mul(256.f * acc[f][j][i], 256.f * acc[f][j + 2][i]);
+            C.hbuf[(int64_t)(rowbase + r) * C.Imax + icol] = f32_to_f16_bits(hv * (1.f / 256.f));
+          }
         }
-        src = C.hbuf + irow * C.Imax;
       }
-      tok[r] = t;
-      wt[r] = w;
-      rowsrc[r] = src;
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kSlab * Gk; i += 256) {
-      const int r = i / Gk, g = i - r * Gk;
-      float v = 0.f;
-      if (r < srows) {
-        const float* hp = C.hsum + (int64_t)(inbase + slab + r) * hsw + 2 * g;
-        v = hp[0] + hp[1];
-      }
-      Hs[i] = v;
-    }
-
-    f32x16_t acc = {};
-    for (int g = 0; g < Gk; g++) {
-      const uint8_t* blk = wbase + (int64_t)(nb * Gk + g) * kBlockBytes;
-      const uint4 cd = *reinterpret_cast<const uint4*>(blk + lane * 16);
-      const uint32_t sb = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
-      __syncthreads();
-      stage_a(As, rowsrc, g * kGroup);
-      __syncthreads();
-      const f32x16_t p = group_mma(As, arow, h, cd);
-      const float s = bf16_bits_to_f32(sb & 0xFFFFu), b = bf16_bits_to_f32(sb >> 16);
-      const float bp = b - 128.f * s;
+  } else {
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int r = wm * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-        acc[i] = fmaf(s, p[i], fmaf(bp, Hs[r * Gk + g], acc[i]));
-      }
-    }
-
+    for (int f = 0; f < 2; f++) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int r = wm * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-      if (r < srows) atomicAdd(C.y + (int64_t)tok[r] * H + nb * 32 + col, wt[r] * acc[i]);
+      for (int b = 0; b < 4; b++) {
+        if (4 * wn + b >= nvb) continue;
+        const int ocol = (cb0 + 4 * wn + b) * 32 + col;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int r = wm * 64 + f * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (r < rows) atomicAdd(C.y + (int64_t)tok[r] * H + ocol, wt[r] * (256.f * acc[f][b][i]));
+        }
+      }
     }
   }
 }
@@ -238,22 +272,28 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s) {
-  const int G = L.H / kGroup;
+template <bool kGateUp>
+static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm<kGateUp>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  const size_t smem = (size_t)kSlab * G * 4 + (size_t)kSlab * kAStride * 2 + kSlab * 8 + kSlab * 4;
-  dim3 grid(max_tiles, Imax / 64);
-  k_gateup_gemm<<<grid, dim3(256), smem, s>>>(L, C);
+  const int n_ct = kGateUp ? (Imax + 127) / 128 : (L.H + 255) / 256;
+  const int tiles8 = (max_tiles + 7) / 8 * 8;
+  k_expert_gemm<kGateUp><<<dim3((unsigned)(tiles8 * n_ct)), dim3(kWaves * 64), kSmem, s>>>(L, C, n_ct);
   return hipGetLastError();
 }
 
+hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s) {
+  return launch_expert_gemm<true>(L, C, max_tiles, s);
+}
+
 hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s) {
-  const int Imax = L.I > L.Is ? L.I : L.Is;
-  const int Gk = Imax / kGroup;
-  const size_t smem = (size_t)kSlab * Gk * 4 + (size_t)kSlab * kAStride * 2 + kSlab * 8 + kSlab * 8;
-  dim3 grid(max_tiles, L.H / 64);
-  k_down_gemm<<<grid, dim3(256), smem, s>>>(L, C);
-  return hipGetLastError();
+  return launch_expert_gemm<false>(L, C, max_tiles, s);
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {

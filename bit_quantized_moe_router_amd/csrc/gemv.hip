@@ -6,10 +6,12 @@
 // With one to a few rows the layer is bound by weight bytes, so each expert's
 // packed weights are streamed once: a wave reads one 1152-byte block (32
 // output rows x one 64-column group) with a single 16-byte load per lane, so a
-// lane holds 32 codes of one output row.  Codes expand to bf16 pairs
-// (128 + q) and meet the activation pairs in v_dot2_f32_bf16; the per-group
-// affine fold is acc += s * dot + (b - 128 s) * sum(x over the group).  The
-// two lanes that share an output row are combined with one cross-half
+// lane holds 32 codes of one output row.  Every wave issues the loads of
+// several blocks before it computes, so most of the working set is in flight
+// at once.  Codes expand to bf16 pairs (128 + q) and meet the activation pairs
+// in v_dot2_f32_bf16; the per-group affine fold is
+//   acc += s * dot + (b - 128 s) * sum(x over the group).
+// The two lanes that share an output row are combined with one cross-half
 // shuffle, the waves of a workgroup through LDS.  No atomics: every output is
 // produced by exactly one workgroup, in a fixed order.
 #include "launch.h"
@@ -17,13 +19,16 @@
 namespace moe {
 
 constexpr int kGemvMaxRows = 8;
-constexpr int kGemvWaves = 4;
+constexpr int kGuWaves = 8;    // gate/up workgroup: 8 waves split the H/64 groups
+constexpr int kGuPref = 4;     // groups per wave whose loads are issued together
+constexpr int kDnWaves = 16;   // down workgroup: 16 waves split the (expert, group) items
+constexpr int kDnPref = 4;
 
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU.  grid = (expert slots: active experts, then the shared
-// expert; I/32 row blocks).  Waves split the H/64 groups.
+// expert; I/32 row blocks).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_gemv_gateup(LayerArgs L, ChunkArgs C) {
+__global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, ChunkArgs C) {
   const int slot = blockIdx.x;
   const int nact = *C.n_active;
   const bool shared = slot == nact;
@@ -35,11 +40,32 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(LayerArgs L, ChunkArgs C) {
   const int rows = shared ? C.T : C.counts[e];
   const int seg = shared ? 0 : C.offsets[e];
   const int H = L.H, G = H / kGroup;
-  const uint8_t* wbase = expert_base(L, e);
+  const uint8_t* wbase = expert_base(L, e) + (int64_t)nb * G * 2 * kBlockBytes;
 
   extern __shared__ uint16_t xl[];  // [rows][H]
   __shared__ int tok[kGemvMaxRows], orow[kGemvMaxRows];
-  __shared__ float red[kGemvWaves][kGemvMaxRows][2][32];
+  __shared__ float red[kGuWaves][kGemvMaxRows][2][32];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = lane >> 5, col = lane & 31;
+
+  // Issue this wave's first weight loads before anything else.
+  uint4 cg[kGuPref], cu[kGuPref];
+  uint32_t sbg[kGuPref], sbu[kGuPref];
+  auto load = [&](int g0) {
+#pragma unroll
+    for (int p = 0; p < kGuPref; p++) {
+      const int g = g0 + p * kGuWaves;
+      if (g < G) {
+        const uint8_t* blk = wbase + (int64_t)g * 2 * kBlockBytes;
+        cg[p] = *reinterpret_cast<const uint4*>(blk + lane * 16);
+        cu[p] = *reinterpret_cast<const uint4*>(blk + kBlockBytes + lane * 16);
+        sbg[p] = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
+        sbu[p] = *reinterpret_cast<const uint32_t*>(blk + kBlockBytes + kCodeBytes + col * 4);
+      }
+    }
+  };
+  load(wave);
+
   if (threadIdx.x < rows) {
     const int r = threadIdx.x;
     tok[r] = shared ? r : C.sorted[seg + r] / L.k;
@@ -53,48 +79,47 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(LayerArgs L, ChunkArgs C) {
   }
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = lane >> 5, col = lane & 31;
   float accg[kGemvMaxRows], accu[kGemvMaxRows];
 #pragma unroll
   for (int j = 0; j < kGemvMaxRows; j++) accg[j] = accu[j] = 0.f;
 
-  for (int g = wave; g < G; g += kGemvWaves) {
-    const uint8_t* blk = wbase + ((int64_t)(nb * G + g) * 2) * kBlockBytes;
-    const uint4 cg = *reinterpret_cast<const uint4*>(blk + lane * 16);
-    const uint4 cu = *reinterpret_cast<const uint4*>(blk + kBlockBytes + lane * 16);
-    const uint32_t sbg = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
-    const uint32_t sbu = *reinterpret_cast<const uint32_t*>(blk + kBlockBytes + kCodeBytes + col * 4);
-    uint32_t qg[16], qu[16];
-    expand_codes(cg.x, qg + 0);
-    expand_codes(cg.y, qg + 4);
-    expand_codes(cg.z, qg + 8);
-    expand_codes(cg.w, qg + 12);
-    expand_codes(cu.x, qu + 0);
-    expand_codes(cu.y, qu + 4);
-    expand_codes(cu.z, qu + 8);
-    expand_codes(cu.w, qu + 12);
-    const float sg = bf16_bits_to_f32(sbg & 0xFFFFu), bpg = bf16_bits_to_f32(sbg >> 16) - 128.f * sg;
-    const float su = bf16_bits_to_f32(sbu & 0xFFFFu), bpu = bf16_bits_to_f32(sbu >> 16) - 128.f * su;
+  for (int g0 = wave; g0 < G; g0 += kGuPref * kGuWaves) {
+    if (g0 != wave) load(g0);
 #pragma unroll
-    for (int j = 0; j < kGemvMaxRows; j++) {
-      if (j < rows) {
-        const uint4* xp = reinterpret_cast<const uint4*>(xl + j * H + g * kGroup + h * 32);
-        float dg = 0.f, du = 0.f;
+    for (int p = 0; p < kGuPref; p++) {
+      const int g = g0 + p * kGuWaves;
+      if (g >= G) break;
+      uint32_t qg[16], qu[16];
+      expand_codes(cg[p].x, qg + 0);
+      expand_codes(cg[p].y, qg + 4);
+      expand_codes(cg[p].z, qg + 8);
+      expand_codes(cg[p].w, qg + 12);
+      expand_codes(cu[p].x, qu + 0);
+      expand_codes(cu[p].y, qu + 4);
+      expand_codes(cu[p].z, qu + 8);
+      expand_codes(cu[p].w, qu + 12);
+      const float sg = bf16_bits_to_f32(sbg[p] & 0xFFFFu), bpg = bf16_bits_to_f32(sbg[p] >> 16) - 128.f * sg;
+      const float su = bf16_bits_to_f32(sbu[p] & 0xFFFFu), bpu = bf16_bits_to_f32(sbu[p] >> 16) - 128.f * su;
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-          const uint4 xv = xp[c];
-          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      for (int j = 0; j < kGemvMaxRows; j++) {
+        if (j < rows) {
+          const uint4* xp = reinterpret_cast<const uint4*>(xl + j * H + g * kGroup + h * 32);
+          float dg = 0.f, du = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            dg = dot2_bf16(qg[4 * c + i], xw[i], dg);
-            du = dot2_bf16(qu[4 * c + i], xw[i], du);
+          for (int c = 0; c < 4; c++) {
+            const uint4 xv = xp[c];
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              dg = dot2_bf16(qg[4 * c + i], xw[i], dg);
+              du = dot2_bf16(qu[4 * c + i], xw[i], du);
+            }
           }
+          // The group's activation sum covers both lane halves: fold it in once.
+          const float xs = h == 0 ? C.xsum[(int64_t)tok[j] * G + g] : 0.f;
+          accg[j] = fmaf(sg, dg, fmaf(bpg, xs, accg[j]));
+          accu[j] = fmaf(su, du, fmaf(bpu, xs, accu[j]));
         }
-        // The group's activation sum covers both lane halves: fold it in once.
-        const float xs = h == 0 ? C.xsum[(int64_t)tok[j] * G + g] : 0.f;
-        accg[j] = fmaf(sg, dg, fmaf(bpg, xs, accg[j]));
-        accu[j] = fmaf(su, du, fmaf(bpu, xs, accu[j]));
       }
     }
   }
@@ -110,71 +135,97 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(LayerArgs L, ChunkArgs C) {
     }
   }
   __syncthreads();
-  // Thread 32*j + n finishes row j, column n (256 threads = 8 rows x 32 columns).
-  const int j = threadIdx.x >> 5, n = threadIdx.x & 31;
-  const bool ok = j < rows;
-  float gs = 0.f, us = 0.f;
-  if (ok) {
+  // Thread 32*j + n finishes row j, column n.
+  for (int base = 0; base < kGemvMaxRows * 32; base += blockDim.x) {
+    const int j = (base + threadIdx.x) >> 5, n = threadIdx.x & 31;
+    const bool ok = j < rows;
+    float gs = 0.f, us = 0.f;
+    if (ok) {
 #pragma unroll
-    for (int w = 0; w < kGemvWaves; w++) {
-      gs += red[w][j][0][n];
-      us += red[w][j][1][n];
+      for (int w = 0; w < kGuWaves; w++) {
+        gs += red[w][j][0][n];
+        us += red[w][j][1][n];
+      }
     }
-  }
-  const uint16_t hb = f32_to_bf16_rne(silu_mul(gs, us));
-  float hs = ok ? bf16_bits_to_f32(hb) : 0.f;
+    const uint16_t hb = f32_to_bf16_rne(silu_mul(gs, us));
+    float hs = ok ? bf16_bits_to_f32(hb) : 0.f;
 #pragma unroll
-  for (int off = 1; off < 32; off <<= 1) hs += __shfl_xor(hs, off);
-  if (ok) {
-    C.hbuf[(int64_t)orow[j] * C.Imax + nb * 32 + n] = hb;
-    if (n == 0) C.hsum[(int64_t)orow[j] * (C.Imax / 32) + nb] = hs;
+    for (int off = 1; off < 32; off <<= 1) hs += __shfl_xor(hs, off);
+    if (ok) {
+      C.hbuf[(int64_t)orow[j] * C.Imax + nb * 32 + n] = hb;
+      if (n == 0) C.hsum[(int64_t)orow[j] * (C.Imax / 32) + nb] = hs;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // down + routing weight + shared add + combine.  grid = H/32 output row
 // blocks; the workgroup walks every (expert slot, group) item, waves taking
-// items round-robin, and writes y for all tokens of the chunk.
+// items round-robin with their loads issued in batches, and writes y for all
+// tokens of the chunk.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_gemv_down(LayerArgs L, ChunkArgs C) {
+__global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkArgs C) {
   const int nb = blockIdx.x;
   const int nact = *C.n_active;
-  const int nslots = nact + (L.Is > 0 ? 1 : 0);
   const int H = L.H, T = C.T;
   const int hsw = C.Imax / 32;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, col = lane & 31;
-  __shared__ float red[kGemvWaves][kGemvMaxRows][32];
+  const int Gi = L.I / kGroup, Gs = L.Is / kGroup;
+  const int nitems = nact * Gi + Gs;
+  __shared__ float red[kDnWaves][kGemvMaxRows][32];
 
   float acc[kGemvMaxRows];
 #pragma unroll
   for (int t = 0; t < kGemvMaxRows; t++) acc[t] = 0.f;
 
-  int item = 0;
-  for (int slot = 0; slot < nslots; slot++) {
-    const bool shared = slot == nact;
-    const int e = shared ? L.E : C.active[slot];
-    const int Kw = shared ? L.Is : L.I;
-    const int Gk = Kw / kGroup;
-    const int rows = shared ? T : C.counts[e];
-    const int seg = shared ? 0 : C.offsets[e];
-    const uint8_t* wbase = expert_base(L, e) + (shared ? L.shared_gateup_bytes : L.gateup_bytes);
-    for (int g = 0; g < Gk; g++, item++) {
-      if ((item % kGemvWaves) != wave) continue;
-      const uint8_t* blk = wbase + (int64_t)(nb * Gk + g) * kBlockBytes;
-      const uint4 cd = *reinterpret_cast<const uint4*>(blk + lane * 16);
-      const uint32_t sb = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
+  uint4 cd[kDnPref];
+  uint32_t sb[kDnPref];
+  int pe[kDnPref], pg[kDnPref];
+  for (int it0 = wave; it0 < nitems; it0 += kDnPref * kDnWaves) {
+#pragma unroll
+    for (int p = 0; p < kDnPref; p++) {
+      const int it = it0 + p * kDnWaves;
+      pe[p] = -1;
+      pg[p] = 0;
+      if (it < nitems) {
+        int e, g;
+        if (it < nact * Gi) {
+          const int s = it / Gi;
+          e = C.active[s];
+          g = it - s * Gi;
+        } else {
+          e = L.E;
+          g = it - nact * Gi;
+        }
+        const bool sh = e == L.E;
+        const int Gk = sh ? Gs : Gi;
+        const uint8_t* blk = expert_base(L, e) + (sh ? L.shared_gateup_bytes : L.gateup_bytes) +
+                             (int64_t)(nb * Gk + g) * kBlockBytes;
+        cd[p] = *reinterpret_cast<const uint4*>(blk + lane * 16);
+        sb[p] = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
+        pe[p] = e;
+        pg[p] = g;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kDnPref; p++) {
+      if (pe[p] < 0) break;
+      const int e = pe[p], g = pg[p];
+      const bool sh = e == L.E;
+      const int rows = sh ? T : C.counts[e];
+      const int seg = sh ? 0 : C.offsets[e];
       uint32_t q[16];
-      expand_codes(cd.x, q + 0);
-      expand_codes(cd.y, q + 4);
-      expand_codes(cd.z, q + 8);
-      expand_codes(cd.w, q + 12);
-      const float s = bf16_bits_to_f32(sb & 0xFFFFu), bp = bf16_bits_to_f32(sb >> 16) - 128.f * s;
+      expand_codes(cd[p].x, q + 0);
+      expand_codes(cd[p].y, q + 4);
+      expand_codes(cd[p].z, q + 8);
+      expand_codes(cd[p].w, q + 12);
+      const float s = bf16_bits_to_f32(sb[p] & 0xFFFFu), bp = bf16_bits_to_f32(sb[p] >> 16) - 128.f * s;
       for (int j = 0; j < rows; j++) {
-        const int64_t irow = shared ? C.Tk + j : seg + j;
+        const int64_t irow = sh ? C.Tk + j : seg + j;
         int t;
         float w;
-        if (shared) {
+        if (sh) {
           t = j;
           w = 1.f;
         } else {
@@ -212,7 +263,7 @@ __global__ __launch_bounds__(256) void k_gemv_down(LayerArgs L, ChunkArgs C) {
     const int t = i >> 5, n = i & 31;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kGemvWaves; w++) v += red[w][t][n];
+    for (int w = 0; w < kDnWaves; w++) v += red[w][t][n];
     C.y[(int64_t)t * H + nb * 32 + n] = v;
   }
 }
@@ -223,12 +274,12 @@ hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_
   const int slots = (L.E < C.Tk ? L.E : C.Tk) + 1;
   dim3 grid(slots, Imax / 32);
   const size_t smem = (size_t)C.T * L.H * 2;
-  k_gemv_gateup<<<grid, dim3(256), smem, s>>>(L, C);
+  k_gemv_gateup<<<grid, dim3(kGuWaves * 64), smem, s>>>(L, C);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s) {
-  k_gemv_down<<<dim3(L.H / 32), dim3(256), 0, s>>>(L, C);
+  k_gemv_down<<<dim3(L.H / 32), dim3(kDnWaves * 64), 0, s>>>(L, C);
   return hipGetLastError();
 }
 

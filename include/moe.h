@@ -72,8 +72,8 @@ typedef struct {
                               T <= R* and the grouped GEMM path above; -1 = library default;
                               0 = always GEMM; at most 8 */
     int32_t max_chunk;     /* tokens per prefill chunk (1..8192); routing metadata is per chunk */
-    int32_t tile_rows;     /* BM: rows per tile of the block map; 0 = library default (64);
-                              one of 16, 32, 64, 128 */
+    int32_t tile_rows;     /* BM: rows per tile of the block map; 0 = library default (256);
+                              one of 16, 32, 64, 128, 256 */
 } moe_layer_desc;
 
 /*
@@ -179,15 +179,18 @@ const char *moe_status_str(moe_status s);
 const char *moe_last_error(void);
 
 /*
- * Kernel timing for measurement tools.  While enabled, the library records a
- * HIP event pair around every launch of the kernels named below, on the
- * launch stream.  moe_profile_read synchronises on those events, returns the
+ * Kernel timing for measurement tools.  moe_profile_enable(mask) makes the
+ * library record a HIP event pair, on the launch stream, around every launch
+ * of the kernels whose bit is set in `mask` (bit i = kernel id i; 0 turns
+ * timing off).  moe_profile_read synchronises on those events and returns the
  * summed duration (ms) and launch count of kernel `kernel_id` since the last
- * reset, and never runs on the forward path.  Not thread-safe.
- *   0 = router logits, 1 = top-k, 2 = routing metadata, 3 = gate/up grouped
- *   GEMM, 4 = down grouped GEMM, 5 = gate/up GEMV, 6 = down GEMV
+ * reset.  Never needed on the forward path.  Not thread-safe.
+ *   0 = router logits (screen, or exact for T <= 8), 1 = exact top-k
+ *   selection (T > 8), 2 = routing metadata (with top-k for T <= 8),
+ *   3 = gate/up grouped GEMM, 4 = down grouped GEMM, 5 = gate/up GEMV,
+ *   6 = down GEMV
  */
-moe_status moe_profile_enable(int32_t on);
+moe_status moe_profile_enable(int32_t mask);
 moe_status moe_profile_reset(void);
 moe_status moe_profile_read(int32_t kernel_id, double *total_ms, int32_t *launches);
 

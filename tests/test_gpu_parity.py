@@ -132,7 +132,7 @@ ROUTE_CASES = ["tiny", "decode", "smallrow2", "smallrow5", "smallrow8", "prefill
 def test_route_bitexact(M, name):
     case = mi.make_case(name)
     lay = get_layer(M, case)
-    BM = lay.desc.tile_rows or 64
+    BM = lay.desc.tile_rows or 256  # library default
     x, bias = case["x"], case["bias"]
     for c0 in range(0, case["T"], mi.CHUNK):
         xc = x[c0:c0 + mi.CHUNK]
@@ -259,3 +259,33 @@ def test_zero_tokens_is_noop(M):
     moe_forward_prefill(lay.desc, lay.packed, lay.router_w, None, x, 0, y, lay.ws)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+# ---- routing corner cases: exact ties and degenerate router weights ---------------
+
+@pytest.mark.parametrize("T", [4, 64, 300])
+def test_route_exact_ties(M, T):
+    """Pairs of identical router rows give exactly equal logits; the lower expert must win."""
+    case = mi.small_layer(T, 256, 32, 4, 64, 64, seed=71)
+    w = case["w"]
+    w["router_w"][1::2] = w["router_w"][0::2]
+    lay = M.MoELayer(w, 4, max_tokens=T, max_chunk=2048, tile_rows=16)
+    r = lay.route(dev(M, case["x"]), None)
+    torch.cuda.synchronize()
+    ref = orc.route(case["x"], w["router_w"], None, 4, 16)
+    check_route(r, ref, f"ties T={T}")
+    assert np.all(ref["topk_ids"][:, 0] % 2 == 0)
+
+
+@pytest.mark.parametrize("T", [3, 40])
+def test_route_zero_router_with_bias(M, T):
+    case = mi.small_layer(T, 128, 24, 5, 64, 0, seed=81)
+    w = case["w"]
+    w["router_w"][...] = 0
+    bias = np.linspace(1.0, -1.0, 24).astype(np.float32)
+    lay = M.MoELayer(w, 5, max_tokens=T, max_chunk=2048, tile_rows=16)
+    r = lay.route(dev(M, case["x"]), dev(M, bias))
+    torch.cuda.synchronize()
+    ref = orc.route(case["x"], w["router_w"], bias, 5, 16, with_shared=False)
+    check_route(r, ref, f"zero router T={T}")
+    assert np.array_equal(ref["topk_ids"], np.tile(np.arange(5, dtype=np.int32), (T, 1)))
