@@ -140,7 +140,7 @@ def main():
         for i in range(a.steps):
             step(i)
 
-    kern_all = breakdown(prefill_pass, [moe.K_LOGITS, moe.K_TOPK, moe.K_META, moe.K_DOWN_GEMM])
+    kern_all = breakdown(prefill_pass, [moe.K_LOGITS, moe.K_TOPK, moe.K_META, moe.K_DOWN_GEMM, moe.K_COMBINE])
 
     # Dominant kernel: gate/up grouped GEMM, one launch per 2048-token chunk.
     Tc = 2048

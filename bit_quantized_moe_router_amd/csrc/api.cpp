@@ -86,7 +86,8 @@ Blob blob_geom(const moe_layer_desc* d) {
 }
 
 struct Ws {
-  size_t logits, wnorm, xsum, x16, ids, tw, counts, offsets, sorted, tiles, n_tiles, active, n_active, hbuf, hsum;
+  size_t logits, wnorm, xsum, x16, ids, tw, counts, offsets, sorted, inv, tiles, sched, n_tiles, active, n_active,
+      hbuf, hsum, obuf;
   size_t total;
 };
 
@@ -97,8 +98,8 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   const int64_t rows = Tc * k + Tc;
   Ws w;
   size_t o = 0;
-  w.logits = o; o += al(Tc * E * 4);
-  w.wnorm = o; o += al(E * 4);
+  w.logits = o; o += al(4 * Tc * E * 4);  // 4 partial slices of the screened logits
+  w.wnorm = o; o += al(4 * E * 8);
   w.xsum = o; o += al(Tc * (H / 64) * 4);
   w.x16 = o; o += al(Tc * H * 2);
   w.ids = o; o += al(Tc * k * 4);
@@ -106,12 +107,15 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   w.counts = o; o += al(E * 4);
   w.offsets = o; o += al((E + 1) * 4);
   w.sorted = o; o += al(Tc * k * 4);
+  w.inv = o; o += al(Tc * k * 4);
   w.tiles = o; o += al(max_tiles_for(d, Tc) * 3 * 4);
+  w.sched = o; o += al(max_tiles_for(d, Tc) * 4);
   w.n_tiles = o; o += al(4);
   w.active = o; o += al(E * 4);
   w.n_active = o; o += al(4);
   w.hbuf = o; o += al(rows * Im * 2);
   w.hsum = o; o += al(rows * (Im / 32) * 4);
+  w.obuf = o; o += al(Tc * k * H * 2);
   w.total = o;
   return w;
 }
@@ -142,7 +146,7 @@ moe_status check_device() {
 }
 
 // ---- kernel timing (measurement mode) ----------------------------------------
-constexpr int kNumKernels = 7;
+constexpr int kNumKernels = 8;
 struct Pending {
   int kid;
   hipEvent_t a, b;
@@ -209,8 +213,9 @@ LayerArgs layer_args(const moe_layer_desc* d, const void* packed) {
 }
 
 struct RouteOut {
-  int32_t *ids, *counts, *offsets, *sorted, *tiles, *n_tiles, *active, *n_active;
-  float *tw, *logits, *wnorm, *xsum;
+  int32_t *ids, *counts, *offsets, *sorted, *inv, *tiles, *sched, *n_tiles, *active, *n_active;
+  float *tw, *logits, *xsum;
+  double* wsq;
   uint16_t* x16;
 };
 
@@ -219,21 +224,22 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
   const int E = d->n_experts, k = d->top_k, H = d->hidden;
   bool two = false;
   TRY(timed(0, s, "router logits", [&] {
-    return launch_route_logits(x, T, H, wr, bias, E, k, o.logits, o.wnorm, o.ids, o.tw, o.xsum, o.x16, s, &two);
+    return launch_route_logits(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.xsum, o.x16, s, &two);
   }));
   if (!two) {
     // Few tokens: exact logits are already there; top-k + metadata in one launch.
     return timed(2, s, "top-k + routing metadata", [&] {
       return launch_topk_meta(o.logits, T, E, k, o.ids, o.tw, tile_rows(d), d->shared_inter > 0 ? 1 : 0,
-                              o.counts, o.offsets, o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, s);
+                              o.counts, o.offsets, o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv,
+                              o.sched, s);
     });
   }
   TRY(timed(1, s, "top-k", [&] {
-    return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wnorm, o.ids, o.tw, o.xsum, o.x16, s);
+    return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.xsum, o.x16, s);
   }));
   TRY(timed(2, s, "routing metadata", [&] {
     return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, o.counts, o.offsets,
-                       o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, s);
+                       o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv, o.sched, s);
   }));
   return MOE_OK;
 }
@@ -241,7 +247,7 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
 RouteOut ws_route(void* ws, const Ws& w) {
   RouteOut o;
   o.logits = at<float>(ws, w.logits);
-  o.wnorm = at<float>(ws, w.wnorm);
+  o.wsq = at<double>(ws, w.wnorm);
   o.xsum = at<float>(ws, w.xsum);
   o.x16 = at<uint16_t>(ws, w.x16);
   o.ids = at<int32_t>(ws, w.ids);
@@ -249,7 +255,9 @@ RouteOut ws_route(void* ws, const Ws& w) {
   o.counts = at<int32_t>(ws, w.counts);
   o.offsets = at<int32_t>(ws, w.offsets);
   o.sorted = at<int32_t>(ws, w.sorted);
+  o.inv = at<int32_t>(ws, w.inv);
   o.tiles = at<int32_t>(ws, w.tiles);
+  o.sched = at<int32_t>(ws, w.sched);
   o.n_tiles = at<int32_t>(ws, w.n_tiles);
   o.active = at<int32_t>(ws, w.active);
   o.n_active = at<int32_t>(ws, w.n_active);
@@ -269,12 +277,15 @@ ChunkArgs chunk_args(const moe_layer_desc* d, const uint16_t* x, int Tc, const R
   C.counts = o.counts;
   C.offsets = o.offsets;
   C.sorted = o.sorted;
+  C.inv = o.inv;
   C.tiles = o.tiles;
+  C.sched = o.sched;
   C.n_tiles = o.n_tiles;
   C.active = o.active;
   C.n_active = o.n_active;
   C.hbuf = at<uint16_t>(ws, w.hbuf);
   C.hsum = at<float>(ws, w.hsum);
+  C.obuf = at<uint16_t>(ws, w.obuf);
   C.y = y;
   C.Imax = imax(d);
   return C;
@@ -300,9 +311,9 @@ moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_
   TRY(run_route(d, x, Tc, wr, bias, o, s));
   const ChunkArgs C = chunk_args(d, x, Tc, o, ws, w, y);
   const int mt = (int)max_tiles_for(d, Tc);
-  TRY(timed(-1, s, "zero y", [&] { return launch_fill_zero(y, (int64_t)Tc * d->hidden, s); }));
   TRY(timed(3, s, "gate/up GEMM", [&] { return launch_gateup_gemm(L, C, mt, s); }));
   TRY(timed(4, s, "down GEMM", [&] { return launch_down_gemm(L, C, mt, s); }));
+  TRY(timed(7, s, "combine", [&] { return launch_combine(L, C, s); }));
   return MOE_OK;
 }
 

@@ -65,12 +65,15 @@ struct ChunkArgs {
   const int32_t* counts;  // [E]
   const int32_t* offsets; // [E+1]
   const int32_t* sorted;  // [T*k]
+  const int32_t* inv;     // [T*k] inverse of sorted: position of assignment t*k+j
   const int32_t* tiles;   // [..][3]
   const int32_t* n_tiles; // [1]
+  const int32_t* sched;   // [n_tiles] tile indices in execution order (longest first)
   const int32_t* active;  // [E] experts with rows, increasing
   const int32_t* n_active;// [1]
   uint16_t* hbuf;         // [T*k + T][Imax]: fp16(h / 256) on the GEMM path, bf16 h on the GEMV path
   float* hsum;            // [T*k + T][Imax/32] GEMV path: sums of bf16(h) over 32-column halves of a group
+  uint16_t* obuf;         // [T*k][H] GEMM path: fp16(routed expert output / 256) per sorted position
   float* y;               // [T][H]
   int Imax;               // row stride of hbuf
 };

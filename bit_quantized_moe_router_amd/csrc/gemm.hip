@@ -40,7 +40,8 @@
 //
 // Workgroup ids are mapped so that the column tiles of one row tile run on the
 // same XCD back to back (dispatch is round-robin over the 8 XCDs), which
-// keeps the tile's activation rows in that XCD's L2.
+// keeps the tile's activation rows in that XCD's L2; row tiles run in the
+// routing kernel's longest-first order (full tiles before partial ones).
 #include "launch.h"
 
 namespace moe {
@@ -49,25 +50,36 @@ constexpr int kTileRows = 256;
 constexpr int kWaves = 8;
 constexpr int kBlocks = 8;                           // 32-column weight blocks per tile
 constexpr int kBufBytes = kBlocks * kCodeBytes * 4;  // fp16 tile of one group: 8 x 4 x 64 x 16 B
-constexpr int kSmem = 2 * kBufBytes + kTileRows * 8; // + token / weight per row
+constexpr int kARow = 144;                           // bytes per A row in LDS: 64 fp16 + 16 B pad
+constexpr int kABufBytes = kTileRows * kARow;        // one group of A rows
+constexpr int kSmem = 2 * kBufBytes + 2 * kABufBytes + kTileRows * 4;  // + token per row
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-// 8 codes of one packed dword -> 8 fp16 weights w = s*q + b (round to nearest
-// even), in k order, as four dwords of fp16 pairs.
-__device__ __forceinline__ uint4 dequant8(uint32_t d, float s, float b) {
-  uint32_t e = d & 0x0F0F0F0Fu;         // bytes: q0 q4 q1 q5
-  uint32_t o = (d >> 4) & 0x0F0F0F0Fu;  // bytes: q2 q6 q3 q7
-  asm("" : "+v"(e), "+v"(o));            // keep the masks; bytes convert with v_cvt_f32_ubyteN
-  const float w0 = fmaf((float)(e & 0xFFu), s, b), w1 = fmaf((float)((e >> 16) & 0xFFu), s, b);
-  const float w2 = fmaf((float)(o & 0xFFu), s, b), w3 = fmaf((float)((o >> 16) & 0xFFu), s, b);
-  const float w4 = fmaf((float)((e >> 8) & 0xFFu), s, b), w5 = fmaf((float)(e >> 24), s, b);
-  const float w6 = fmaf((float)((o >> 8) & 0xFFu), s, b), w7 = fmaf((float)(o >> 24), s, b);
-  f16x2_t p0 = {(_Float16)w0, (_Float16)w1}, p1 = {(_Float16)w2, (_Float16)w3};
-  f16x2_t p2 = {(_Float16)w4, (_Float16)w5}, p3 = {(_Float16)w6, (_Float16)w7};
-  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+
+// (a & mask) | magic in one VALU op.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask), "v"(magic));
+  return r;
+}
+
+// 8 codes of one packed dword -> 8 fp16 weights w = s*q + b in k order, as
+// four dwords of fp16 pairs.  Pair i of codes sits in nibbles i and 4+i, so
+// ((d >> 4i) & 0x000F000F) | 0x64006400 is the fp16 pair (1024 + q, 1024 + q')
+// (fp16 0x6400 = 1024 and its 10 mantissa bits step by 1); subtracting 1024 is
+// exact, and one packed fp16 FMA per pair rounds s*q + b once.
+__device__ __forceinline__ uint4 dequant8(uint32_t d, f16x2v_t s2, f16x2v_t b2, uint32_t mask, uint32_t magic) {
+  const f16x2v_t off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const f16x2v_t q = __builtin_bit_cast(f16x2v_t, and_or(d >> (4 * i), mask, magic)) + off;
+    w[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
@@ -79,8 +91,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_expert_gemm(LayerArgs L, ChunkA
   // ---- workgroup -> (tile, column tile), XCD-aware ----
   const int lin = blockIdx.x;
   const int xcd = lin & 7, m = lin >> 3;
-  const int tile = (m / n_ct) * 8 + xcd, ct = m % n_ct;
-  if (tile >= *C.n_tiles) return;
+  const int slot = (m / n_ct) * 8 + xcd, ct = m % n_ct;
+  if (slot >= *C.n_tiles) return;
+  const int tile = C.sched[slot];
   const int e = C.tiles[3 * tile], r0 = C.tiles[3 * tile + 1], rows = C.tiles[3 * tile + 2];
   const bool shared = e == L.E;
   const int Iw = shared ? L.Is : L.I;
@@ -100,85 +113,101 @@ __global__ __launch_bounds__(kWaves * 64) void k_expert_gemm(LayerArgs L, ChunkA
   const int rowbase = shared ? C.Tk + r0 : seg + r0;  // hbuf row of the tile's first row
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* bt = smem;                                       // [2][blk][c][lane] x 16 B
-  int* tok = reinterpret_cast<int*>(smem + 2 * kBufBytes);  // [256]
-  float* wt = reinterpret_cast<float*>(tok + kTileRows);    // [256]
+  uint8_t* bt = smem;                                     // B: [2][blk][c][lane] x 16 B
+  uint8_t* at = smem + 2 * kBufBytes;                     // A: [2][256 rows][kARow B]
+  int* tok = reinterpret_cast<int*>(at + 2 * kABufBytes);  // [256]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, col = lane & 31;
 
-  // Row metadata: token (and routing weight for down).
   if (tid < kTileRows) {
     int t = 0;
-    float w = 0.f;
-    if (tid < rows) {
-      if (shared) {
-        t = r0 + tid;
-        w = 1.f;
-      } else {
-        const int a = C.sorted[seg + r0 + tid];
-        t = a / L.k;
-        w = C.tw[a];
-      }
-    }
+    if (tid < rows) t = shared ? r0 + tid : C.sorted[seg + r0 + tid] / L.k;
     tok[tid] = t;
-    wt[tid] = w;
   }
 
   // ---- weight block rebuilt by this wave: LDS block `wave`, lane `lane` ----
   // gate/up: LDS blocks 0..3 are gate, 4..7 up, column block cb0 + (wave & 3);
   // down: column block cb0 + wave.
   const int qj = kGateUp ? (wave & 3) : wave;
-  const bool qvalid = qj < nvb;  // wave-uniform
-  const int qjc = qvalid ? qj : nvb - 1;  // invalid blocks read a valid block and store nothing
+  const int qjc = qj < nvb ? qj : nvb - 1;  // columns past the edge rebuild a valid block, never stored
   const uint8_t* qsrc = kGateUp ? wbase + ((int64_t)(cb0 + qjc) * G * 2 + (wave >> 2)) * kBlockBytes
                                 : wbase + (int64_t)(cb0 + qjc) * G * kBlockBytes;
   const int64_t qstride = kGateUp ? 2 * kBlockBytes : kBlockBytes;
   uint4* qdst0 = reinterpret_cast<uint4*>(bt) + wave * 4 * 64 + lane;
 
-  __syncthreads();  // tok / wt visible
+  __syncthreads();  // tok visible
 
-  // ---- A operand pointers: rows 64*wm + 32*f + col, lane half h ----
-  const uint16_t* aptr[2];
-#pragma unroll
-  for (int f = 0; f < 2; f++) {
-    const int r = wm * 64 + f * 32 + col;
-    const int rr = r < rows ? r : 0;
-    if (kGateUp) {
-      aptr[f] = C.x16 + (int64_t)tok[rr] * H + h * 32;
-    } else {
-      aptr[f] = C.hbuf + (int64_t)(rowbase + rr) * C.Imax + h * 32;
-    }
+  // ---- A staging: thread t moves 16-byte parts (row t/8 + 64 i, part t%8), i < 4 ----
+  const int apart = tid & 7, arow0 = tid >> 3;
+  const uint16_t* asrc0;
+  const uint16_t* asrc1;
+  const uint16_t* asrc2;
+  const uint16_t* asrc3;
+  // Every thread stages all four rows each group, without branches, so the
+  // number of loads in flight is the same on every path and the compiler can
+  // wait for exactly the loads it needs; rows past the tile's end load a
+  // valid row (cache hits) and their results are never stored out.
+  {
+    auto rowptr = [&](int r) {
+      const int rr = r < rows ? r : rows - 1;
+      return (kGateUp ? C.x16 + (int64_t)tok[rr] * H : C.hbuf + (int64_t)(rowbase + rr) * C.Imax) + apart * 8;
+    };
+    asrc0 = rowptr(arow0);
+    asrc1 = rowptr(arow0 + 64);
+    asrc2 = rowptr(arow0 + 128);
+    asrc3 = rowptr(arow0 + 192);
   }
-  const bool wave_active = __builtin_amdgcn_readfirstlane(wm * 64 < rows ? 1 : 0) != 0;
-  // Wave's weight blocks in the LDS tile.
-  int wblk[4];
-#pragma unroll
-  for (int b = 0; b < 4; b++) wblk[b] = kGateUp ? (b >> 1) * 4 + 2 * wn + (b & 1) : 4 * wn + b;
+  // Two staging register sets: A of even groups in ae*, of odd groups in ao*,
+  // loaded two groups before they are written to LDS.
+  uint4 ae0 = make_uint4(0, 0, 0, 0), ae1 = ae0, ae2 = ae0, ae3 = ae0;
+  uint4 ao0 = ae0, ao1 = ae0, ao2 = ae0, ao3 = ae0;
+  uint8_t* const adst = at + apart * 16 + arow0 * kARow;
+#define MOE_LOAD_A(g, S)                                                                   \
+  do {                                                                                     \
+    const int gg_ = (g) < G ? (g) : G - 1; /* past the end: a valid, unused group */       \
+    S##0 = *reinterpret_cast<const uint4*>(asrc0 + gg_ * kGroup);                 \
+    S##1 = *reinterpret_cast<const uint4*>(asrc1 + gg_ * kGroup);                 \
+    S##2 = *reinterpret_cast<const uint4*>(asrc2 + gg_ * kGroup);                 \
+    S##3 = *reinterpret_cast<const uint4*>(asrc3 + gg_ * kGroup);                 \
+  } while (0)
+#define MOE_STORE_A(buf, S)                                                                \
+  do {                                                                                     \
+    uint8_t* d_ = adst + (buf) * kABufBytes;                                               \
+    *reinterpret_cast<uint4*>(d_) = S##0;                                         \
+    *reinterpret_cast<uint4*>(d_ + 64 * kARow) = S##1;                            \
+    *reinterpret_cast<uint4*>(d_ + 128 * kARow) = S##2;                           \
+    *reinterpret_cast<uint4*>(d_ + 192 * kARow) = S##3;                           \
+  } while (0)
 
-  auto load_a = [&](int g, uint4 (&dst)[2][4]) {
-    const int gg = g < G ? g : G - 1;  // past the end: a valid, unused group
-#pragma unroll
-    for (int f = 0; f < 2; f++)
-#pragma unroll
-      for (int c = 0; c < 4; c++) dst[f][c] = *reinterpret_cast<const uint4*>(aptr[f] + gg * kGroup + c * 8);
-  };
+  // ---- weight codes: a ring of 4 groups in registers (qc0..qc3, qs0..qs3) ----
+  uint4 qc0, qc1, qc2, qc3;
+  uint32_t qs0, qs1, qs2, qs3;
   auto load_q = [&](int g, uint4& code, uint32_t& sb) {
     const int gg = g < G ? g : G - 1;
     const uint8_t* blk = qsrc + gg * qstride;
     code = *reinterpret_cast<const uint4*>(blk + lane * 16);
     sb = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
   };
+  const uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
   auto dequant_store = [&](int buf, const uint4& code, uint32_t sb) {
-    const float s = bf16_bits_to_f32(sb & 0xFFFFu), b = bf16_bits_to_f32(sb >> 16);
+    const _Float16 sh = (_Float16)bf16_bits_to_f32(sb & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(sb >> 16);
+    const f16x2v_t s2 = {sh, sh}, b2 = {bh, bh};
     uint4* dst = qdst0 + buf * (kBufBytes / 16);
-    dst[0 * 64] = dequant8(code.x, s, b);
-    dst[1 * 64] = dequant8(code.y, s, b);
-    dst[2 * 64] = dequant8(code.z, s, b);
-    dst[3 * 64] = dequant8(code.w, s, b);
+    dst[0 * 64] = dequant8(code.x, s2, b2, kMask, kMagic);
+    dst[1 * 64] = dequant8(code.y, s2, b2, kMask, kMagic);
+    dst[2 * 64] = dequant8(code.z, s2, b2, kMask, kMagic);
+    dst[3 * 64] = dequant8(code.w, s2, b2, kMask, kMagic);
   };
+
+  const bool wave_active = __builtin_amdgcn_readfirstlane(wm * 64 < rows ? 1 : 0) != 0;
+  int wblk[4];
+#pragma unroll
+  for (int b = 0; b < 4; b++) wblk[b] = kGateUp ? (b >> 1) * 4 + 2 * wn + (b & 1) : 4 * wn + b;
+  // A fragment byte offsets inside an A buffer: rows 64 wm + 32 f + col, columns 32 h + 8 c.
+  const int aoff0 = (wm * 64 + col) * kARow + h * 64;
 
   f32x16_t acc[2][4];
 #pragma unroll
@@ -186,48 +215,84 @@ __global__ __launch_bounds__(kWaves * 64) void k_expert_gemm(LayerArgs L, ChunkA
 #pragma unroll
     for (int b = 0; b < 4; b++) acc[f][b] = f32x16_t{};
 
-  auto mma_group = [&](int buf, const uint4 (&a)[2][4]) {
-    const uint4* bsrc = reinterpret_cast<const uint4*>(bt + buf * kBufBytes);
+  // One group of MFMAs on buffers `cur`, fused with the rebuild of the next
+  // group's weights (code, sb) into B buffer `nxt`.  The sched_group_barrier
+  // sequence pins an interleaved order (each MFMA followed by two VALU ops of
+  // the rebuild), so the VALU work runs under the MFMA pipe.
+  auto mma_fused = [&](int cur, const uint4& code, uint32_t sb, int nxt) {
+    const _Float16 sh = (_Float16)bf16_bits_to_f32(sb & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(sb >> 16);
+    const f16x2v_t s2 = {sh, sh}, b2 = {bh, bh};
+    const uint4* bsrc = reinterpret_cast<const uint4*>(bt + cur * kBufBytes);
+    const uint8_t* asrc_l = at + cur * kABufBytes + aoff0;
+    uint4* dst = qdst0 + nxt * (kBufBytes / 16);
+    const uint32_t cw[4] = {code.x, code.y, code.z, code.w};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      f16x8_t bv[4];
+      f16x8_t bv[4], av[2];
 #pragma unroll
       for (int b = 0; b < 4; b++) bv[b] = __builtin_bit_cast(f16x8_t, bsrc[(wblk[b] * 4 + c) * 64 + lane]);
 #pragma unroll
-      for (int f = 0; f < 2; f++) {
-        const f16x8_t av = __builtin_bit_cast(f16x8_t, a[f][c]);
+      for (int f = 0; f < 2; f++)
+        av[f] = *reinterpret_cast<const f16x8_t*>(asrc_l + f * 32 * kARow + c * 16);
+      const uint4 dq = dequant8(cw[c], s2, b2, kMask, kMagic);
 #pragma unroll
-        for (int b = 0; b < 4; b++) acc[f][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[b], acc[f][b], 0, 0, 0);
+      for (int f = 0; f < 2; f++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) acc[f][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[f], bv[b], acc[f][b], 0, 0, 0);
+      dst[c * 64] = dq;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 6 LDS reads (A and B operands of this k-step)
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // 2 VALU
       }
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // 1 LDS write (rebuilt weights)
     }
   };
 
-  // Prologue: group 0 weights into buffer 0; A of group 0; codes of group 1.
-  uint4 a0[2][4], a1[2][4];
-  uint4 qc0, qc1;
-  uint32_t qs0, qs1;
+  // One pipeline step for group g, ring slot g % 4 holding (QC, QS) for the
+  // codes of g+4 to load and (NC, NS) the codes of g+1 to rebuild; AS is the
+  // staging set of group g+1 (its parity): MFMAs of g (buffers g%2) fused with
+  // the rebuild of g+1, A of g+1 into LDS, loads for A of g+3 and codes of g+4.
+#define MOE_GEMM_STEP(g, CUR, QC, QS, NC, NS, AS)               \
+  do {                                                        \
+    if (wave_active)                                          \
+      mma_fused(CUR, NC, NS, (CUR) ^ 1);                      \
+    else                                                      \
+      dequant_store((CUR) ^ 1, NC, NS);                       \
+    MOE_STORE_A((CUR) ^ 1, AS);                               \
+    MOE_LOAD_A((g) + 3, AS);                                  \
+    load_q((g) + 4, QC, QS);                                  \
+    __syncthreads();                                          \
+  } while (0)
+
+  // Prologue: codes of groups 0..3, A and weights of group 0, A loads of groups 1, 2.
   load_q(0, qc0, qs0);
-  load_a(0, a0);
-  if (qvalid) dequant_store(0, qc0, qs0);
   load_q(1, qc1, qs1);
+  load_q(2, qc2, qs2);
+  load_q(3, qc3, qs3);
+  MOE_LOAD_A(0, ae);
+  MOE_STORE_A(0, ae);
+  dequant_store(0, qc0, qs0);
+  MOE_LOAD_A(1, ao);
+  MOE_LOAD_A(2, ae);
   __syncthreads();
 
-  // Two groups per iteration; register sets and LDS buffers alternate.
-  for (int g = 0; g < G; g += 2) {
-    // even group g: A in a0, weights in buffer 0, codes of g+1 in qc1.
-    load_a(g + 1, a1);
-    if (qvalid && g + 1 < G) dequant_store(1, qc1, qs1);
-    load_q(g + 2, qc0, qs0);
-    if (wave_active) mma_group(0, a0);
-    __syncthreads();
+  for (int g = 0; g < G; g += 4) {
+    MOE_GEMM_STEP(g, 0, qc0, qs0, qc1, qs1, ao);
     if (g + 1 >= G) break;
-    // odd group g+1: A in a1, weights in buffer 1, codes of g+2 in qc0.
-    load_a(g + 2, a0);
-    if (qvalid && g + 2 < G) dequant_store(0, qc0, qs0);
-    load_q(g + 3, qc1, qs1);
-    if (wave_active) mma_group(1, a1);
-    __syncthreads();
+    MOE_GEMM_STEP(g + 1, 1, qc1, qs1, qc2, qs2, ae);
+    if (g + 2 >= G) break;
+    MOE_GEMM_STEP(g + 2, 0, qc2, qs2, qc3, qs3, ao);
+    if (g + 3 >= G) break;
+    MOE_GEMM_STEP(g + 3, 1, qc3, qs3, qc0, qs0, ae);
   }
+#undef MOE_GEMM_STEP
+#undef MOE_LOAD_A
+#undef MOE_STORE_A
 
   if (!wave_active) return;
   // ---- epilogue: undo the 2^-8 activation scale ----
@@ -249,6 +314,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_expert_gemm(LayerArgs L, ChunkA
       }
     }
   } else {
+    // Routed rows: fp16(out / 256) per assignment, combined per token later
+    // (k_combine); the shared expert's rows go straight into y in fp32.
 #pragma unroll
     for (int f = 0; f < 2; f++) {
 #pragma unroll
@@ -258,17 +325,49 @@ __global__ __launch_bounds__(kWaves * 64) void k_expert_gemm(LayerArgs L, ChunkA
 #pragma unroll
         for (int i = 0; i < 16; i++) {
           const int r = wm * 64 + f * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (r < rows) atomicAdd(C.y + (int64_t)tok[r] * H + ocol, wt[r] * (256.f * acc[f][b][i]));
+          if (r < rows) {
+            if (shared)
+              C.y[(int64_t)tok[r] * H + ocol] = 256.f * acc[f][b][i];
+            else
+              C.obuf[(int64_t)(rowbase + r) * H + ocol] = f32_to_f16_bits(acc[f][b][i]);
+          }
         }
       }
     }
   }
 }
 
-__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (; i < n; i += stride) p[i] = 0.f;
+// y[t] = (shared expert's output, already in y) + sum_j w_tj * 256 * obuf[pos(t, j)]
+// in top-k order.  One workgroup per token, 8 columns per thread.
+__global__ __launch_bounds__(256) void k_combine(LayerArgs L, ChunkArgs C) {
+  const int t = blockIdx.x;
+  const int H = L.H, k = L.k;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float acc[8];
+    if (L.Is > 0) {
+      const float4 a = *reinterpret_cast<const float4*>(C.y + (int64_t)t * H + c);
+      const float4 b = *reinterpret_cast<const float4*>(C.y + (int64_t)t * H + c + 4);
+      acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
+      acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] = 0.f;
+    }
+    for (int j = 0; j < k; j++) {
+      const int a = t * k + j;
+      const float w = 256.f * C.tw[a];
+      const uint4 o = *reinterpret_cast<const uint4*>(C.obuf + (int64_t)C.inv[a] * H + c);
+      const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const f16x2v_t p = __builtin_bit_cast(f16x2v_t, ow[i]);
+        acc[2 * i] = fmaf(w, (float)p.x, acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, (float)p.y, acc[2 * i + 1]);
+      }
+    }
+    *reinterpret_cast<float4*>(C.y + (int64_t)t * H + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(C.y + (int64_t)t * H + c + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -296,11 +395,8 @@ hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tile
   return launch_expert_gemm<false>(L, C, max_tiles, s);
 }
 
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  k_fill_zero<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n);
+hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s) {
+  k_combine<<<dim3(C.T), dim3(256), 0, s>>>(L, C);
   return hipGetLastError();
 }
 

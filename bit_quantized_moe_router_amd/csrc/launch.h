@@ -18,26 +18,29 @@ struct PackArgs {
 };
 
 hipError_t launch_pack(const PackArgs& P, hipStream_t s);
-// Router logits: exact float64 ones for T <= 8, bf16-MFMA screened ones (and
-// router row norms) otherwise; *two_launches tells which.
+// Router logits: exact float64 ones for T <= 8, otherwise bf16-MFMA screened
+// partial sums over 4 slices of h (and partial squared router row norms);
+// *two_launches tells which.
 hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
-                               int k, float* logits, float* wnorm, int32_t* ids, float* tw, float* xsum,
+                               int k, float* logits, double* wsq, int32_t* ids, float* tw, float* xsum,
                                uint16_t* x16, hipStream_t s, bool* two_launches);
 // Top-k selection (exact recomputation of the screened candidates for T > 8).
 hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
-                               int k, const float* logits, const float* wnorm, int32_t* ids, float* tw,
+                               int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
                                float* xsum, uint16_t* x16, hipStream_t s);
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
-                       int32_t* n_tiles, int32_t* active, int32_t* n_active, hipStream_t s);
+                       int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
+                       int32_t* sched, hipStream_t s);
 // T <= 8: top-k of exact logits and the metadata in one single-workgroup launch.
 hipError_t launch_topk_meta(const float* logits, int T, int E, int k, int32_t* ids, float* tw, int BM,
                             int with_shared, int32_t* counts, int32_t* offsets, int32_t* sorted,
                             int32_t* tiles, int32_t* n_tiles, int32_t* active, int32_t* n_active,
-                            hipStream_t s);
+                            int32_t* inv, int32_t* sched, hipStream_t s);
 hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s);
 hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s);
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// y[t] += sum_j w_tj * routed output of assignment (t, j) (GEMM path).
+hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);
 hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);
 hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);
 

@@ -155,91 +155,119 @@ __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Many tokens, step 1: screened logits a = sum_h x * bf16(Wr) + bias with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  Workgroup tile 64 tokens x
-// 64 experts, four 32x32 waves, operands loaded straight from memory.  The
-// workgroups of the first token tile also write |Wr_e|_2 (float64 sum,
-// rounded up) for the error bound.
+// Many tokens, step 1: screened logits a = sum_h x * bf16(Wr) with
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation), split over kScreenSplit
+// slices of h so that enough waves are in flight; each slice writes its
+// partial sums (summed with the bias in a fixed order by k_route_exact).
+// Workgroup tile 64 tokens x 64 experts, four 32x32 waves, operands loaded
+// straight from memory one group ahead.  The workgroups of the first token
+// tile also write the partial sums of Wr_e^2 (float64) for the error bound.
 // ---------------------------------------------------------------------------
+constexpr int kScreenSplit = 4;
+
+// LDS bytes of one k_route_exact wave: x row (bf16), candidate experts and
+// logits (E each), selected logits (16).
+__host__ __device__ constexpr int route_exact_wave_bytes(int H, int E) { return H * 2 + E * 8 + 64; }
+
 __global__ __launch_bounds__(256) void k_screen(const uint16_t* __restrict__ x, int T, int H,
-                                                const float* __restrict__ wr,
-                                                const float* __restrict__ bias, int E,
-                                                float* __restrict__ approx, float* __restrict__ wnorm) {
+                                                const float* __restrict__ wr, int E,
+                                                float* __restrict__ approx, double* __restrict__ wsq) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, c32 = lane & 31;
   const int t = blockIdx.x * 64 + wm * 32 + c32;
   const int e = blockIdx.y * 64 + wn * 32 + c32;
   const bool tv = t < T, ev = e < E;
+  const int G = H / kGroup;
+  const int gs = blockIdx.z, g0 = G * gs / kScreenSplit, g1 = G * (gs + 1) / kScreenSplit;
   const uint16_t* xr = x + (int64_t)(tv ? t : 0) * H + h * 32;
   const float* wrow = wr + (int64_t)(ev ? e : 0) * H + h * 32;
   const bool norms = blockIdx.x == 0 && wm == 0;
   f32x16_t acc = {};
   double ss = 0.0;
-  const int G = H / kGroup;
-  for (int g = 0; g < G; g++) {
-    uint4 a[4];
-    float4 w[8];
+  uint4 a[2][4];
+  float4 w[2][8];
+  auto load = [&](int g, int s) {
+    const int gg = g < g1 ? g : (g1 > 0 ? g1 - 1 : 0);  // empty slices read group 0 and add nothing
 #pragma unroll
-    for (int c = 0; c < 4; c++)
-      a[c] = tv ? *reinterpret_cast<const uint4*>(xr + g * kGroup + c * 8) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < 4; c++) a[s][c] = *reinterpret_cast<const uint4*>(xr + gg * kGroup + c * 8);
 #pragma unroll
-    for (int q = 0; q < 8; q++)
-      w[q] = ev ? *reinterpret_cast<const float4*>(wrow + g * kGroup + q * 4) : make_float4(0, 0, 0, 0);
+    for (int q = 0; q < 8; q++) w[s][q] = *reinterpret_cast<const float4*>(wrow + gg * kGroup + q * 4);
+  };
+  auto compute = [&](int s) {
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      const float4 p = w[2 * c], r = w[2 * c + 1];
+      const float4 p = w[s][2 * c], r = w[s][2 * c + 1];
       bf16x8_t b = {(__bf16)p.x, (__bf16)p.y, (__bf16)p.z, (__bf16)p.w,
                     (__bf16)r.x, (__bf16)r.y, (__bf16)r.z, (__bf16)r.w};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[c]), b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[s][c]), b, acc, 0, 0, 0);
     }
     if (norms) {
 #pragma unroll
       for (int q = 0; q < 8; q++) {
-        ss = fma((double)w[q].x, (double)w[q].x, ss);
-        ss = fma((double)w[q].y, (double)w[q].y, ss);
-        ss = fma((double)w[q].z, (double)w[q].z, ss);
-        ss = fma((double)w[q].w, (double)w[q].w, ss);
+        ss = fma((double)w[s][q].x, (double)w[s][q].x, ss);
+        ss = fma((double)w[s][q].y, (double)w[s][q].y, ss);
+        ss = fma((double)w[s][q].z, (double)w[s][q].z, ss);
+        ss = fma((double)w[s][q].w, (double)w[s][q].w, ss);
       }
     }
+  };
+  load(g0, 0);
+  for (int g = g0; g < g1; g += 2) {
+    load(g + 1, 1);
+    compute(0);
+    if (g + 1 >= g1) break;
+    load(g + 2, 0);
+    compute(1);
   }
-  const float b = (ev && bias) ? bias[e] : 0.f;
+  float* out = approx + (int64_t)gs * T * E;
+  if (ev) {
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int tok = blockIdx.x * 64 + wm * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-    if (tok < T && ev) approx[(int64_t)tok * E + e] = acc[i] + b;
+    for (int i = 0; i < 16; i++) {
+      const int tok = blockIdx.x * 64 + wm * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (tok < T) out[(int64_t)tok * E + e] = acc[i];
+    }
   }
   if (norms) {
     ss += __shfl_xor(ss, 32);
-    if (h == 0 && ev) wnorm[e] = (float)(sqrt(ss) * (1.0 + 1e-6));
+    if (h == 0 && ev) wsq[gs * E + e] = ss;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Many tokens, step 2: one wave per token.  Error bound of a screened logit
-// against the float64-accumulated one (both with the bias added in fp32):
-//   |a - l| <= (2^-8 + 2 H 2^-23) * sum_h |x_h||w_h| + 2^-22 (|a| + |l| + 1)
-// covering the bf16 rounding of Wr (at most 2^-8 relative, any rounding
-// mode), fp32 accumulation of H exact products in any order (2 H 2^-23) and
-// the final roundings; sum |x||w| <= |x|_2 max_e |w_e|_2.  Experts with
-// a >= a_k - 2 B (a_k the k-th largest screened logit) are recomputed in
-// float64 and the exact top-k is taken among them.  Also writes the per-group
-// activation sums.
+// Many tokens, step 2: one wave per token.  Bound B on the distance between a
+// screened logit a and the exact one l (float64 sum rounded to fp32, plus the
+// fp32 bias):
+//   B = (2^-8 + (H + 4) 2^-21) |x|_2 max_e |w_e|_2 + 2^-21 (2 max|a| + 1)
+// The first term covers the bf16 rounding of Wr (at most 2^-8 relative) and
+// the fp32 accumulation of H exact bf16 products and of the slices in any
+// order (at most (H + 3) 2^-24 relative to sum |x||w| <= |x|_2 |w_e|_2, taken
+// 8 times over); the second the roundings of the bias additions.  Every
+// expert of the exact top-k has a >= a_k - 2 B (a_k the k-th largest screened
+// logit), so those experts are recomputed in float64 (four at a time, 16
+// lanes each) and the exact top-k is taken among them by rank.  Also writes
+// the per-group activation sums and the fp16 activation copy of the grouped
+// GEMM.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict__ x, int T, int H,
                                                      const float* __restrict__ wr,
                                                      const float* __restrict__ bias, int E, int k,
                                                      const float* __restrict__ approx,
-                                                     const float* __restrict__ wnorm,
+                                                     const double* __restrict__ wsq,
                                                      int32_t* __restrict__ ids, float* __restrict__ tw,
                                                      float* __restrict__ xsum, uint16_t* __restrict__ x16) {
-  extern __shared__ uint16_t xl_all[];  // [4][H]
+  // Per wave in LDS: x row, candidate experts and logits, selected logits.
+  extern __shared__ __attribute__((aligned(16))) uint8_t rsm[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  uint16_t* xl = xl_all + wave * H;
+  const int wbytes = route_exact_wave_bytes(H, E);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(rsm + wave * wbytes);
+  int* cand_e = reinterpret_cast<int*>(rsm + wave * wbytes + H * 2);
+  float* cand_v = reinterpret_cast<float*>(cand_e + E);
+  float* sel_v = cand_v + E;
   const uint16_t* xr = x + (int64_t)t * H;
 
-  // x row -> LDS, per-group sums, |x|_2^2 in float64.
+  // x row -> LDS, per-group sums, fp16 copy, |x|_2^2 in float64.
   double xx = 0.0;
   for (int h0 = 0; h0 < H; h0 += 256) {
     const int h = h0 + 4 * lane;
@@ -264,23 +292,34 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
   }
   const double xnorm = sqrt(wave_sum_f64(xx)) * (1.0 + 1e-6);
 
+  // Screened logits: fixed-order sum of the slices, then the fp32 bias.
   float a[kMaxEPerLane];
   bool alive[kMaxEPerLane];
-  float wmax = 0.f, amax = 0.f;
+  float amax = 0.f;
+  double w2max = 0.0;
 #pragma unroll
   for (int j = 0; j < kMaxEPerLane; j++) {
     const int e = lane + 64 * j;
     alive[j] = e < E;
-    a[j] = alive[j] ? approx[(int64_t)t * E + e] : 0.f;
+    float v = 0.f;
     if (alive[j]) {
-      wmax = fmaxf(wmax, wnorm[e]);
-      amax = fmaxf(amax, fabsf(a[j]));
+      v = approx[(int64_t)t * E + e];
+      double w2 = wsq[e];
+#pragma unroll
+      for (int s = 1; s < kScreenSplit; s++) {
+        v += approx[(int64_t)s * T * E + (int64_t)t * E + e];
+        w2 += wsq[s * E + e];
+      }
+      if (bias) v = v + bias[e];
+      amax = fmaxf(amax, fabsf(v));
+      w2max = fmax(w2max, w2);
     }
+    a[j] = v;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    wmax = fmaxf(wmax, __shfl_xor(wmax, off));
     amax = fmaxf(amax, __shfl_xor(amax, off));
+    w2max = fmax(w2max, __shfl_xor(w2max, off));
   }
   // k-th largest screened logit.
   float kv;
@@ -292,43 +331,68 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
     wave_topk(a, al2, k, kv, ki);
   }
   const float ak = __shfl(kv, k - 1);
-  const double c1 = 0.00390625 + 2.0 * H * 1.1920928955078125e-07;
-  const double B = c1 * xnorm * (double)wmax + 2.384185791015625e-07 * (2.0 * amax + 1.0) * 2.0;
+  const double c1 = 0.00390625 + 2.0 * (H + 4) * 1.1920928955078125e-07;
+  const double B = c1 * xnorm * (sqrt(w2max) * (1.0 + 1e-6)) + 2.384185791015625e-07 * (2.0 * amax + 1.0) * 2.0;
   const double lo = (double)ak - 2.0 * B;
 
-  // Exact float64 logits of the candidates; everything else drops out.
-  float v[kMaxEPerLane];
-  const float* bb = bias;
+  // Candidate list in increasing expert order.
+  int C = 0;
 #pragma unroll
   for (int j = 0; j < kMaxEPerLane; j++) {
     const bool cand = alive[j] && (double)a[j] >= lo;
-    v[j] = 0.f;
-    uint64_t m = __ballot(cand);
-    while (m) {
-      const int l = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      const int e = l + 64 * j;
-      const float* wrow = wr + (int64_t)e * H;
-      double acc = 0.0;
-      for (int h = 4 * lane; h < H; h += 256) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wrow + h);
-        const uint2 xv = *reinterpret_cast<const uint2*>(xl + h);
-        acc = fma((double)bf16_bits_to_f32(xv.x & 0xFFFFu), (double)w4.x, acc);
-        acc = fma((double)bf16_bits_to_f32(xv.x >> 16), (double)w4.y, acc);
-        acc = fma((double)bf16_bits_to_f32(xv.y & 0xFFFFu), (double)w4.z, acc);
-        acc = fma((double)bf16_bits_to_f32(xv.y >> 16), (double)w4.w, acc);
-      }
-      const double s = wave_sum_f64(acc);
-      float lg = (float)s;
-      if (bb) lg = lg + bb[e];
-      if (lane == l) v[j] = lg;
-    }
-    alive[j] = cand;
+    const uint64_t m = __ballot(cand);
+    if (cand) cand_e[C + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = lane + 64 * j;
+    C += __popcll(m);
   }
-  float myv;
-  int myi;
-  wave_topk(v, alive, k, myv, myi);
-  write_topk(myv, myi, k, t, ids, tw);
+  __builtin_amdgcn_wave_barrier();
+
+  // Exact float64 logits, four candidates at a time (16 lanes each).
+  const int q = lane >> 4, l16 = lane & 15;
+  for (int c0 = 0; c0 < C; c0 += 4) {
+    const int c = c0 + q;
+    const int e = c < C ? cand_e[c] : cand_e[c0];
+    const float* wrow = wr + (int64_t)e * H;
+    double acc = 0.0;
+#pragma unroll 8
+    for (int h = 4 * l16; h < H; h += 64) {
+      const float4 w4 = *reinterpret_cast<const float4*>(wrow + h);
+      const uint2 xv = *reinterpret_cast<const uint2*>(xl + h);
+      acc = fma((double)bf16_bits_to_f32(xv.x & 0xFFFFu), (double)w4.x, acc);
+      acc = fma((double)bf16_bits_to_f32(xv.x >> 16), (double)w4.y, acc);
+      acc = fma((double)bf16_bits_to_f32(xv.y & 0xFFFFu), (double)w4.z, acc);
+      acc = fma((double)bf16_bits_to_f32(xv.y >> 16), (double)w4.w, acc);
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
+    float lg = (float)acc;
+    if (bias) lg = lg + bias[e];
+    if (l16 == 0 && c < C) cand_v[c] = lg;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // Exact top-k by rank: candidate c ranks below every c' with a larger logit
+  // or an equal logit and a lower expert index.
+  for (int c = lane; c < C; c += 64) {
+    const float vc = cand_v[c];
+    const int ec = cand_e[c];
+    int rank = 0;
+    for (int c2 = 0; c2 < C; c2++) {
+      const float v2 = cand_v[c2];
+      rank += (v2 > vc || (v2 == vc && cand_e[c2] < ec)) ? 1 : 0;
+    }
+    if (rank < k) {
+      ids[(int64_t)t * k + rank] = ec;
+      sel_v[rank] = vc;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const float myv = lane < k ? sel_v[lane] : 0.f;
+  const float vmax = __shfl(myv, 0);
+  const float ex = lane < k ? __expf(myv - vmax) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane < k) tw[(int64_t)t * k + lane] = ex / sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -348,9 +412,11 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                           int32_t* __restrict__ sorted, int32_t* __restrict__ tiles,
                           int32_t* __restrict__ n_tiles, int32_t* __restrict__ active,
-                          int32_t* __restrict__ n_active) {
+                          int32_t* __restrict__ n_active, int32_t* __restrict__ inv,
+                          int32_t* __restrict__ sched) {
   __shared__ int cnt[kMetaWaves * kMaxE];  // [wave][expert]
-  __shared__ int sc0[kMaxE], sc1[kMaxE], sc2[kMaxE];
+  __shared__ int sc0[kMaxE], sc1[kMaxE], sc2[kMaxE], sc3[kMaxE], sc4[kMaxE];
+  __shared__ int s_full_total;
   __shared__ int s_routed_tiles, s_nact;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -364,30 +430,50 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
   for (int a = seg0 + lane; a < seg1; a += 64) atomicAdd(&cnt[wave * E + ids[a]], 1);
   __syncthreads();
 
-  int tot = 0, nt = 0, act = 0;
+  int tot = 0, nt = 0, act = 0, nfull = 0, npart = 0;
   if (tid < E) {
     for (int w = 0; w < kMetaWaves; w++) tot += cnt[w * E + tid];
     nt = (tot + BM - 1) / BM;
     act = tot > 0 ? 1 : 0;
+    nfull = tot / BM;
+    npart = nt - nfull;
     sc0[tid] = tot;
     sc1[tid] = nt;
     sc2[tid] = act;
+    sc3[tid] = nfull;
+    sc4[tid] = npart;
   }
   __syncthreads();
   for (int off = 1; off < E; off <<= 1) {
-    int a0 = 0, a1 = 0, a2 = 0;
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0, a4 = 0;
     if (tid < E && tid >= off) {
       a0 = sc0[tid - off];
       a1 = sc1[tid - off];
       a2 = sc2[tid - off];
+      a3 = sc3[tid - off];
+      a4 = sc4[tid - off];
     }
     __syncthreads();
     if (tid < E && tid >= off) {
       sc0[tid] += a0;
       sc1[tid] += a1;
       sc2[tid] += a2;
+      sc3[tid] += a3;
+      sc4[tid] += a4;
     }
     __syncthreads();
+  }
+  if (tid == E - 1) s_full_total = sc3[tid];
+  __syncthreads();
+  // Execution order of the tiles for the grouped GEMMs (longest first): the
+  // shared expert's full tiles, the routed full tiles, the routed partial
+  // tiles, the shared expert's partial tile.
+  const int sfull = with_shared ? T / BM : 0;
+  if (sched && tid < E) {
+    const int ts = sc1[tid] - nt;
+    const int fpos = sfull + sc3[tid] - nfull;
+    for (int r = 0; r < nfull; r++) sched[fpos + r] = ts + r;
+    if (npart) sched[sfull + s_full_total + sc4[tid] - 1] = ts + nfull;
   }
   if (tid < E) {
     const int off_e = sc0[tid] - tot;
@@ -420,6 +506,7 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
     tiles[3 * (rt + r) + 0] = E;
     tiles[3 * (rt + r) + 1] = r * BM;
     tiles[3 * (rt + r) + 2] = min(BM, T - r * BM);
+    if (sched) sched[r < sfull ? r : rt + nshared - 1] = rt + r;
   }
   if (tid == 0) {
     n_tiles[0] = rt + nshared;
@@ -443,6 +530,7 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
       rank = __popcll(m & lt_mask);
       pos = cnt[wave * E + e] + rank;
       sorted[pos] = a;
+      if (inv) inv[a] = pos;
     }
     __builtin_amdgcn_wave_barrier();
     if (valid && rank == 0) cnt[wave * E + e] += __popcll(m);
@@ -454,8 +542,9 @@ __global__ __launch_bounds__(1024) void k_meta(const int32_t* __restrict__ ids, 
                                                int BM, int with_shared, int32_t* __restrict__ counts,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
                                                int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-                                               int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
-  meta_body(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active);
+                                               int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                               int32_t* __restrict__ inv, int32_t* __restrict__ sched) {
+  meta_body(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
 }
 
 // Few tokens: top-k of the exact logits (wave t for token t) and the routing
@@ -465,7 +554,8 @@ __global__ __launch_bounds__(1024) void k_topk_meta(const float* __restrict__ lo
                                                     int BM, int with_shared, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
                                                     int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-                                                    int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+                                                    int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                                    int32_t* __restrict__ inv, int32_t* __restrict__ sched) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (wave < T) {
     const float* l = logits + (int64_t)wave * E;
@@ -483,12 +573,12 @@ __global__ __launch_bounds__(1024) void k_topk_meta(const float* __restrict__ lo
     write_topk(myv, myi, k, wave, ids, tw);
   }
   __syncthreads();
-  meta_body(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active);
+  meta_body(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
 }
 
 // ---------------------------------------------------------------------------
 hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
-                               int k, float* logits, float* wnorm, int32_t* ids, float* tw, float* xsum,
+                               int k, float* logits, double* wsq, int32_t* ids, float* tw, float* xsum,
                                uint16_t* x16, hipStream_t s, bool* two_launches) {
   if (T == 0) return hipSuccess;
   if (T <= kSmallT) {
@@ -496,34 +586,43 @@ hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr,
     *two_launches = false;
     return hipGetLastError();
   }
-  k_screen<<<dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s>>>(x, T, H, wr, bias, E, logits, wnorm);
+  k_screen<<<dim3((T + 63) / 64, (E + 63) / 64, kScreenSplit), dim3(256), 0, s>>>(x, T, H, wr, E, logits, wsq);
   *two_launches = true;
   return hipGetLastError();
 }
 
 hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
-                               int k, const float* logits, const float* wnorm, int32_t* ids, float* tw,
+                               int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
                                float* xsum, uint16_t* x16, hipStream_t s) {
   if (T <= kSmallT) return hipSuccess;  // few tokens: k_topk_meta selects from the exact logits
-  k_route_exact<<<dim3((T + 3) / 4), dim3(256), (size_t)4 * H * 2, s>>>(x, T, H, wr, bias, E, k, logits,
-                                                                        wnorm, ids, tw, xsum, x16);
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route_exact),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 4 * route_exact_wave_bytes(8192, 512));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const size_t smem = (size_t)4 * route_exact_wave_bytes(H, E);
+  k_route_exact<<<dim3((T + 3) / 4), dim3(256), smem, s>>>(x, T, H, wr, bias, E, k, logits, wsq, ids, tw, xsum,
+                                                            x16);
   return hipGetLastError();
 }
 
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
-                       int32_t* n_tiles, int32_t* active, int32_t* n_active, hipStream_t s) {
+                       int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
+                       int32_t* sched, hipStream_t s) {
   k_meta<<<dim3(1), dim3(1024), 0, s>>>(ids, T, k, E, BM, with_shared, counts, offsets, sorted,
-                                        tiles, n_tiles, active, n_active);
+                                        tiles, n_tiles, active, n_active, inv, sched);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_meta(const float* logits, int T, int E, int k, int32_t* ids, float* tw, int BM,
                             int with_shared, int32_t* counts, int32_t* offsets, int32_t* sorted,
                             int32_t* tiles, int32_t* n_tiles, int32_t* active, int32_t* n_active,
-                            hipStream_t s) {
+                            int32_t* inv, int32_t* sched, hipStream_t s) {
   k_topk_meta<<<dim3(1), dim3(1024), 0, s>>>(logits, T, E, k, ids, tw, BM, with_shared, counts, offsets,
-                                             sorted, tiles, n_tiles, active, n_active);
+                                             sorted, tiles, n_tiles, active, n_active, inv, sched);
   return hipGetLastError();
 }
 

@@ -188,7 +188,7 @@ const char *moe_last_error(void);
  *   0 = router logits (screen, or exact for T <= 8), 1 = exact top-k
  *   selection (T > 8), 2 = routing metadata (with top-k for T <= 8),
  *   3 = gate/up grouped GEMM, 4 = down grouped GEMM, 5 = gate/up GEMV,
- *   6 = down GEMV
+ *   6 = down GEMV, 7 = per-token combine of the grouped-GEMM path
  */
 moe_status moe_profile_enable(int32_t mask);
 moe_status moe_profile_reset(void);
