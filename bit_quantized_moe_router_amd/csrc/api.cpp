@@ -32,7 +32,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
   return s;
 }
 
-constexpr int kDefaultTileRows = 256;
+constexpr int kDefaultTileRows = 128;
 constexpr int kDefaultGemvMaxRows = 4;
 constexpr int kMaxRowsDecode = 8;
 
@@ -55,8 +55,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (d->max_chunk < 1 || d->max_chunk > 8192)
     return fail(MOE_ERR_INVALID_ARGUMENT, "max_chunk must be in 1..8192 (got %d)", d->max_chunk);
   const int bm = d->tile_rows;
-  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "tile_rows must be 0, 16, 32, 64, 128 or 256 (got %d)", bm);
+  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "tile_rows must be 0, 16, 32, 64 or 128 (got %d)", bm);
   return MOE_OK;
 }
 
@@ -109,7 +109,7 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   w.sorted = o; o += al(Tc * k * 4);
   w.inv = o; o += al(Tc * k * 4);
   w.tiles = o; o += al(max_tiles_for(d, Tc) * 3 * 4);
-  w.sched = o; o += al(max_tiles_for(d, Tc) * 4);
+  w.sched = o; o += al(max_tiles_for(d, Tc) * 16);  // int4 tile descriptor per slot
   w.n_tiles = o; o += al(4);
   w.active = o; o += al(E * 4);
   w.n_active = o; o += al(4);

@@ -5,18 +5,29 @@
 //   gate/up: per tile of routed rows, h = silu(x Wg^T) * (x Wu^T)
 //   down:    y[token] += routing weight * (h Wd^T), the shared expert with 1
 //
-// Workgroup = 8 waves over a tile of up to 256 rows of one expert x 256 weight
-// columns (gate/up: 128 intermediate columns of gate and the same 128 of up;
-// down: 256 output columns).  Wave (wm, wn) owns rows 64*wm.. and half the
-// columns: 2 x 4 blocks of v_mfma_f32_32x32x16_f16, fp32 accumulation.
+// Workgroup = 8 waves (two per SIMD) over a tile of up to 128 rows of one
+// expert.  Each wave owns 2 weight blocks of 32 columns (gate/up: one block
+// of gate and the same block of up; down: 2 output blocks) and all rows of
+// the tile: up to 4 x 2 accumulators of v_mfma_f32_32x32x16_f16 (fp32).  The
+// kernel is instantiated per number of 32-row fragments the tile needs
+// (1..4), so small tiles issue only the MFMAs of their rows.
 //
-// Weights stay 4-bit in HBM.  Per 64-wide K group the workgroup reads the
-// packed codes of its 8 blocks of 32 columns (one 16-byte load per thread,
-// one block per wave), rebuilds w = s*q + b in fp32, rounds it to fp16 and
-// writes it to LDS in MFMA operand order (block, k-step, lane), so that every
-// wave reads its B operands with conflict-free 16-byte LDS reads.  The LDS
-// tile is double buffered: the weights of group g+1 are rebuilt while the
-// MFMAs of group g run.  The full-precision weights never reach HBM.
+// Weights stay 4-bit in HBM and never pass through LDS: the packed layout puts
+// each lane's 16 bytes of codes exactly where the MFMA B operand needs them,
+// so a wave loads its blocks with one 16-byte load per block and K group,
+// rebuilds w = s*q + b in registers (fp16, one rounding) and feeds them to the
+// MFMAs of the same group.  Codes are prefetched four groups ahead, starting
+// before the token indices of the tile are known.
+//
+// Activations (gathered token rows for gate/up, the expert's contiguous rows
+// of the intermediate for down) are shared by the 8 waves through LDS: per K
+// group the workgroup stages 128 rows x 64 columns (double buffered, one
+// barrier per group); the loads run three groups ahead.  Rows past the tile's
+// count reuse a valid row and are never stored.
+//
+// Results leave through LDS: the workgroup's output tile is assembled there
+// and written back as whole rows with 16-byte stores (the shared expert's
+// down rows, fp32, go straight to y).
 //
 // Operand precision: the pages rebuild weights in bf16; here the operands are
 // fp16 (11 significant bits instead of 8), which cuts the rounding error of
@@ -24,13 +35,6 @@
 // by the routing kernels) and the intermediate as fp16(h / 256); the power-of-
 // two scale is exact and keeps any bf16-sized value inside the fp16 range, and
 // the epilogues multiply it back.
-//
-// Activations go from memory straight to registers (gathered token rows for
-// gate/up, contiguous rows of the expert's segment for down), one group ahead,
-// in two register sets that alternate between even and odd groups.  Rows
-// beyond the tile's valid count reuse a valid row's address and are never
-// stored; a wave whose 64 rows are all beyond the count skips its MFMAs.
-// Workgroups beyond n_tiles (read on the device) exit.
 //
 // MFMA 32x32x16 operand layout (wave64): lane l supplies row (A) / column (B)
 // l % 32 and eight consecutive k-slots 8*(l/32)..+7; the result holds column
@@ -46,17 +50,19 @@
 
 namespace moe {
 
-constexpr int kTileRows = 256;
+constexpr int kTileRows = 128;                 // largest tile the kernel takes
 constexpr int kWaves = 8;
-constexpr int kBlocks = 8;                           // 32-column weight blocks per tile
-constexpr int kBufBytes = kBlocks * kCodeBytes * 4;  // fp16 tile of one group: 8 x 4 x 64 x 16 B
-constexpr int kARow = 144;                           // bytes per A row in LDS: 64 fp16 + 16 B pad
-constexpr int kABufBytes = kTileRows * kARow;        // one group of A rows
-constexpr int kSmem = 2 * kBufBytes + 2 * kABufBytes + kTileRows * 4;  // + token per row
+constexpr int kARow = 144;                     // bytes per A row in LDS: 64 fp16 + 16 B pad
+constexpr int kABufBytes = kTileRows * kARow;  // one K group of A rows
+constexpr int kSmemMain = 2 * kABufBytes + kTileRows * 4;  // + token per row
+constexpr int kGateUpColsPerWg = kWaves * 32;  // intermediate columns per workgroup
+constexpr int kDownColsPerWg = kWaves * 64;    // output columns per workgroup
+constexpr int kEpiRowGateUp = kGateUpColsPerWg * 2 + 16;  // LDS bytes per output row (fp16 + pad)
+constexpr int kEpiRowDown = kDownColsPerWg * 2 + 16;
+constexpr int kSmemGateUp = kTileRows * kEpiRowGateUp > kSmemMain ? kTileRows * kEpiRowGateUp : kSmemMain;
+constexpr int kSmemDown = kTileRows * kEpiRowDown > kSmemMain ? kTileRows * kEpiRowDown : kSmemMain;
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
 typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
 
 // (a & mask) | magic in one VALU op.
@@ -71,270 +77,269 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t m
 // ((d >> 4i) & 0x000F000F) | 0x64006400 is the fp16 pair (1024 + q, 1024 + q')
 // (fp16 0x6400 = 1024 and its 10 mantissa bits step by 1); subtracting 1024 is
 // exact, and one packed fp16 FMA per pair rounds s*q + b once.
-__device__ __forceinline__ uint4 dequant8(uint32_t d, f16x2v_t s2, f16x2v_t b2, uint32_t mask, uint32_t magic) {
+__device__ __forceinline__ f16x8_t dequant8(uint32_t d, f16x2v_t s2, f16x2v_t b2) {
   const f16x2v_t off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const f16x2v_t q = __builtin_bit_cast(f16x2v_t, and_or(d >> (4 * i), mask, magic)) + off;
+    const f16x2v_t q = __builtin_bit_cast(f16x2v_t, and_or(d >> (4 * i), 0x000F000Fu, 0x64006400u)) + off;
     w[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return __builtin_bit_cast(f16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-template <bool kGateUp>
-__global__ __launch_bounds__(kWaves * 64) void k_expert_gemm(LayerArgs L, ChunkArgs C, int n_ct) {
-  // ---- workgroup -> (tile, column tile), XCD-aware ----
-  const int lin = blockIdx.x;
-  const int xcd = lin & 7, m = lin >> 3;
-  const int slot = (m / n_ct) * 8 + xcd, ct = m % n_ct;
-  if (slot >= *C.n_tiles) return;
-  const int tile = C.sched[slot];
-  const int e = C.tiles[3 * tile], r0 = C.tiles[3 * tile + 1], rows = C.tiles[3 * tile + 2];
-  const bool shared = e == L.E;
-  const int Iw = shared ? L.Is : L.I;
-  if (Iw == 0) return;
+// Weight codes of one K group for the wave's 2 blocks.
+struct QGroup {
+  uint4 c0, c1;
+  uint32_t s0, s1;
+};
+
+// Per-workgroup tile description.
+struct Tile {
+  int e, r0, rows, rowbase, ncols, G, ct;
+  bool shared;
+};
+
+template <bool kGateUp, int NF>
+__device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C, const Tile& T, uint8_t* smem) {
   const int H = L.H;
-  // gate/up: columns = intermediate (32-row blocks of gate and up); down: output columns.
-  const int ncols = kGateUp ? Iw : H;
-  const int K = kGateUp ? H : Iw;
-  const int G = K / kGroup;
-  const int cb0 = ct * (kGateUp ? 4 : 8);  // first 32-column block of this column tile
-  if (cb0 * 32 >= ncols) return;
-  const int nvb = min(kGateUp ? 4 : 8, ncols / 32 - cb0);  // valid 32-column blocks (gate/up: per matrix)
-
-  const uint8_t* ebase = expert_base(L, e);
-  const uint8_t* wbase = kGateUp ? ebase : ebase + (shared ? L.shared_gateup_bytes : L.gateup_bytes);
-  const int seg = shared ? 0 : C.offsets[e];
-  const int rowbase = shared ? C.Tk + r0 : seg + r0;  // hbuf row of the tile's first row
-
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* bt = smem;                                     // B: [2][blk][c][lane] x 16 B
-  uint8_t* at = smem + 2 * kBufBytes;                     // A: [2][256 rows][kARow B]
-  int* tok = reinterpret_cast<int*>(at + 2 * kABufBytes);  // [256]
-
+  const int G = T.G;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, col = lane & 31;
+  uint8_t* at = smem;  // A: [2][128 rows][kARow B]
+  int* tok = reinterpret_cast<int*>(smem + 2 * kABufBytes);
 
-  if (tid < kTileRows) {
-    int t = 0;
-    if (tid < rows) t = shared ? r0 + tid : C.sorted[seg + r0 + tid] / L.k;
-    tok[tid] = t;
+  // ---- the wave's 2 weight blocks: base of group 0 and stride per group ----
+  // gate/up: block nb = 8 ct + wave of gate (b = 0) and of up (b = 1);
+  // down: blocks nb = 2 (8 ct + wave) + b.
+  const int nb0 = kGateUp ? T.ct * kWaves + wave : (T.ct * kWaves + wave) * 2;
+  const int nvb = min(kGateUp ? 1 : 2, T.ncols / 32 - nb0);  // valid blocks of this wave (<= 0: none)
+  const bool wave_cols = __builtin_amdgcn_readfirstlane(nvb > 0 ? 1 : 0) != 0;
+  const uint8_t* ebase = expert_base(L, T.e);
+  const uint8_t* wbase = kGateUp ? ebase : ebase + (T.shared ? L.shared_gateup_bytes : L.gateup_bytes);
+  const int64_t qstride = kGateUp ? 2 * kBlockBytes : kBlockBytes;
+  const uint8_t *qb0, *qb1;
+  if (kGateUp) {
+    const int nb = wave_cols ? nb0 : 0;
+    qb0 = wbase + (int64_t)nb * G * 2 * kBlockBytes;
+    qb1 = qb0 + kBlockBytes;
+  } else {
+    // A block past the column edge reloads a valid one; its results are never stored.
+    const int n0 = wave_cols ? nb0 : 0, n1 = wave_cols && nvb > 1 ? nb0 + 1 : n0;
+    qb0 = wbase + (int64_t)n0 * G * kBlockBytes;
+    qb1 = wbase + (int64_t)n1 * G * kBlockBytes;
+  }
+  auto load_q = [&](int g, QGroup& q) {
+    const int64_t off = (int64_t)(g < G ? g : G - 1) * qstride;
+    q.c0 = *reinterpret_cast<const uint4*>(qb0 + off + lane * 16);
+    q.c1 = *reinterpret_cast<const uint4*>(qb1 + off + lane * 16);
+    q.s0 = *reinterpret_cast<const uint32_t*>(qb0 + off + kCodeBytes + col * 4);
+    q.s1 = *reinterpret_cast<const uint32_t*>(qb1 + off + kCodeBytes + col * 4);
+  };
+  QGroup q0, q1, q2, q3;
+  load_q(0, q0);
+  load_q(1, q1);
+  load_q(2, q2);
+  load_q(3, q3);
+
+  // ---- token of each row (gate/up gathers activation rows by token) ----
+  if (kGateUp) {
+    if (tid < kTileRows) {
+      int t = 0;
+      if (tid < T.rows) t = T.shared ? T.r0 + tid : C.sorted[T.rowbase + tid] / L.k;
+      tok[tid] = t;
+    }
+    __syncthreads();
   }
 
-  // ---- weight block rebuilt by this wave: LDS block `wave`, lane `lane` ----
-  // gate/up: LDS blocks 0..3 are gate, 4..7 up, column block cb0 + (wave & 3);
-  // down: column block cb0 + wave.
-  const int qj = kGateUp ? (wave & 3) : wave;
-  const int qjc = qj < nvb ? qj : nvb - 1;  // columns past the edge rebuild a valid block, never stored
-  const uint8_t* qsrc = kGateUp ? wbase + ((int64_t)(cb0 + qjc) * G * 2 + (wave >> 2)) * kBlockBytes
-                                : wbase + (int64_t)(cb0 + qjc) * G * kBlockBytes;
-  const int64_t qstride = kGateUp ? 2 * kBlockBytes : kBlockBytes;
-  uint4* qdst0 = reinterpret_cast<uint4*>(bt) + wave * 4 * 64 + lane;
-
-  __syncthreads();  // tok visible
-
-  // ---- A staging: thread t moves 16-byte parts (row t/8 + 64 i, part t%8), i < 4 ----
+  // ---- A staging: thread t moves 16-byte part t%8 of rows t/8 and t/8 + 64 ----
   const int apart = tid & 7, arow0 = tid >> 3;
-  const uint16_t* asrc0;
-  const uint16_t* asrc1;
-  const uint16_t* asrc2;
-  const uint16_t* asrc3;
-  // Every thread stages all four rows each group, without branches, so the
-  // number of loads in flight is the same on every path and the compiler can
-  // wait for exactly the loads it needs; rows past the tile's end load a
-  // valid row (cache hits) and their results are never stored out.
+  const uint16_t *asrc0, *asrc1;
   {
     auto rowptr = [&](int r) {
-      const int rr = r < rows ? r : rows - 1;
-      return (kGateUp ? C.x16 + (int64_t)tok[rr] * H : C.hbuf + (int64_t)(rowbase + rr) * C.Imax) + apart * 8;
+      const int rr = r < T.rows ? r : T.rows - 1;
+      return (kGateUp ? C.x16 + (int64_t)tok[rr] * H : C.hbuf + (int64_t)(T.rowbase + rr) * C.Imax) + apart * 8;
     };
     asrc0 = rowptr(arow0);
     asrc1 = rowptr(arow0 + 64);
-    asrc2 = rowptr(arow0 + 128);
-    asrc3 = rowptr(arow0 + 192);
   }
-  // Two staging register sets: A of even groups in ae*, of odd groups in ao*,
-  // loaded two groups before they are written to LDS.
-  uint4 ae0 = make_uint4(0, 0, 0, 0), ae1 = ae0, ae2 = ae0, ae3 = ae0;
-  uint4 ao0 = ae0, ao1 = ae0, ao2 = ae0, ao3 = ae0;
   uint8_t* const adst = at + apart * 16 + arow0 * kARow;
-#define MOE_LOAD_A(g, S)                                                                   \
-  do {                                                                                     \
-    const int gg_ = (g) < G ? (g) : G - 1; /* past the end: a valid, unused group */       \
-    S##0 = *reinterpret_cast<const uint4*>(asrc0 + gg_ * kGroup);                 \
-    S##1 = *reinterpret_cast<const uint4*>(asrc1 + gg_ * kGroup);                 \
-    S##2 = *reinterpret_cast<const uint4*>(asrc2 + gg_ * kGroup);                 \
-    S##3 = *reinterpret_cast<const uint4*>(asrc3 + gg_ * kGroup);                 \
+  // Rows of fragments the tile does not use are not staged.
+#define MOE_LOAD_A(g, S)                                                      \
+  do {                                                                        \
+    const int gg_ = (g) < G ? (g) : G - 1; /* past the end: a valid, unused group */ \
+    S##0 = *reinterpret_cast<const uint4*>(asrc0 + gg_ * kGroup);            \
+    if (NF > 2) S##1 = *reinterpret_cast<const uint4*>(asrc1 + gg_ * kGroup); \
   } while (0)
-#define MOE_STORE_A(buf, S)                                                                \
-  do {                                                                                     \
-    uint8_t* d_ = adst + (buf) * kABufBytes;                                               \
-    *reinterpret_cast<uint4*>(d_) = S##0;                                         \
-    *reinterpret_cast<uint4*>(d_ + 64 * kARow) = S##1;                            \
-    *reinterpret_cast<uint4*>(d_ + 128 * kARow) = S##2;                           \
-    *reinterpret_cast<uint4*>(d_ + 192 * kARow) = S##3;                           \
+#define MOE_STORE_A(buf, S)                                                   \
+  do {                                                                        \
+    uint8_t* d_ = adst + (buf) * kABufBytes;                                  \
+    *reinterpret_cast<uint4*>(d_) = S##0;                                     \
+    if (NF > 2) *reinterpret_cast<uint4*>(d_ + 64 * kARow) = S##1;            \
   } while (0)
 
-  // ---- weight codes: a ring of 4 groups in registers (qc0..qc3, qs0..qs3) ----
-  uint4 qc0, qc1, qc2, qc3;
-  uint32_t qs0, qs1, qs2, qs3;
-  auto load_q = [&](int g, uint4& code, uint32_t& sb) {
-    const int gg = g < G ? g : G - 1;
-    const uint8_t* blk = qsrc + gg * qstride;
-    code = *reinterpret_cast<const uint4*>(blk + lane * 16);
-    sb = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
-  };
-  const uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
-  auto dequant_store = [&](int buf, const uint4& code, uint32_t sb) {
-    const _Float16 sh = (_Float16)bf16_bits_to_f32(sb & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(sb >> 16);
-    const f16x2v_t s2 = {sh, sh}, b2 = {bh, bh};
-    uint4* dst = qdst0 + buf * (kBufBytes / 16);
-    dst[0 * 64] = dequant8(code.x, s2, b2, kMask, kMagic);
-    dst[1 * 64] = dequant8(code.y, s2, b2, kMask, kMagic);
-    dst[2 * 64] = dequant8(code.z, s2, b2, kMask, kMagic);
-    dst[3 * 64] = dequant8(code.w, s2, b2, kMask, kMagic);
-  };
-
-  const bool wave_active = __builtin_amdgcn_readfirstlane(wm * 64 < rows ? 1 : 0) != 0;
-  int wblk[4];
+  f32x16_t acc[NF][2];
 #pragma unroll
-  for (int b = 0; b < 4; b++) wblk[b] = kGateUp ? (b >> 1) * 4 + 2 * wn + (b & 1) : 4 * wn + b;
-  // A fragment byte offsets inside an A buffer: rows 64 wm + 32 f + col, columns 32 h + 8 c.
-  const int aoff0 = (wm * 64 + col) * kARow + h * 64;
+  for (int f = 0; f < NF; f++) {
+    acc[f][0] = f32x16_t{};
+    acc[f][1] = f32x16_t{};
+  }
 
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int f = 0; f < 2; f++)
-#pragma unroll
-    for (int b = 0; b < 4; b++) acc[f][b] = f32x16_t{};
-
-  // One group of MFMAs on buffers `cur`, fused with the rebuild of the next
-  // group's weights (code, sb) into B buffer `nxt`.  The sched_group_barrier
-  // sequence pins an interleaved order (each MFMA followed by two VALU ops of
-  // the rebuild), so the VALU work runs under the MFMA pipe.
-  auto mma_fused = [&](int cur, const uint4& code, uint32_t sb, int nxt) {
-    const _Float16 sh = (_Float16)bf16_bits_to_f32(sb & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(sb >> 16);
-    const f16x2v_t s2 = {sh, sh}, b2 = {bh, bh};
-    const uint4* bsrc = reinterpret_cast<const uint4*>(bt + cur * kBufBytes);
-    const uint8_t* asrc_l = at + cur * kABufBytes + aoff0;
-    uint4* dst = qdst0 + nxt * (kBufBytes / 16);
-    const uint32_t cw[4] = {code.x, code.y, code.z, code.w};
+  const int aoff0 = col * kARow + h * 64;  // lane's A bytes: row 32 f + col, columns 32 h + 8 c
+  // MFMAs of one K group: A from LDS buffer `cur`, B rebuilt from q (zero
+  // weights when `live` is false: groups padded past G).
+  auto compute = [&](int cur, const QGroup& q, bool live) {
+    const uint32_t sb0 = live ? q.s0 : 0u, sb1 = live ? q.s1 : 0u;
+    const _Float16 sh0 = (_Float16)bf16_bits_to_f32(sb0 & 0xFFFFu), bh0 = (_Float16)bf16_bits_to_f32(sb0 >> 16);
+    const _Float16 sh1 = (_Float16)bf16_bits_to_f32(sb1 & 0xFFFFu), bh1 = (_Float16)bf16_bits_to_f32(sb1 >> 16);
+    const f16x2v_t s20 = {sh0, sh0}, b20 = {bh0, bh0}, s21 = {sh1, sh1}, b21 = {bh1, bh1};
+    const uint32_t cw0[4] = {q.c0.x, q.c0.y, q.c0.z, q.c0.w};
+    const uint32_t cw1[4] = {q.c1.x, q.c1.y, q.c1.z, q.c1.w};
+    const uint8_t* abase = at + cur * kABufBytes + aoff0;
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      f16x8_t bv[4], av[2];
+      f16x8_t av[NF];
 #pragma unroll
-      for (int b = 0; b < 4; b++) bv[b] = __builtin_bit_cast(f16x8_t, bsrc[(wblk[b] * 4 + c) * 64 + lane]);
+      for (int f = 0; f < NF; f++) av[f] = *reinterpret_cast<const f16x8_t*>(abase + f * 32 * kARow + c * 16);
+      const f16x8_t bv0 = dequant8(cw0[c], s20, b20);
+      const f16x8_t bv1 = dequant8(cw1[c], s21, b21);
 #pragma unroll
-      for (int f = 0; f < 2; f++)
-        av[f] = *reinterpret_cast<const f16x8_t*>(asrc_l + f * 32 * kARow + c * 16);
-      const uint4 dq = dequant8(cw[c], s2, b2, kMask, kMagic);
-#pragma unroll
-      for (int f = 0; f < 2; f++)
-#pragma unroll
-        for (int b = 0; b < 4; b++) acc[f][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[f], bv[b], acc[f][b], 0, 0, 0);
-      dst[c * 64] = dq;
-    }
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 6 LDS reads (A and B operands of this k-step)
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // 2 VALU
+      for (int f = 0; f < NF; f++) {
+        acc[f][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[f], bv0, acc[f][0], 0, 0, 0);
+        acc[f][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[f], bv1, acc[f][1], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // 1 LDS write (rebuilt weights)
     }
   };
 
-  // One pipeline step for group g, ring slot g % 4 holding (QC, QS) for the
-  // codes of g+4 to load and (NC, NS) the codes of g+1 to rebuild; AS is the
-  // staging set of group g+1 (its parity): MFMAs of g (buffers g%2) fused with
-  // the rebuild of g+1, A of g+1 into LDS, loads for A of g+3 and codes of g+4.
-#define MOE_GEMM_STEP(g, CUR, QC, QS, NC, NS, AS)               \
-  do {                                                        \
-    if (wave_active)                                          \
-      mma_fused(CUR, NC, NS, (CUR) ^ 1);                      \
-    else                                                      \
-      dequant_store((CUR) ^ 1, NC, NS);                       \
-    MOE_STORE_A((CUR) ^ 1, AS);                               \
-    MOE_LOAD_A((g) + 3, AS);                                  \
-    load_q((g) + 4, QC, QS);                                  \
-    __syncthreads();                                          \
+  // Pipeline step of group g: MFMAs of g (codes Q, A buffer g%2), A of g+1
+  // into the other buffer, loads of A for g+3 (register set AS) and of the
+  // codes of g+4 (into Q, which g no longer needs).
+#define MOE_GEMM_STEP(g, CUR, Q, AS)          \
+  do {                                        \
+    if (wave_cols) compute(CUR, Q, (g) < G);  \
+    MOE_STORE_A((CUR) ^ 1, AS);               \
+    MOE_LOAD_A((g) + 3, AS);                  \
+    load_q((g) + 4, Q);                       \
+    __syncthreads();                          \
   } while (0)
 
-  // Prologue: codes of groups 0..3, A and weights of group 0, A loads of groups 1, 2.
-  load_q(0, qc0, qs0);
-  load_q(1, qc1, qs1);
-  load_q(2, qc2, qs2);
-  load_q(3, qc3, qs3);
+  uint4 ae0 = make_uint4(0, 0, 0, 0), ae1 = ae0;
+  uint4 ao0 = ae0, ao1 = ae0;
+  // Prologue: A of group 0 into LDS; A loads of groups 1, 2.
   MOE_LOAD_A(0, ae);
   MOE_STORE_A(0, ae);
-  dequant_store(0, qc0, qs0);
   MOE_LOAD_A(1, ao);
   MOE_LOAD_A(2, ae);
   __syncthreads();
 
-  for (int g = 0; g < G; g += 4) {
-    MOE_GEMM_STEP(g, 0, qc0, qs0, qc1, qs1, ao);
-    if (g + 1 >= G) break;
-    MOE_GEMM_STEP(g + 1, 1, qc1, qs1, qc2, qs2, ae);
-    if (g + 2 >= G) break;
-    MOE_GEMM_STEP(g + 2, 0, qc2, qs2, qc3, qs3, ao);
-    if (g + 3 >= G) break;
-    MOE_GEMM_STEP(g + 3, 1, qc3, qs3, qc0, qs0, ae);
+  // G is padded up to a multiple of 4 with groups whose weights read as zero;
+  // a loop without early exits lets the compiler count the loads in flight
+  // across the back edge instead of draining them at the loop header.
+  const int Gp = (G + 3) & ~3;
+  for (int g = 0; g < Gp; g += 4) {
+    MOE_GEMM_STEP(g, 0, q0, ao);
+    MOE_GEMM_STEP(g + 1, 1, q1, ae);
+    MOE_GEMM_STEP(g + 2, 0, q2, ao);
+    MOE_GEMM_STEP(g + 3, 1, q3, ae);
   }
 #undef MOE_GEMM_STEP
 #undef MOE_LOAD_A
 #undef MOE_STORE_A
 
-  if (!wave_active) return;
-  // ---- epilogue: undo the 2^-8 activation scale ----
-  if (kGateUp) {
+  // ---- epilogue (the last step ended with a barrier: LDS is free) ----
+  if (!kGateUp && T.shared) {
+    // Shared expert: y = 256 * acc in fp32, straight to memory.
+    if (!wave_cols) return;
 #pragma unroll
-    for (int f = 0; f < 2; f++) {
+    for (int f = 0; f < NF; f++) {
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
-        if (2 * wn + j >= nvb) continue;
-        const int icol = (cb0 + 2 * wn + j) * 32 + col;
+      for (int b = 0; b < 2; b++) {
+        if (b >= nvb) continue;
+        const int ocol = (nb0 + b) * 32 + col;
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-          const int r = wm * 64 + f * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (r < rows) {
-            const float hv = silu_mul(256.f * acc[f][j][i], 256.f * acc[f][j + 2][i]);
-            C.hbuf[(int64_t)(rowbase + r) * C.Imax + icol] = f32_to_f16_bits(hv * (1.f / 256.f));
-          }
+          const int r = f * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (r < T.rows) C.y[(int64_t)(T.r0 + r) * H + ocol] = 256.f * acc[f][b][i];
         }
       }
     }
-  } else {
-    // Routed rows: fp16(out / 256) per assignment, combined per token later
-    // (k_combine); the shared expert's rows go straight into y in fp32.
+    return;
+  }
+  // gate/up: fp16(silu(256 g) * 256 u / 256) into hbuf; down (routed rows):
+  // fp16(out / 256) into obuf, combined per token later (k_combine).  The
+  // tile is assembled in LDS, then stored row by row in 16-byte pieces.
+  constexpr int kRowB = kGateUp ? kEpiRowGateUp : kEpiRowDown;
+  if (wave_cols) {
 #pragma unroll
-    for (int f = 0; f < 2; f++) {
+    for (int f = 0; f < NF; f++) {
 #pragma unroll
-      for (int b = 0; b < 4; b++) {
-        if (4 * wn + b >= nvb) continue;
-        const int ocol = (cb0 + 4 * wn + b) * 32 + col;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int r = wm * 64 + f * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (r < rows) {
-            if (shared)
-              C.y[(int64_t)tok[r] * H + ocol] = 256.f * acc[f][b][i];
-            else
-              C.obuf[(int64_t)(rowbase + r) * H + ocol] = f32_to_f16_bits(acc[f][b][i]);
-          }
+      for (int i = 0; i < 16; i++) {
+        const int r = f * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (kGateUp) {
+          const float hv = silu_mul(256.f * acc[f][0][i], 256.f * acc[f][1][i]);
+          *reinterpret_cast<uint16_t*>(smem + r * kRowB + (wave * 32 + col) * 2) = f32_to_f16_bits(hv * (1.f / 256.f));
+        } else {
+          *reinterpret_cast<uint16_t*>(smem + r * kRowB + (wave * 64 + col) * 2) = f32_to_f16_bits(acc[f][0][i]);
+          *reinterpret_cast<uint16_t*>(smem + r * kRowB + (wave * 64 + 32 + col) * 2) = f32_to_f16_bits(acc[f][1][i]);
         }
       }
     }
   }
+  __syncthreads();
+  constexpr int kColsWg = kGateUp ? kGateUpColsPerWg : kDownColsPerWg;
+  constexpr int kPieces = kColsWg / 8;           // 16-byte pieces per row
+  constexpr int kRowsPerPass = kWaves * 64 / kPieces;
+  const int piece = tid % kPieces, prow = tid / kPieces;
+  const int c0 = T.ct * kColsWg + piece * 8;      // first column of this thread's piece
+  if (c0 < T.ncols) {
+    uint16_t* dst = kGateUp ? C.hbuf + (int64_t)T.rowbase * C.Imax + c0 : C.obuf + (int64_t)T.rowbase * H + c0;
+    const int64_t rs = kGateUp ? C.Imax : H;
+#pragma unroll
+    for (int r = prow; r < NF * 32; r += kRowsPerPass)
+      if (r < T.rows) *reinterpret_cast<uint4*>(dst + r * rs) = *reinterpret_cast<const uint4*>(smem + r * kRowB + piece * 16);
+  }
+}
+
+template <bool kGateUp>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_expert_gemm(LayerArgs L, ChunkArgs C, int n_ct) {
+  // ---- workgroup -> (tile, column tile), XCD-aware ----
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, m = lin >> 3;
+  const int slot = (m / n_ct) * 8 + xcd, ct = m % n_ct;
+  // n_tiles and the slot's descriptor are read together (independent loads).
+  const int nt = *C.n_tiles;
+  const int4 d = reinterpret_cast<const int4*>(C.sched)[slot < nt ? slot : 0];
+  if (slot >= nt) return;
+  Tile T;
+  T.e = d.x;
+  T.r0 = d.y;
+  T.rows = d.z;
+  T.rowbase = d.w;  // hbuf / obuf row of the tile's first row
+  T.ct = ct;
+  T.shared = T.e == L.E;
+  const int Iw = T.shared ? L.Is : L.I;
+  if (Iw == 0 || T.rows <= 0) return;
+  // gate/up: columns = intermediate (32-row blocks of gate and up); down: output columns.
+  T.ncols = kGateUp ? Iw : L.H;
+  if (ct * (kGateUp ? kGateUpColsPerWg : kDownColsPerWg) >= T.ncols) return;
+  T.G = (kGateUp ? L.H : Iw) / kGroup;
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int nf = (T.rows + 31) >> 5;
+  if (nf <= 1)
+    gemm_tile<kGateUp, 1>(L, C, T, smem);
+  else if (nf == 2)
+    gemm_tile<kGateUp, 2>(L, C, T, smem);
+  else if (nf == 3)
+    gemm_tile<kGateUp, 3>(L, C, T, smem);
+  else
+    gemm_tile<kGateUp, 4>(L, C, T, smem);
 }
 
 // y[t] = (shared expert's output, already in y) + sum_j w_tj * 256 * obuf[pos(t, j)]
@@ -373,17 +378,19 @@ __global__ __launch_bounds__(256) void k_combine(LayerArgs L, ChunkArgs C) {
 // ---------------------------------------------------------------------------
 template <bool kGateUp>
 static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s) {
+  constexpr int smem = kGateUp ? kSmemGateUp : kSmemDown;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm<kGateUp>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm<kGateUp>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  const int n_ct = kGateUp ? (Imax + 127) / 128 : (L.H + 255) / 256;
+  const int n_ct = kGateUp ? (Imax + kGateUpColsPerWg - 1) / kGateUpColsPerWg
+                           : (L.H + kDownColsPerWg - 1) / kDownColsPerWg;
   const int tiles8 = (max_tiles + 7) / 8 * 8;
-  k_expert_gemm<kGateUp><<<dim3((unsigned)(tiles8 * n_ct)), dim3(kWaves * 64), kSmem, s>>>(L, C, n_ct);
+  k_expert_gemm<kGateUp><<<dim3((unsigned)(tiles8 * n_ct)), dim3(kWaves * 64), smem, s>>>(L, C, n_ct);
   return hipGetLastError();
 }
 

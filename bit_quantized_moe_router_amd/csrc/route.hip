@@ -468,12 +468,17 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
   // Execution order of the tiles for the grouped GEMMs (longest first): the
   // shared expert's full tiles, the routed full tiles, the routed partial
   // tiles, the shared expert's partial tile.
+  // Each slot holds the tile's descriptor (expert, first row, rows, first
+  // row in expert-sorted order).
   const int sfull = with_shared ? T / BM : 0;
   if (sched && tid < E) {
-    const int ts = sc1[tid] - nt;
+    const int off_e = sc0[tid] - tot;
     const int fpos = sfull + sc3[tid] - nfull;
-    for (int r = 0; r < nfull; r++) sched[fpos + r] = ts + r;
-    if (npart) sched[sfull + s_full_total + sc4[tid] - 1] = ts + nfull;
+    for (int r = 0; r < nfull; r++)
+      reinterpret_cast<int4*>(sched)[fpos + r] = make_int4(tid, r * BM, BM, off_e + r * BM);
+    if (npart)
+      reinterpret_cast<int4*>(sched)[sfull + s_full_total + sc4[tid] - 1] =
+          make_int4(tid, nfull * BM, tot - nfull * BM, off_e + nfull * BM);
   }
   if (tid < E) {
     const int off_e = sc0[tid] - tot;
@@ -506,7 +511,9 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
     tiles[3 * (rt + r) + 0] = E;
     tiles[3 * (rt + r) + 1] = r * BM;
     tiles[3 * (rt + r) + 2] = min(BM, T - r * BM);
-    if (sched) sched[r < sfull ? r : rt + nshared - 1] = rt + r;
+    if (sched)
+      reinterpret_cast<int4*>(sched)[r < sfull ? r : rt + nshared - 1] =
+          make_int4(E, r * BM, min(BM, T - r * BM), T * k + r * BM);
   }
   if (tid == 0) {
     n_tiles[0] = rt + nshared;

@@ -72,8 +72,8 @@ typedef struct {
                               T <= R* and the grouped GEMM path above; -1 = library default;
                               0 = always GEMM; at most 8 */
     int32_t max_chunk;     /* tokens per prefill chunk (1..8192); routing metadata is per chunk */
-    int32_t tile_rows;     /* BM: rows per tile of the block map; 0 = library default (256);
-                              one of 16, 32, 64, 128, 256 */
+    int32_t tile_rows;     /* BM: rows per tile of the block map; 0 = library default (128);
+                              one of 16, 32, 64, 128 */
 } moe_layer_desc;
 
 /*

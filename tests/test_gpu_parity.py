@@ -132,7 +132,7 @@ ROUTE_CASES = ["tiny", "decode", "smallrow2", "smallrow5", "smallrow8", "prefill
 def test_route_bitexact(M, name):
     case = mi.make_case(name)
     lay = get_layer(M, case)
-    BM = lay.desc.tile_rows or 256  # library default
+    BM = lay.desc.tile_rows or 128  # library default
     x, bias = case["x"], case["bias"]
     for c0 in range(0, case["T"], mi.CHUNK):
         xc = x[c0:c0 + mi.CHUNK]
