@@ -141,19 +141,15 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
     q.s0 = *reinterpret_cast<const uint32_t*>(qb0 + off + kCodeBytes + col * 4);
     q.s1 = *reinterpret_cast<const uint32_t*>(qb1 + off + kCodeBytes + col * 4);
   };
+  // ---- token of each row (gate/up gathers activation rows by token) ----
+  // The index load goes out before the first weight codes so that waiting
+  // for it leaves those in flight.
+  int my_tok = 0;
+  if (kGateUp && tid < kTileRows && tid < T.rows) my_tok = T.shared ? T.r0 + tid : C.sorted[T.rowbase + tid];
   QGroup q0, q1, q2, q3;
   load_q(0, q0);
-  load_q(1, q1);
-  load_q(2, q2);
-  load_q(3, q3);
-
-  // ---- token of each row (gate/up gathers activation rows by token) ----
   if (kGateUp) {
-    if (tid < kTileRows) {
-      int t = 0;
-      if (tid < T.rows) t = T.shared ? T.r0 + tid : C.sorted[T.rowbase + tid] / L.k;
-      tok[tid] = t;
-    }
+    if (tid < kTileRows) tok[tid] = T.shared ? my_tok : my_tok / L.k;
     __syncthreads();
   }
 
@@ -191,37 +187,65 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   }
 
   const int aoff0 = col * kARow + h * 64;  // lane's A bytes: row 32 f + col, columns 32 h + 8 c
-  // MFMAs of one K group: A from LDS buffer `cur`, B rebuilt from q (zero
-  // weights when `live` is false: groups padded past G).
-  auto compute = [&](int cur, const QGroup& q, bool live) {
-    const uint32_t sb0 = live ? q.s0 : 0u, sb1 = live ? q.s1 : 0u;
-    const _Float16 sh0 = (_Float16)bf16_bits_to_f32(sb0 & 0xFFFFu), bh0 = (_Float16)bf16_bits_to_f32(sb0 >> 16);
-    const _Float16 sh1 = (_Float16)bf16_bits_to_f32(sb1 & 0xFFFFu), bh1 = (_Float16)bf16_bits_to_f32(sb1 >> 16);
-    const f16x2v_t s20 = {sh0, sh0}, b20 = {bh0, bh0}, s21 = {sh1, sh1}, b21 = {bh1, bh1};
+  // Scale and bias of one block as fp16 pairs; zero (weights rebuild to 0)
+  // for groups padded past G.
+  auto sbpair = [&](uint32_t sb, bool live, f16x2v_t& s2, f16x2v_t& b2) {
+    const uint32_t v = live ? sb : 0u;
+    const _Float16 sh = (_Float16)bf16_bits_to_f32(v & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(v >> 16);
+    s2 = f16x2v_t{sh, sh};
+    b2 = f16x2v_t{bh, bh};
+  };
+  // B operands of k-step 0 of the current group, rebuilt during the last
+  // k-step of the previous group.
+  f16x8_t bc0, bc1;
+  // MFMAs of one K group (codes q, A buffer `cur`), software pipelined: the
+  // A fragments and weights of k-step c+1 (for c = 3: k-step 0 of the next
+  // group, codes qn) are read and rebuilt while the MFMAs of k-step c run.
+  auto compute = [&](int cur, const QGroup& q, const QGroup& qn, bool live, bool live_n) {
+    f16x2v_t s20, b20, s21, b21, n20, m20, n21, m21;
+    sbpair(q.s0, live, s20, b20);
+    sbpair(q.s1, live, s21, b21);
+    sbpair(qn.s0, live_n, n20, m20);
+    sbpair(qn.s1, live_n, n21, m21);
     const uint32_t cw0[4] = {q.c0.x, q.c0.y, q.c0.z, q.c0.w};
     const uint32_t cw1[4] = {q.c1.x, q.c1.y, q.c1.z, q.c1.w};
     const uint8_t* abase = at + cur * kABufBytes + aoff0;
+    f16x8_t av[NF];
+#pragma unroll
+    for (int f = 0; f < NF; f++) av[f] = *reinterpret_cast<const f16x8_t*>(abase + f * 32 * kARow);
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      f16x8_t av[NF];
+      f16x8_t an[NF], bn0, bn1;
+      if (c < 3) {
 #pragma unroll
-      for (int f = 0; f < NF; f++) av[f] = *reinterpret_cast<const f16x8_t*>(abase + f * 32 * kARow + c * 16);
-      const f16x8_t bv0 = dequant8(cw0[c], s20, b20);
-      const f16x8_t bv1 = dequant8(cw1[c], s21, b21);
+        for (int f = 0; f < NF; f++) an[f] = *reinterpret_cast<const f16x8_t*>(abase + f * 32 * kARow + (c + 1) * 16);
+        bn0 = dequant8(cw0[c + 1], s20, b20);
+        bn1 = dequant8(cw1[c + 1], s21, b21);
+      } else {
+        bn0 = dequant8(qn.c0.x, n20, m20);
+        bn1 = dequant8(qn.c1.x, n21, m21);
+      }
 #pragma unroll
       for (int f = 0; f < NF; f++) {
-        acc[f][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[f], bv0, acc[f][0], 0, 0, 0);
-        acc[f][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[f], bv1, acc[f][1], 0, 0, 0);
+        acc[f][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[f], bc0, acc[f][0], 0, 0, 0);
+        acc[f][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[f], bc1, acc[f][1], 0, 0, 0);
       }
+      if (c < 3) {
+#pragma unroll
+        for (int f = 0; f < NF; f++) av[f] = an[f];
+      }
+      bc0 = bn0;
+      bc1 = bn1;
     }
   };
 
-  // Pipeline step of group g: MFMAs of g (codes Q, A buffer g%2), A of g+1
-  // into the other buffer, loads of A for g+3 (register set AS) and of the
-  // codes of g+4 (into Q, which g no longer needs).
-#define MOE_GEMM_STEP(g, CUR, Q, AS)          \
-  do {                                        \
-    if (wave_cols) compute(CUR, Q, (g) < G);  \
+  // Pipeline step of group g: MFMAs of g (codes Q, A buffer g%2; QN holds
+  // the codes of g+1), A of g+1 into the other buffer, loads of A for g+3
+  // (register set AS) and of the codes of g+4 (into Q, which g no longer
+  // needs).
+#define MOE_GEMM_STEP(g, CUR, Q, QN, AS)                     \
+  do {                                                       \
+    if (wave_cols) compute(CUR, Q, QN, (g) < G, (g) + 1 < G);  \
     MOE_STORE_A((CUR) ^ 1, AS);               \
     MOE_LOAD_A((g) + 3, AS);                  \
     load_q((g) + 4, Q);                       \
@@ -230,11 +254,24 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
 
   uint4 ae0 = make_uint4(0, 0, 0, 0), ae1 = ae0;
   uint4 ao0 = ae0, ao1 = ae0;
-  // Prologue: A of group 0 into LDS; A loads of groups 1, 2.
+  // Prologue: the loads go out in the order of the steady state (A of j+3,
+  // then codes of j+4, for j = -3..-1) so that the loads in flight at the
+  // loop header line up with those at the back edge and the compiler's
+  // counts of loads to wait for are the steady-state ones.
   MOE_LOAD_A(0, ae);
-  MOE_STORE_A(0, ae);
+  load_q(1, q1);
   MOE_LOAD_A(1, ao);
+  load_q(2, q2);
+  MOE_STORE_A(0, ae);
   MOE_LOAD_A(2, ae);
+  load_q(3, q3);
+  if (wave_cols) {
+    f16x2v_t s20, b20, s21, b21;
+    sbpair(q0.s0, true, s20, b20);
+    sbpair(q0.s1, true, s21, b21);
+    bc0 = dequant8(q0.c0.x, s20, b20);
+    bc1 = dequant8(q0.c1.x, s21, b21);
+  }
   __syncthreads();
 
   // G is padded up to a multiple of 4 with groups whose weights read as zero;
@@ -242,10 +279,10 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   // across the back edge instead of draining them at the loop header.
   const int Gp = (G + 3) & ~3;
   for (int g = 0; g < Gp; g += 4) {
-    MOE_GEMM_STEP(g, 0, q0, ao);
-    MOE_GEMM_STEP(g + 1, 1, q1, ae);
-    MOE_GEMM_STEP(g + 2, 0, q2, ao);
-    MOE_GEMM_STEP(g + 3, 1, q3, ae);
+    MOE_GEMM_STEP(g, 0, q0, q1, ao);
+    MOE_GEMM_STEP(g + 1, 1, q1, q2, ae);
+    MOE_GEMM_STEP(g + 2, 0, q2, q3, ao);
+    MOE_GEMM_STEP(g + 3, 1, q3, q0, ae);
   }
 #undef MOE_GEMM_STEP
 #undef MOE_LOAD_A
