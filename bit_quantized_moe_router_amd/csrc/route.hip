@@ -155,98 +155,168 @@ __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Many tokens, step 1: screened logits a = sum_h x * bf16(Wr) with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation), split over kScreenSplit
-// slices of h so that enough waves are in flight; each slice writes its
-// partial sums (summed with the bias in a fixed order by k_route_exact).
-// Workgroup tile 64 tokens x 64 experts, four 32x32 waves, operands loaded
-// straight from memory one group ahead.  The workgroups of the first token
-// tile also write the partial sums of Wr_e^2 (float64) for the error bound.
+// Many tokens, step 1: screened logits.  Each router weight w (fp32) is split
+// into hi = bf16(w) and lo = bf16(w - hi) (w - hi is exact in fp32, and
+// |w - hi - lo| <= 2^-17 |w|); a = sum_h x*hi + x*lo with
+// v_mfma_f32_32x32x16_bf16 (bf16 x bf16 products exact in fp32, fp32
+// accumulation), split over kScreenSplit slices of h, each slice writing its
+// partial sums.  Workgroup tile 64 tokens x 64 experts, four 32x32 waves; per
+// 64-wide group the workgroup stages x and the hi/lo weights in LDS (double
+// buffered, loads two groups ahead).  The workgroups of the first token tile
+// also write the per-slice sums of w^2 (float64) for the error bound.
 // ---------------------------------------------------------------------------
 constexpr int kScreenSplit = 4;
+constexpr int kScrRow = 144;                   // LDS bytes per row of one group: 64 bf16 + pad
+constexpr int kScrBuf = 64 * kScrRow;          // one 64-row tile of one group
+constexpr int kScrSmem = 2 * 3 * kScrBuf;      // x, hi, lo; double buffered
 
-// LDS bytes of one k_route_exact wave: x row (bf16), candidate experts and
-// logits (E each), selected logits (16).
-__host__ __device__ constexpr int route_exact_wave_bytes(int H, int E) { return H * 2 + E * 8 + 64; }
+// LDS bytes of one k_route_exact workgroup: reduction slots, x row (bf16),
+// screened logits, candidate experts and logits (E each), selected logits (16).
+__host__ __device__ constexpr int route_exact_smem_bytes(int H, int E) { return 256 + H * 2 + E * 12 + 64; }
 
 __global__ __launch_bounds__(256) void k_screen(const uint16_t* __restrict__ x, int T, int H,
                                                 const float* __restrict__ wr, int E,
                                                 float* __restrict__ approx, double* __restrict__ wsq) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) uint8_t sm[kScrSmem];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, c32 = lane & 31;
-  const int t = blockIdx.x * 64 + wm * 32 + c32;
-  const int e = blockIdx.y * 64 + wn * 32 + c32;
-  const bool tv = t < T, ev = e < E;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   const int G = H / kGroup;
   const int gs = blockIdx.z, g0 = G * gs / kScreenSplit, g1 = G * (gs + 1) / kScreenSplit;
-  const uint16_t* xr = x + (int64_t)(tv ? t : 0) * H + h * 32;
-  const float* wrow = wr + (int64_t)(ev ? e : 0) * H + h * 32;
-  const bool norms = blockIdx.x == 0 && wm == 0;
-  f32x16_t acc = {};
-  double ss = 0.0;
-  uint4 a[2][4];
-  float4 w[2][8];
-  auto load = [&](int g, int s) {
-    const int gg = g < g1 ? g : (g1 > 0 ? g1 - 1 : 0);  // empty slices read group 0 and add nothing
-#pragma unroll
-    for (int c = 0; c < 4; c++) a[s][c] = *reinterpret_cast<const uint4*>(xr + gg * kGroup + c * 8);
-#pragma unroll
-    for (int q = 0; q < 8; q++) w[s][q] = *reinterpret_cast<const float4*>(wrow + gg * kGroup + q * 4);
+  const bool norms = blockIdx.x == 0;
+
+  // Staging: x pieces (row tid/8 and tid/8 + 32, 16-byte part tid%8); weight
+  // float4s (rows tid/16 + 16 i, i < 4, part tid%16).  Rows past T or E
+  // reload a valid row whose results are never stored.
+  const int xp = tid & 7, xr0 = tid >> 3;
+  const uint16_t* xs0 = x + (int64_t)min(t0 + xr0, T - 1) * H + xp * 8;
+  const uint16_t* xs1 = x + (int64_t)min(t0 + xr0 + 32, T - 1) * H + xp * 8;
+  const int wp = tid & 15, wr0 = tid >> 4;
+  const float* ws0 = wr + (int64_t)min(e0 + wr0, E - 1) * H + wp * 4;
+  const float* ws1 = wr + (int64_t)min(e0 + wr0 + 16, E - 1) * H + wp * 4;
+  const float* ws2 = wr + (int64_t)min(e0 + wr0 + 32, E - 1) * H + wp * 4;
+  const float* ws3 = wr + (int64_t)min(e0 + wr0 + 48, E - 1) * H + wp * 4;
+  double ss0 = 0.0, ss1 = 0.0, ss2 = 0.0, ss3 = 0.0;
+
+  // One register set of staged data: x pieces X0, X1 and weight float4s W0..W3.
+#define MOE_SCR_LOAD(g, S)                                                        \
+  do {                                                                            \
+    const int gg_ = (g) < g1 ? (g) : g1 - 1;                                      \
+    S##x0 = *reinterpret_cast<const uint4*>(xs0 + gg_ * kGroup);                  \
+    S##x1 = *reinterpret_cast<const uint4*>(xs1 + gg_ * kGroup);                  \
+    S##w0 = *reinterpret_cast<const float4*>(ws0 + gg_ * kGroup);                 \
+    S##w1 = *reinterpret_cast<const float4*>(ws1 + gg_ * kGroup);                 \
+    S##w2 = *reinterpret_cast<const float4*>(ws2 + gg_ * kGroup);                 \
+    S##w3 = *reinterpret_cast<const float4*>(ws3 + gg_ * kGroup);                 \
+  } while (0)
+  auto stage_w = [&](const float4 w, int row, uint8_t* xb, double& ss) {
+    const __bf16 h0 = (__bf16)w.x, h1 = (__bf16)w.y, h2 = (__bf16)w.z, h3 = (__bf16)w.w;
+    const __bf16 l0 = (__bf16)(w.x - (float)h0), l1 = (__bf16)(w.y - (float)h1);
+    const __bf16 l2 = (__bf16)(w.z - (float)h2), l3 = (__bf16)(w.w - (float)h3);
+    const int off = row * kScrRow + wp * 8;
+    *reinterpret_cast<uint2*>(xb + kScrBuf + off) =
+        make_uint2(__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16),
+                   __builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16));
+    *reinterpret_cast<uint2*>(xb + 2 * kScrBuf + off) =
+        make_uint2(__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16),
+                   __builtin_bit_cast(uint16_t, l2) | ((uint32_t)__builtin_bit_cast(uint16_t, l3) << 16));
+    if (norms) {
+      ss = fma((double)w.x, (double)w.x, ss);
+      ss = fma((double)w.y, (double)w.y, ss);
+      ss = fma((double)w.z, (double)w.z, ss);
+      ss = fma((double)w.w, (double)w.w, ss);
+    }
   };
-  auto compute = [&](int s) {
+#define MOE_SCR_STAGE(S, buf)                                                     \
+  do {                                                                            \
+    uint8_t* xb_ = sm + (buf) * 3 * kScrBuf;                                      \
+    *reinterpret_cast<uint4*>(xb_ + xr0 * kScrRow + xp * 16) = S##x0;             \
+    *reinterpret_cast<uint4*>(xb_ + (xr0 + 32) * kScrRow + xp * 16) = S##x1;      \
+    stage_w(S##w0, wr0, xb_, ss0);                                                \
+    stage_w(S##w1, wr0 + 16, xb_, ss1);                                           \
+    stage_w(S##w2, wr0 + 32, xb_, ss2);                                           \
+    stage_w(S##w3, wr0 + 48, xb_, ss3);                                           \
+  } while (0)
+  f32x16_t acc = {};
+  // k-slot j of MFMA c for lane half h carries column 32h + 8c + j of the group (A and B alike).
+  const int aoff = (wm * 32 + c32) * kScrRow + h * 64, boff = (wn * 32 + c32) * kScrRow + h * 64;
+  auto compute = [&](int buf) {
+    const uint8_t* xb = sm + buf * 3 * kScrBuf;
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      const float4 p = w[s][2 * c], r = w[s][2 * c + 1];
-      bf16x8_t b = {(__bf16)p.x, (__bf16)p.y, (__bf16)p.z, (__bf16)p.w,
-                    (__bf16)r.x, (__bf16)r.y, (__bf16)r.z, (__bf16)r.w};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[s][c]), b, acc, 0, 0, 0);
-    }
-    if (norms) {
-#pragma unroll
-      for (int q = 0; q < 8; q++) {
-        ss = fma((double)w[s][q].x, (double)w[s][q].x, ss);
-        ss = fma((double)w[s][q].y, (double)w[s][q].y, ss);
-        ss = fma((double)w[s][q].z, (double)w[s][q].z, ss);
-        ss = fma((double)w[s][q].w, (double)w[s][q].w, ss);
-      }
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xb + aoff + c * 16);
+      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(xb + kScrBuf + boff + c * 16);
+      const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(xb + 2 * kScrBuf + boff + c * 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl, acc, 0, 0, 0);
     }
   };
-  load(g0, 0);
-  for (int g = g0; g < g1; g += 2) {
-    load(g + 1, 1);
-    compute(0);
-    if (g + 1 >= g1) break;
-    load(g + 2, 0);
-    compute(1);
+
+  const int n = g1 - g0;  // groups of this slice (may be 0 for tiny H)
+  if (n > 0) {
+    uint4 ax0, ax1, bx0, bx1;
+    float4 aw0, aw1, aw2, aw3, bw0, bw1, bw2, bw3;
+    MOE_SCR_LOAD(g0, a);
+    MOE_SCR_LOAD(g0 + 1, b);
+    MOE_SCR_STAGE(a, 0);
+    MOE_SCR_LOAD(g0 + 2, a);
+    __syncthreads();
+    for (int r = 0; r < n; r += 2) {
+      compute(0);
+      if (r + 1 < n) MOE_SCR_STAGE(b, 1);  // workgroup-uniform condition
+      MOE_SCR_LOAD(g0 + r + 3, b);
+      __syncthreads();
+      if (r + 1 >= n) break;
+      compute(1);
+      if (r + 2 < n) MOE_SCR_STAGE(a, 0);
+      MOE_SCR_LOAD(g0 + r + 4, a);
+      __syncthreads();
+    }
   }
+#undef MOE_SCR_LOAD
+#undef MOE_SCR_STAGE
+
   float* out = approx + (int64_t)gs * T * E;
-  if (ev) {
+  const int e = e0 + wn * 32 + c32;
+  if (e < E) {
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const int tok = blockIdx.x * 64 + wm * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+      const int tok = t0 + wm * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
       if (tok < T) out[(int64_t)tok * E + e] = acc[i];
     }
   }
   if (norms) {
-    ss += __shfl_xor(ss, 32);
-    if (h == 0 && ev) wsq[gs * E + e] = ss;
+    const double sv[4] = {ss0, ss1, ss2, ss3};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      double v = sv[i];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+      const int ee = e0 + wr0 + 16 * i;
+      if (wp == 0 && ee < E) wsq[gs * E + ee] = v;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Many tokens, step 2: one wave per token.  Bound B on the distance between a
-// screened logit a and the exact one l (float64 sum rounded to fp32, plus the
-// fp32 bias):
-//   B = (2^-8 + (H + 4) 2^-21) |x|_2 max_e |w_e|_2 + 2^-21 (2 max|a| + 1)
-// The first term covers the bf16 rounding of Wr (at most 2^-8 relative) and
-// the fp32 accumulation of H exact bf16 products and of the slices in any
-// order (at most (H + 3) 2^-24 relative to sum |x||w| <= |x|_2 |w_e|_2, taken
-// 8 times over); the second the roundings of the bias additions.  Every
-// expert of the exact top-k has a >= a_k - 2 B (a_k the k-th largest screened
-// logit), so those experts are recomputed in float64 (four at a time, 16
-// lanes each) and the exact top-k is taken among them by rank.  Also writes
-// the per-group activation sums and the fp16 activation copy of the grouped
-// GEMM.
+// Many tokens, step 2: one wave per token.  With S = sum_h x w (exact), the
+// screened logit a = fp32(sum over slices in float64 + bias) and the exact
+// logit l = fp32(fp32(S) + bias) differ by at most
+//   B = (2^-17 + 1056 2^-24 + 2^-23) |x|_2 max_e |w_e|_2 + 2^-22 (max|a| + 1),
+// taken with a 2^-10 relative margin:
+//  * |w - hi - lo| <= 2^-17 |w| (bf16 rounding of w, then of the exact rest);
+//  * each slice accumulates 2 x 512 exact products in fp32 (at most 1024
+//    roundings of 2^-24 relative to sum |x||w|, bounded by |x|_2 |w_e|_2);
+//  * the slices and the bias are summed in float64 (error negligible, covered
+//    by the rounding of the result to fp32, 2^-24 |a|);
+//  * the exact logit carries two fp32 roundings (2^-24 |S| and 2^-24 |l|).
+// Every expert of the exact top-k has a >= a_k - 2 B for any a_k not above
+// the k-th largest screened logit (here the k-th largest of the per-lane
+// maxima), so only those experts are recomputed in float64 (one per half
+// wave) and the exact top-k is taken among them by rank.
+// Also writes the per-group activation sums and the fp16 activation copy of
+// the grouped GEMM.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict__ x, int T, int H,
                                                      const float* __restrict__ wr,
@@ -255,123 +325,159 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
                                                      const double* __restrict__ wsq,
                                                      int32_t* __restrict__ ids, float* __restrict__ tw,
                                                      float* __restrict__ xsum, uint16_t* __restrict__ x16) {
-  // Per wave in LDS: x row, candidate experts and logits, selected logits.
+  // One workgroup per token.  LDS: reduction slots, x row, screened logits,
+  // candidate experts and their exact logits, selected logits.
   extern __shared__ __attribute__((aligned(16))) uint8_t rsm[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  const int wbytes = route_exact_wave_bytes(H, E);
-  uint16_t* xl = reinterpret_cast<uint16_t*>(rsm + wave * wbytes);
-  int* cand_e = reinterpret_cast<int*>(rsm + wave * wbytes + H * 2);
+  __shared__ int s_C;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  double* red = reinterpret_cast<double*>(rsm);                 // [4 waves][3]
+  uint16_t* xl = reinterpret_cast<uint16_t*>(rsm + 256);
+  float* av = reinterpret_cast<float*>(rsm + 256 + H * 2);
+  int* cand_e = reinterpret_cast<int*>(av + E);
   float* cand_v = reinterpret_cast<float*>(cand_e + E);
   float* sel_v = cand_v + E;
   const uint16_t* xr = x + (int64_t)t * H;
 
-  // x row -> LDS, per-group sums, fp16 copy, |x|_2^2 in float64.
-  double xx = 0.0;
-  for (int h0 = 0; h0 < H; h0 += 256) {
-    const int h = h0 + 4 * lane;
-    float s = 0.f;
-    if (h < H) {
-      const uint2 v = *reinterpret_cast<const uint2*>(xr + h);
-      *reinterpret_cast<uint2*>(xl + h) = v;
-      const uint32_t c01 = f32_to_f16_scaled(v.x & 0xFFFFu) | ((uint32_t)f32_to_f16_scaled(v.x >> 16) << 16);
-      const uint32_t c23 = f32_to_f16_scaled(v.y & 0xFFFFu) | ((uint32_t)f32_to_f16_scaled(v.y >> 16) << 16);
-      *reinterpret_cast<uint2*>(x16 + (int64_t)t * H + h) = make_uint2(c01, c23);
-      const float f0 = bf16_bits_to_f32(v.x & 0xFFFFu), f1 = bf16_bits_to_f32(v.x >> 16);
-      const float f2 = bf16_bits_to_f32(v.y & 0xFFFFu), f3 = bf16_bits_to_f32(v.y >> 16);
-      s = (f0 + f1) + (f2 + f3);
-      xx = fma((double)f0, (double)f0, xx);
-      xx = fma((double)f1, (double)f1, xx);
-      xx = fma((double)f2, (double)f2, xx);
-      xx = fma((double)f3, (double)f3, xx);
-    }
+  // ---- x row (LDS copy, fp16 copy, per-group sums, |x|^2) and the screened
+  // logits (slices and bias summed in float64, rounded once); all loads are
+  // independent of each other ----
+  constexpr int kMaxXIter = 4;  // H <= 8192
+  uint4 xv[kMaxXIter];
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off);
-    if ((lane & 15) == 0 && h < H) xsum[(int64_t)t * (H / kGroup) + h / kGroup] = s;
+  for (int i = 0; i < kMaxXIter; i++) {
+    const int h = 8 * tid + 2048 * i;
+    if (h < H) xv[i] = *reinterpret_cast<const uint4*>(xr + h);
   }
-  const double xnorm = sqrt(wave_sum_f64(xx)) * (1.0 + 1e-6);
-
-  // Screened logits: fixed-order sum of the slices, then the fp32 bias.
-  float a[kMaxEPerLane];
-  bool alive[kMaxEPerLane];
   float amax = 0.f;
   double w2max = 0.0;
+  for (int e = tid; e < E; e += 256) {
+    double vd = (double)approx[(int64_t)t * E + e];
+    double w2 = wsq[e];
 #pragma unroll
-  for (int j = 0; j < kMaxEPerLane; j++) {
-    const int e = lane + 64 * j;
-    alive[j] = e < E;
-    float v = 0.f;
-    if (alive[j]) {
-      v = approx[(int64_t)t * E + e];
-      double w2 = wsq[e];
-#pragma unroll
-      for (int s = 1; s < kScreenSplit; s++) {
-        v += approx[(int64_t)s * T * E + (int64_t)t * E + e];
-        w2 += wsq[s * E + e];
-      }
-      if (bias) v = v + bias[e];
-      amax = fmaxf(amax, fabsf(v));
-      w2max = fmax(w2max, w2);
+    for (int s = 1; s < kScreenSplit; s++) {
+      vd += (double)approx[(int64_t)s * T * E + (int64_t)t * E + e];
+      w2 += wsq[s * E + e];
     }
-    a[j] = v;
+    if (bias) vd += (double)bias[e];
+    const float v = (float)vd;
+    av[e] = v;
+    amax = fmaxf(amax, fabsf(v));
+    w2max = fmax(w2max, w2);
+  }
+  double xx = 0.0;
+#pragma unroll
+  for (int i = 0; i < kMaxXIter; i++) {
+    const int h = 8 * tid + 2048 * i;
+    if (h < H) {  // H is a multiple of 64: a group of 8 threads is all in or all out
+      const uint4 v = xv[i];
+      *reinterpret_cast<uint4*>(xl + h) = v;
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t c[4];
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        c[j] = f32_to_f16_scaled(w[j] & 0xFFFFu) | ((uint32_t)f32_to_f16_scaled(w[j] >> 16) << 16);
+        const float f0 = bf16_bits_to_f32(w[j] & 0xFFFFu), f1 = bf16_bits_to_f32(w[j] >> 16);
+        s += f0 + f1;
+        xx = fma((double)f0, (double)f0, xx);
+        xx = fma((double)f1, (double)f1, xx);
+      }
+      *reinterpret_cast<uint4*>(x16 + (int64_t)t * H + h) = make_uint4(c[0], c[1], c[2], c[3]);
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      if ((tid & 7) == 0) xsum[(int64_t)t * (H / kGroup) + h / kGroup] = s;
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
+    xx += __shfl_xor(xx, off);
     amax = fmaxf(amax, __shfl_xor(amax, off));
     w2max = fmax(w2max, __shfl_xor(w2max, off));
   }
-  // k-th largest screened logit.
-  float kv;
-  int ki;
-  {
-    bool al2[kMaxEPerLane];
-#pragma unroll
-    for (int j = 0; j < kMaxEPerLane; j++) al2[j] = alive[j];
-    wave_topk(a, al2, k, kv, ki);
+  if (lane == 0) {
+    red[3 * wave + 0] = xx;
+    red[3 * wave + 1] = (double)amax;
+    red[3 * wave + 2] = w2max;
   }
-  const float ak = __shfl(kv, k - 1);
-  const double c1 = 0.00390625 + 2.0 * (H + 4) * 1.1920928955078125e-07;
-  const double B = c1 * xnorm * (sqrt(w2max) * (1.0 + 1e-6)) + 2.384185791015625e-07 * (2.0 * amax + 1.0) * 2.0;
-  const double lo = (double)ak - 2.0 * B;
+  __syncthreads();
 
-  // Candidate list in increasing expert order.
-  int C = 0;
+  // ---- wave 0: k-th largest screened logit, error bound, candidate list ----
+  if (wave == 0) {
+    xx = red[0] + red[3] + red[6] + red[9];
+    const double amx = fmax(fmax(red[1], red[4]), fmax(red[7], red[10]));
+    const double w2m = fmax(fmax(red[2], red[5]), fmax(red[8], red[11]));
+    const double xnorm = sqrt(xx) * (1.0 + 1e-6);
+    float a[kMaxEPerLane];
+    bool alive[kMaxEPerLane];
+    float m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kMaxEPerLane; j++) {
-    const bool cand = alive[j] && (double)a[j] >= lo;
-    const uint64_t m = __ballot(cand);
-    if (cand) cand_e[C + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = lane + 64 * j;
-    C += __popcll(m);
+    for (int j = 0; j < kMaxEPerLane; j++) {
+      const int e = lane + 64 * j;
+      alive[j] = e < E;
+      a[j] = alive[j] ? av[e] : 0.f;
+      if (alive[j]) m = fmaxf(m, a[j]);
+    }
+    // Lower bound of the k-th largest screened logit: the k-th largest of the
+    // lanes' maxima (those are k distinct logits, all at least that large).
+    // Bitonic sort of the 64 lane maxima, descending.
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const float o = __shfl_xor(m, stride);
+        const bool desc = (lane & size) == 0 || size == 64;
+        const bool upper = (lane & stride) != 0;
+        m = (desc != upper) ? fmaxf(m, o) : fminf(m, o);
+      }
+    }
+    const float ak = __shfl(m, k - 1);
+    const double c1 = 7.62939453125e-06 + 1056.0 * 5.9604644775390625e-08 + 1.1920928955078125e-07;
+    const double B = (c1 * xnorm * (sqrt(w2m) * (1.0 + 1e-6)) + 2.384185791015625e-07 * (amx + 1.0)) *
+                     (1.0 + 0.0009765625);
+    const double lo = (double)ak - 2.0 * B;
+    // Candidate list in increasing expert order.
+    int C = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxEPerLane; j++) {
+      const bool cand = alive[j] && (double)a[j] >= lo;
+      const uint64_t m = __ballot(cand);
+      if (cand) cand_e[C + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = lane + 64 * j;
+      C += __popcll(m);
+    }
+    if (lane == 0) s_C = C;
   }
-  __builtin_amdgcn_wave_barrier();
+  __syncthreads();
 
-  // Exact float64 logits, four candidates at a time (16 lanes each).
-  const int q = lane >> 4, l16 = lane & 15;
-  for (int c0 = 0; c0 < C; c0 += 4) {
-    const int c = c0 + q;
-    const int e = c < C ? cand_e[c] : cand_e[c0];
+  // ---- exact float64 logits of the candidates, one per half-wave ----
+  const int C = s_C;
+  const int hw = tid >> 5, l32 = tid & 31;
+  for (int c = hw; c < C; c += 8) {
+    const int e = cand_e[c];
     const float* wrow = wr + (int64_t)e * H;
     double acc = 0.0;
-#pragma unroll 8
-    for (int h = 4 * l16; h < H; h += 64) {
+#pragma unroll 16
+    for (int h = 4 * l32; h < H; h += 128) {
       const float4 w4 = *reinterpret_cast<const float4*>(wrow + h);
-      const uint2 xv = *reinterpret_cast<const uint2*>(xl + h);
-      acc = fma((double)bf16_bits_to_f32(xv.x & 0xFFFFu), (double)w4.x, acc);
-      acc = fma((double)bf16_bits_to_f32(xv.x >> 16), (double)w4.y, acc);
-      acc = fma((double)bf16_bits_to_f32(xv.y & 0xFFFFu), (double)w4.z, acc);
-      acc = fma((double)bf16_bits_to_f32(xv.y >> 16), (double)w4.w, acc);
+      const uint2 xq = *reinterpret_cast<const uint2*>(xl + h);
+      acc = fma((double)bf16_bits_to_f32(xq.x & 0xFFFFu), (double)w4.x, acc);
+      acc = fma((double)bf16_bits_to_f32(xq.x >> 16), (double)w4.y, acc);
+      acc = fma((double)bf16_bits_to_f32(xq.y & 0xFFFFu), (double)w4.z, acc);
+      acc = fma((double)bf16_bits_to_f32(xq.y >> 16), (double)w4.w, acc);
     }
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
+    for (int off = 1; off < 32; off <<= 1) acc += __shfl_xor(acc, off);
     float lg = (float)acc;
     if (bias) lg = lg + bias[e];
-    if (l16 == 0 && c < C) cand_v[c] = lg;
+    if (l32 == 0) cand_v[c] = lg;
   }
-  __builtin_amdgcn_wave_barrier();
+  __syncthreads();
 
-  // Exact top-k by rank: candidate c ranks below every c' with a larger logit
-  // or an equal logit and a lower expert index.
+  // ---- wave 0: exact top-k by rank (a candidate ranks below every other
+  // with a larger logit, or an equal logit and a lower expert index), then
+  // the softmax over the selected logits ----
+  if (wave != 0) return;
   for (int c = lane; c < C; c += 64) {
     const float vc = cand_v[c];
     const int ec = cand_e[c];
@@ -602,16 +708,8 @@ hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr,
                                int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
                                float* xsum, uint16_t* x16, hipStream_t s) {
   if (T <= kSmallT) return hipSuccess;  // few tokens: k_topk_meta selects from the exact logits
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route_exact),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 4 * route_exact_wave_bytes(8192, 512));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const size_t smem = (size_t)4 * route_exact_wave_bytes(H, E);
-  k_route_exact<<<dim3((T + 3) / 4), dim3(256), smem, s>>>(x, T, H, wr, bias, E, k, logits, wsq, ids, tw, xsum,
-                                                            x16);
+  const size_t smem = (size_t)route_exact_smem_bytes(H, E);
+  k_route_exact<<<dim3(T), dim3(256), smem, s>>>(x, T, H, wr, bias, E, k, logits, wsq, ids, tw, xsum, x16);
   return hipGetLastError();
 }
 
