@@ -239,7 +239,8 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
   }));
   TRY(timed(2, s, "routing metadata", [&] {
     return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, o.counts, o.offsets,
-                       o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv, o.sched, s);
+                       o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv, o.sched,
+                       reinterpret_cast<int32_t*>(o.logits), s);  // the screened logits are dead by now
   }));
   return MOE_OK;
 }

@@ -31,7 +31,7 @@ hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr,
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
-                       int32_t* sched, hipStream_t s);
+                       int32_t* sched, int32_t* scratch, hipStream_t s);
 // T <= 8: top-k of exact logits and the metadata in one single-workgroup launch.
 hipError_t launch_topk_meta(const float* logits, int T, int E, int k, int32_t* ids, float* tw, int BM,
                             int with_shared, int32_t* counts, int32_t* offsets, int32_t* sorted,

@@ -504,15 +504,139 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 // Routing metadata for one chunk, one workgroup of 1024 threads (16 waves).
 // The flat assignment range [0, T*k) is cut into 16 contiguous segments, one
-// per wave.  Phase 1 counts per (wave, expert) with LDS atomics (order-free),
-// phase 2 scans the per-expert totals (counts -> offsets, tiles, active list)
-// and turns the per-wave counts into per-wave bases, phase 3 walks each
-// segment in order, 64 assignments at a time, and ranks equal experts inside
-// the wave with ballots on the expert id bits.  The scatter is therefore
-// stable in flat id without any global atomics.
+// per wave, walked 64 assignments (one chunk) at a time.  Inside a chunk the
+// lanes holding the same expert find each other with ballots on the expert id
+// bits; the lowest such lane (the leader) stands for the group.
+//  Phase 1: the leaders add their group sizes to per-(wave, expert) LDS
+//           counters.
+//  Phase 2: wave-level scans over the experts give counts, offsets, the
+//           active list and the tile counts; the per-wave counters become
+//           per-wave bases; tiles are written one per thread.
+//  Phase 3: per chunk, each leader takes its group's base with one LDS
+//           atomic add that returns the old counter (all chunks' atomics of a
+//           batch are issued in order before any result is used), and the
+//           lanes place their assignments at base + rank in the group.
+// The scatter is therefore stable in flat id without any global atomics.
 // ---------------------------------------------------------------------------
 constexpr int kMetaWaves = 16;
 constexpr int kMaxE = 512;
+constexpr int kMetaBatch = 8;   // chunks per wave whose ids are loaded together
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Lanes of this wave that are valid and hold the same expert e.
+__device__ __forceinline__ uint64_t match_mask(int e, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; b++) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(valid && bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+// Scans over the experts given each expert's assignment count (thread e < E
+// holds tot for expert e; every thread of the 1024-thread workgroup calls
+// this): counts, offsets, active list, tile map and execution schedule.
+// Returns thread e's offset (its expert's first sorted position).
+__device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_shared,
+                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                               int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+                               int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                               int32_t* __restrict__ sched) {
+  __shared__ int s_incl[5][kMaxE];         // inclusive scans: rows, tiles, active, full tiles, partial tiles
+  __shared__ int s_wtot[kMaxE / 64][5];    // per-wave totals of those scans
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  int nt = 0, act = 0, nfull = 0, npart = 0;
+  if (tid < E) {
+    nt = (tot + BM - 1) / BM;
+    act = tot > 0 ? 1 : 0;
+    nfull = tot / BM;
+    npart = nt - nfull;
+  }
+  const int nwe = (E + 63) / 64;  // waves that cover the experts
+  int sc[5] = {tot, nt, act, nfull, npart};
+  if (wave < nwe) {
+#pragma unroll
+    for (int q = 0; q < 5; q++) sc[q] = wave_incl_scan(sc[q]);
+    if (lane == 63) {
+#pragma unroll
+      for (int q = 0; q < 5; q++) s_wtot[wave][q] = sc[q];
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+#pragma unroll
+    for (int q = 0; q < 5; q++) {
+      int base = 0;
+      for (int w = 0; w < wave; w++) base += s_wtot[w][q];
+      s_incl[q][tid] = sc[q] + base;
+    }
+  }
+  __syncthreads();
+  const int routed_tiles = s_incl[1][E - 1];
+  const int full_total = s_incl[3][E - 1];
+  int my_off = 0;
+  if (tid < E) {
+    const int off_e = s_incl[0][tid] - tot;
+    my_off = off_e;
+    counts[tid] = tot;
+    offsets[tid] = off_e;
+    if (tid == E - 1) offsets[E] = s_incl[0][tid];
+    if (act) active[s_incl[2][tid] - 1] = tid;
+  }
+  // Routed tiles in (expert, row) order, one per thread; the schedule puts
+  // the shared expert's full tiles first, then the routed full tiles, the
+  // routed partial tiles and the shared expert's partial tile (longest first).
+  // Each slot holds (expert, first row, rows, first row in sorted order).
+  const int sfull = with_shared ? T / BM : 0;
+  for (int j = tid; j < routed_tiles; j += blockDim.x) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_incl[1][mid] > j) hi = mid;
+      else lo = mid + 1;
+    }
+    const int e = lo;
+    const int nt_e = s_incl[1][e] - (e ? s_incl[1][e - 1] : 0);
+    const int tot_e = s_incl[0][e] - (e ? s_incl[0][e - 1] : 0);
+    const int off_e = s_incl[0][e] - tot_e;
+    const int r = j - (s_incl[1][e] - nt_e);
+    const int rows = min(BM, tot_e - r * BM);
+    tiles[3 * j + 0] = e;
+    tiles[3 * j + 1] = r * BM;
+    tiles[3 * j + 2] = rows;
+    if (sched) {
+      const int nfull_e = tot_e / BM;
+      const int slot = r < nfull_e ? sfull + (s_incl[3][e] - nfull_e) + r : sfull + full_total + s_incl[4][e] - 1;
+      reinterpret_cast<int4*>(sched)[slot] = make_int4(e, r * BM, rows, off_e + r * BM);
+    }
+  }
+  const int nshared = with_shared ? (T + BM - 1) / BM : 0;
+  for (int r = tid; r < nshared; r += blockDim.x) {
+    tiles[3 * (routed_tiles + r) + 0] = E;
+    tiles[3 * (routed_tiles + r) + 1] = r * BM;
+    tiles[3 * (routed_tiles + r) + 2] = min(BM, T - r * BM);
+    if (sched)
+      reinterpret_cast<int4*>(sched)[r < sfull ? r : routed_tiles + nshared - 1] =
+          make_int4(E, r * BM, min(BM, T - r * BM), T * k + r * BM);
+  }
+  if (tid == 0) {
+    n_tiles[0] = routed_tiles + nshared;
+    n_active[0] = s_incl[2][E - 1];
+  }
+  __syncthreads();
+  return my_off;
+}
 
 __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, int BM, int with_shared,
                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -520,134 +644,88 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
                           int32_t* __restrict__ n_tiles, int32_t* __restrict__ active,
                           int32_t* __restrict__ n_active, int32_t* __restrict__ inv,
                           int32_t* __restrict__ sched) {
-  __shared__ int cnt[kMetaWaves * kMaxE];  // [wave][expert]
-  __shared__ int sc0[kMaxE], sc1[kMaxE], sc2[kMaxE], sc3[kMaxE], sc4[kMaxE];
-  __shared__ int s_full_total;
-  __shared__ int s_routed_tiles, s_nact;
+  __shared__ int cnt[kMetaWaves * kMaxE];  // [wave][expert]: counts, then bases
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int N = T * k;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   for (int i = tid; i < kMetaWaves * E; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
 
   const int S = (N + kMetaWaves - 1) / kMetaWaves;
   const int seg0 = min(N, wave * S), seg1 = min(N, seg0 + S);
-  for (int a = seg0 + lane; a < seg1; a += 64) atomicAdd(&cnt[wave * E + ids[a]], 1);
+  const int nch = (seg1 - seg0 + 63) / 64;
+
+  // ---- phase 1: per-(wave, expert) counts ----
+  for (int c0 = 0; c0 < nch; c0 += kMetaBatch) {
+    int ev[kMetaBatch];
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; i++) {
+      const int a = seg0 + 64 * (c0 + i) + lane;
+      ev[i] = (c0 + i < nch && a < seg1) ? ids[a] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; i++) {
+      if (c0 + i < nch) {  // wave-uniform
+        const bool valid = ev[i] >= 0;
+        const uint64_t m = match_mask(valid ? ev[i] : 0, valid, nbits);
+        if (valid && (m & lt_mask) == 0) atomicAdd(&cnt[wave * E + ev[i]], __popcll(m));
+      }
+    }
+  }
   __syncthreads();
 
-  int tot = 0, nt = 0, act = 0, nfull = 0, npart = 0;
-  if (tid < E) {
+  // ---- phase 2: scans over experts, tiles; per-wave counters -> bases ----
+  int tot = 0;
+  if (tid < E)
     for (int w = 0; w < kMetaWaves; w++) tot += cnt[w * E + tid];
-    nt = (tot + BM - 1) / BM;
-    act = tot > 0 ? 1 : 0;
-    nfull = tot / BM;
-    npart = nt - nfull;
-    sc0[tid] = tot;
-    sc1[tid] = nt;
-    sc2[tid] = act;
-    sc3[tid] = nfull;
-    sc4[tid] = npart;
-  }
-  __syncthreads();
-  for (int off = 1; off < E; off <<= 1) {
-    int a0 = 0, a1 = 0, a2 = 0, a3 = 0, a4 = 0;
-    if (tid < E && tid >= off) {
-      a0 = sc0[tid - off];
-      a1 = sc1[tid - off];
-      a2 = sc2[tid - off];
-      a3 = sc3[tid - off];
-      a4 = sc4[tid - off];
-    }
-    __syncthreads();
-    if (tid < E && tid >= off) {
-      sc0[tid] += a0;
-      sc1[tid] += a1;
-      sc2[tid] += a2;
-      sc3[tid] += a3;
-      sc4[tid] += a4;
-    }
-    __syncthreads();
-  }
-  if (tid == E - 1) s_full_total = sc3[tid];
-  __syncthreads();
-  // Execution order of the tiles for the grouped GEMMs (longest first): the
-  // shared expert's full tiles, the routed full tiles, the routed partial
-  // tiles, the shared expert's partial tile.
-  // Each slot holds the tile's descriptor (expert, first row, rows, first
-  // row in expert-sorted order).
-  const int sfull = with_shared ? T / BM : 0;
-  if (sched && tid < E) {
-    const int off_e = sc0[tid] - tot;
-    const int fpos = sfull + sc3[tid] - nfull;
-    for (int r = 0; r < nfull; r++)
-      reinterpret_cast<int4*>(sched)[fpos + r] = make_int4(tid, r * BM, BM, off_e + r * BM);
-    if (npart)
-      reinterpret_cast<int4*>(sched)[sfull + s_full_total + sc4[tid] - 1] =
-          make_int4(tid, nfull * BM, tot - nfull * BM, off_e + nfull * BM);
-  }
+  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, counts, offsets, tiles, n_tiles, active,
+                                    n_active, sched);
   if (tid < E) {
-    const int off_e = sc0[tid] - tot;
-    counts[tid] = tot;
-    offsets[tid] = off_e;
-    if (tid == E - 1) {
-      offsets[E] = sc0[tid];
-      s_routed_tiles = sc1[tid];
-      s_nact = sc2[tid];
-    }
     int run = off_e;
     for (int w = 0; w < kMetaWaves; w++) {
       const int c = cnt[w * E + tid];
       cnt[w * E + tid] = run;
       run += c;
     }
-    const int ts = sc1[tid] - nt;
-    for (int r = 0; r < nt; r++) {
-      tiles[3 * (ts + r) + 0] = tid;
-      tiles[3 * (ts + r) + 1] = r * BM;
-      tiles[3 * (ts + r) + 2] = min(BM, tot - r * BM);
-    }
-    if (act) active[sc2[tid] - 1] = tid;
   }
-  __syncthreads();
+  __syncthreads();  // cnt now holds the per-wave bases
 
-  const int rt = s_routed_tiles;
-  const int nshared = with_shared ? (T + BM - 1) / BM : 0;
-  for (int r = tid; r < nshared; r += blockDim.x) {
-    tiles[3 * (rt + r) + 0] = E;
-    tiles[3 * (rt + r) + 1] = r * BM;
-    tiles[3 * (rt + r) + 2] = min(BM, T - r * BM);
-    if (sched)
-      reinterpret_cast<int4*>(sched)[r < sfull ? r : rt + nshared - 1] =
-          make_int4(E, r * BM, min(BM, T - r * BM), T * k + r * BM);
-  }
-  if (tid == 0) {
-    n_tiles[0] = rt + nshared;
-    n_active[0] = s_nact;
-  }
-
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = seg0; base < seg1; base += 64) {
-    const int a = base + lane;
-    const bool valid = a < seg1;
-    const int e = valid ? ids[a] : 0;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < nbits; b++) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(valid && bit);
-      m &= bit ? bb : ~bb;
+  // ---- phase 3: stable scatter ----
+  for (int c0 = 0; c0 < nch; c0 += kMetaBatch) {
+    int ev[kMetaBatch], rk[kMetaBatch], ld[kMetaBatch], bs[kMetaBatch];
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; i++) {
+      const int a = seg0 + 64 * (c0 + i) + lane;
+      ev[i] = (c0 + i < nch && a < seg1) ? ids[a] : -1;
     }
-    int rank = 0, pos = 0;
-    if (valid) {
-      rank = __popcll(m & lt_mask);
-      pos = cnt[wave * E + e] + rank;
-      sorted[pos] = a;
-      if (inv) inv[a] = pos;
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; i++) {
+      rk[i] = 0;
+      ld[i] = 0;
+      bs[i] = 0;
+      if (c0 + i < nch) {  // wave-uniform
+        const bool valid = ev[i] >= 0;
+        const uint64_t m = match_mask(valid ? ev[i] : 0, valid, nbits);
+        rk[i] = __popcll(m & lt_mask);
+        ld[i] = m ? __ffsll((unsigned long long)m) - 1 : 0;
+        if (valid && rk[i] == 0) bs[i] = atomicAdd(&cnt[wave * E + ev[i]], __popcll(m));
+      }
     }
-    __builtin_amdgcn_wave_barrier();
-    if (valid && rank == 0) cnt[wave * E + e] += __popcll(m);
-    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; i++) {
+      if (c0 + i < nch) {
+        const int base = __shfl(bs[i], ld[i]);
+        if (ev[i] >= 0) {
+          const int a = seg0 + 64 * (c0 + i) + lane;
+          const int pos = base + rk[i];
+          sorted[pos] = a;
+          if (inv) inv[a] = pos;
+        }
+      }
+    }
   }
 }
 
@@ -658,6 +736,114 @@ __global__ __launch_bounds__(1024) void k_meta(const int32_t* __restrict__ ids, 
                                                int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                                int32_t* __restrict__ inv, int32_t* __restrict__ sched) {
   meta_body(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
+}
+
+// ---------------------------------------------------------------------------
+// Routing metadata for many tokens: the same computation spread over
+// workgroups.  The flat assignment range is cut into segments of
+// kSegAssign ids (one workgroup each, 4 waves x 4 chunks of 64).
+//  k_meta_count:   per-segment expert counts -> segcnt[seg][E];
+//  k_meta_scan:    one workgroup: totals, the scans and tiles of
+//                  meta_scan_tiles, and per-(segment, expert) bases
+//                  segbase[seg][e] = offset[e] + counts of e in earlier segments;
+//  k_meta_scatter: per segment, per-wave bases from the wave counts, then the
+//                  leader-based stable scatter of meta_body's phase 3.
+// ---------------------------------------------------------------------------
+constexpr int kSegAssign = 1024;
+constexpr int kSegWaves = 4;
+constexpr int kSegChunks = kSegAssign / (64 * kSegWaves);  // chunks per wave
+
+__global__ __launch_bounds__(256) void k_meta_count(const int32_t* __restrict__ ids, int N, int E,
+                                                    int32_t* __restrict__ segcnt) {
+  __shared__ int c[kMaxE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) c[e] = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * kSegAssign;
+  int ev[kSegAssign / 256];
+#pragma unroll
+  for (int i = 0; i < kSegAssign / 256; i++) {
+    const int a = a0 + tid + 256 * i;
+    ev[i] = a < N ? ids[a] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kSegAssign / 256; i++)
+    if (ev[i] >= 0) atomicAdd(&c[ev[i]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) segcnt[(int64_t)blockIdx.x * E + e] = c[e];
+}
+
+__global__ __launch_bounds__(1024) void k_meta_scan(int T, int k, int E, int BM, int with_shared, int nseg,
+                                                    const int32_t* __restrict__ segcnt,
+                                                    int32_t* __restrict__ segbase, int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
+                                                    int32_t* __restrict__ n_tiles, int32_t* __restrict__ active,
+                                                    int32_t* __restrict__ n_active, int32_t* __restrict__ sched) {
+  const int tid = threadIdx.x;
+  int tot = 0;
+  if (tid < E)
+    for (int g = 0; g < nseg; g++) tot += segcnt[(int64_t)g * E + tid];
+  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, counts, offsets, tiles, n_tiles, active,
+                                    n_active, sched);
+  if (tid < E) {
+    int run = off_e;
+    for (int g = 0; g < nseg; g++) {
+      segbase[(int64_t)g * E + tid] = run;
+      run += segcnt[(int64_t)g * E + tid];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_meta_scatter(const int32_t* __restrict__ ids, int N, int E,
+                                                      const int32_t* __restrict__ segbase,
+                                                      int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
+  __shared__ int wc[kSegWaves][kMaxE];  // per-wave counts, then per-wave bases
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i = tid; i < kSegWaves * E; i += 256) (&wc[0][0])[(i / E) * kMaxE + i % E] = 0;
+  const int a0 = blockIdx.x * kSegAssign + wave * (64 * kSegChunks);
+  int ev[kSegChunks];
+#pragma unroll
+  for (int i = 0; i < kSegChunks; i++) {
+    const int a = a0 + 64 * i + lane;
+    ev[i] = a < N ? ids[a] : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSegChunks; i++)
+    if (ev[i] >= 0) atomicAdd(&wc[wave][ev[i]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int run = segbase[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int w = 0; w < kSegWaves; w++) {
+      const int c = wc[w][e];
+      wc[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  int rk[kSegChunks], ld[kSegChunks], bs[kSegChunks];
+#pragma unroll
+  for (int i = 0; i < kSegChunks; i++) {
+    const bool valid = ev[i] >= 0;
+    const uint64_t m = match_mask(valid ? ev[i] : 0, valid, nbits);
+    rk[i] = __popcll(m & lt_mask);
+    ld[i] = m ? __ffsll((unsigned long long)m) - 1 : 0;
+    bs[i] = 0;
+    if (valid && rk[i] == 0) bs[i] = atomicAdd(&wc[wave][ev[i]], __popcll(m));
+  }
+#pragma unroll
+  for (int i = 0; i < kSegChunks; i++) {
+    const int base = __shfl(bs[i], ld[i]);
+    if (ev[i] >= 0) {
+      const int a = a0 + 64 * i + lane;
+      const int pos = base + rk[i];
+      sorted[pos] = a;
+      if (inv) inv[a] = pos;
+    }
+  }
 }
 
 // Few tokens: top-k of the exact logits (wave t for token t) and the routing
@@ -716,9 +902,20 @@ hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr,
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
-                       int32_t* sched, hipStream_t s) {
-  k_meta<<<dim3(1), dim3(1024), 0, s>>>(ids, T, k, E, BM, with_shared, counts, offsets, sorted,
-                                        tiles, n_tiles, active, n_active, inv, sched);
+                       int32_t* sched, int32_t* scratch, hipStream_t s) {
+  const int N = T * k;
+  const int nseg = (N + kSegAssign - 1) / kSegAssign;
+  if (nseg <= 1) {  // one segment: the single-workgroup version
+    k_meta<<<dim3(1), dim3(1024), 0, s>>>(ids, T, k, E, BM, with_shared, counts, offsets, sorted,
+                                          tiles, n_tiles, active, n_active, inv, sched);
+    return hipGetLastError();
+  }
+  int32_t* segcnt = scratch;
+  int32_t* segbase = scratch + (size_t)nseg * E;
+  k_meta_count<<<dim3(nseg), dim3(256), 0, s>>>(ids, N, E, segcnt);
+  k_meta_scan<<<dim3(1), dim3(1024), 0, s>>>(T, k, E, BM, with_shared, nseg, segcnt, segbase, counts, offsets,
+                                              tiles, n_tiles, active, n_active, sched);
+  k_meta_scatter<<<dim3(nseg), dim3(256), 0, s>>>(ids, N, E, segbase, sorted, inv);
   return hipGetLastError();
 }
 
