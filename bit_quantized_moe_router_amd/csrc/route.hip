@@ -16,74 +16,12 @@
 //    screened logit lies within twice a rigorous error bound of the k-th
 //    largest screened logit (k_route_exact).  Any expert of the exact top-k
 //    is inside that window, so the selection equals the all-float64 one.
-#include <climits>
-
 #include "launch.h"
 
 namespace moe {
 
 constexpr int kMaxEPerLane = 8;  // E <= 512
 constexpr int kSmallT = 8;
-
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  // Is (va, ia) ranked before (vb, ib)?  ib == INT_MAX marks "none".
-  if (ib == INT_MAX) return ia != INT_MAX;
-  if (ia == INT_MAX) return false;
-  return va > vb || (va == vb && ia < ib);
-}
-
-// Wave-wide top-k over per-lane candidate arrays (expert e = lane + 64 j).
-// Lane r < k ends with the r-th selected (value, expert).
-__device__ __forceinline__ void wave_topk(const float (&v)[kMaxEPerLane], bool (&alive)[kMaxEPerLane],
-                                          int k, float& myv, int& myi) {
-  const int lane = threadIdx.x & 63;
-  myv = 0.f;
-  myi = 0;
-  for (int r = 0; r < k; r++) {
-    float bv = 0.f;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int j = 0; j < kMaxEPerLane; j++) {
-      const int e = lane + 64 * j;
-      if (alive[j] && better(v[j], e, bv, bi)) {
-        bv = v[j];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (bi != INT_MAX && (bi & 63) == lane) {
-#pragma unroll
-      for (int j = 0; j < kMaxEPerLane; j++)
-        if (j == (bi >> 6)) alive[j] = false;
-    }
-    if (lane == r) {
-      myv = bv;
-      myi = bi;
-    }
-  }
-}
-
-// Softmax over the k selected logits held by lanes 0..k-1; writes ids and weights.
-__device__ __forceinline__ void write_topk(float myv, int myi, int k, int64_t t, int32_t* ids, float* tw) {
-  const int lane = threadIdx.x & 63;
-  const float vmax = __shfl(myv, 0);
-  const float ex = lane < k ? __expf(myv - vmax) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  if (lane < k) {
-    ids[t * k + lane] = myi;
-    tw[t * k + lane] = ex / sum;
-  }
-}
 
 // bf16 bits -> fp16 bits of value / 256 (exact whenever the result is normal).
 __device__ __forceinline__ uint16_t f32_to_f16_scaled(uint16_t b) {
@@ -638,13 +576,13 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
   return my_off;
 }
 
+// cnt: caller's LDS, kMetaWaves * E ints ([wave][expert]: counts, then bases).
 __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, int BM, int with_shared,
                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                           int32_t* __restrict__ sorted, int32_t* __restrict__ tiles,
                           int32_t* __restrict__ n_tiles, int32_t* __restrict__ active,
                           int32_t* __restrict__ n_active, int32_t* __restrict__ inv,
-                          int32_t* __restrict__ sched) {
-  __shared__ int cnt[kMetaWaves * kMaxE];  // [wave][expert]: counts, then bases
+                          int32_t* __restrict__ sched, int* __restrict__ cnt) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int N = T * k;
@@ -735,7 +673,9 @@ __global__ __launch_bounds__(1024) void k_meta(const int32_t* __restrict__ ids, 
                                                int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                                int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                                int32_t* __restrict__ inv, int32_t* __restrict__ sched) {
-  meta_body(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
+  __shared__ int cnt[kMetaWaves * kMaxE];
+  meta_body(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched,
+            cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -846,8 +786,123 @@ __global__ __launch_bounds__(256) void k_meta_scatter(const int32_t* __restrict_
   }
 }
 
+// Routing metadata for at most 128 assignments (T <= 8), computed by one
+// wave without workgroup barriers; same outputs and order as meta_body.
+// Lane l owns experts 8l .. 8l+7 for the scans.  lds: 2 * E ints.
+__device__ void meta_small(const int32_t* __restrict__ ids, int T, int k, int E, int BM, int with_shared,
+                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ sorted, int32_t* __restrict__ tiles,
+                           int32_t* __restrict__ n_tiles, int32_t* __restrict__ active,
+                           int32_t* __restrict__ n_active, int32_t* __restrict__ inv,
+                           int32_t* __restrict__ sched, int* __restrict__ lds) {
+  const int lane = threadIdx.x & 63;
+  const int N = T * k;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int* cnt = lds;      // [E] counts
+  int* run = lds + E;  // [E] next free sorted position
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __builtin_amdgcn_wave_barrier();
+  const int e0v = lane < N ? ids[lane] : 0;
+  const int e1v = lane + 64 < N ? ids[lane + 64] : 0;
+  uint64_t m0 = match_mask(e0v, lane < N, nbits), m1 = match_mask(e1v, lane + 64 < N, nbits);
+  if (lane < N && (m0 & lt_mask) == 0) atomicAdd(&cnt[e0v], __popcll(m0));
+  if (lane + 64 < N && (m1 & lt_mask) == 0) atomicAdd(&cnt[e1v], __popcll(m1));
+  __builtin_amdgcn_wave_barrier();
+
+  // Per lane: its 8 experts' counts, tiles, active flags, full / partial tiles.
+  int c[8], sum[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int e = 8 * lane + i;
+    c[i] = e < E ? cnt[e] : 0;
+    sum[0] += c[i];
+    sum[1] += (c[i] + BM - 1) / BM;
+    sum[2] += c[i] > 0 ? 1 : 0;
+    sum[3] += c[i] / BM;
+    sum[4] += (c[i] + BM - 1) / BM - c[i] / BM;
+  }
+  int excl[5], total[5];
+#pragma unroll
+  for (int q = 0; q < 5; q++) {
+    const int inc = wave_incl_scan(sum[q]);
+    excl[q] = inc - sum[q];
+    total[q] = __shfl(inc, 63);
+  }
+  const int routed_tiles = total[1], full_total = total[3];
+  const int sfull = with_shared ? T / BM : 0;
+  int off = excl[0], tl = excl[1], ac = excl[2], fu = excl[3], pa = excl[4];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int e = 8 * lane + i;
+    if (e < E) {
+      counts[e] = c[i];
+      offsets[e] = off;
+      run[e] = off;
+      if (c[i] > 0) active[ac++] = e;
+      const int nt = (c[i] + BM - 1) / BM, nf = c[i] / BM;
+      for (int r = 0; r < nt; r++) {
+        const int rows = min(BM, c[i] - r * BM);
+        tiles[3 * (tl + r) + 0] = e;
+        tiles[3 * (tl + r) + 1] = r * BM;
+        tiles[3 * (tl + r) + 2] = rows;
+        if (sched) {
+          const int slot = r < nf ? sfull + fu + r : sfull + full_total + pa;
+          reinterpret_cast<int4*>(sched)[slot] = make_int4(e, r * BM, rows, off + r * BM);
+        }
+      }
+      tl += nt;
+      fu += nf;
+      pa += nt - nf;
+      off += c[i];
+    }
+  }
+  if (lane == 63) offsets[E] = total[0];
+  const int nshared = with_shared ? (T + BM - 1) / BM : 0;
+  for (int r = lane; r < nshared; r += 64) {
+    tiles[3 * (routed_tiles + r) + 0] = E;
+    tiles[3 * (routed_tiles + r) + 1] = r * BM;
+    tiles[3 * (routed_tiles + r) + 2] = min(BM, T - r * BM);
+    if (sched)
+      reinterpret_cast<int4*>(sched)[r < sfull ? r : routed_tiles + nshared - 1] =
+          make_int4(E, r * BM, min(BM, T - r * BM), T * k + r * BM);
+  }
+  if (lane == 0) {
+    n_tiles[0] = routed_tiles + nshared;
+    n_active[0] = total[2];
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // Stable scatter: chunk 0, then chunk 1; each group's leader takes the base.
+  {
+    const int rk = __popcll(m0 & lt_mask), ld = m0 ? __ffsll((unsigned long long)m0) - 1 : 0;
+    int b = 0;
+    if (lane < N && rk == 0) b = atomicAdd(&run[e0v], __popcll(m0));
+    b = __shfl(b, ld);
+    if (lane < N) {
+      sorted[b + rk] = lane;
+      if (inv) inv[lane] = b + rk;
+    }
+  }
+  if (N > 64) {
+    const int rk = __popcll(m1 & lt_mask), ld = m1 ? __ffsll((unsigned long long)m1) - 1 : 0;
+    int b = 0;
+    if (lane + 64 < N && rk == 0) b = atomicAdd(&run[e1v], __popcll(m1));
+    b = __shfl(b, ld);
+    if (lane + 64 < N) {
+      sorted[b + rk] = lane + 64;
+      if (inv) inv[lane + 64] = b + rk;
+    }
+  }
+}
+
 // Few tokens: top-k of the exact logits (wave t for token t) and the routing
-// metadata in one workgroup, so decode spends one launch on both.
+// metadata in one workgroup, so decode spends one launch on both.  The top-k
+// takes the k-th largest of the lanes' maxima as a threshold (at most the
+// k-th largest logit), lists the logits at or above it and ranks that short
+// list exactly (larger logit first, equal logits towards the lower expert).
+constexpr int kTopkLds = kSmallT * (2 * kMaxE + 16);  // per-token lists, then the metadata counters
+
 __global__ __launch_bounds__(1024) void k_topk_meta(const float* __restrict__ logits, int T, int E, int k,
                                                     int32_t* __restrict__ ids, float* __restrict__ tw,
                                                     int BM, int with_shared, int32_t* __restrict__ counts,
@@ -855,24 +910,73 @@ __global__ __launch_bounds__(1024) void k_topk_meta(const float* __restrict__ lo
                                                     int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                                     int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                                     int32_t* __restrict__ inv, int32_t* __restrict__ sched) {
+  __shared__ int lds[kTopkLds];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (wave < T) {
+    // Per token: candidate experts (E), their logits (E), selected logits (16).
+    int* cand_e = lds + wave * (2 * E + 16);
+    float* cand_v = reinterpret_cast<float*>(cand_e + E);
+    float* sel_v = cand_v + E;
     const float* l = logits + (int64_t)wave * E;
     float v[kMaxEPerLane];
-    bool alive[kMaxEPerLane];
+    float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kMaxEPerLane; j++) {
       const int e = lane + 64 * j;
-      alive[j] = e < E;
-      v[j] = alive[j] ? l[e] : 0.f;
+      v[j] = e < E ? l[e] : -INFINITY;
+      m = fmaxf(m, v[j]);
     }
-    float myv;
-    int myi;
-    wave_topk(v, alive, k, myv, myi);
-    write_topk(myv, myi, k, wave, ids, tw);
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const float o = __shfl_xor(m, stride);
+        const bool desc = (lane & size) == 0 || size == 64;
+        const bool upper = (lane & stride) != 0;
+        m = (desc != upper) ? fmaxf(m, o) : fminf(m, o);
+      }
+    }
+    const float thr = __shfl(m, k - 1);
+    int C = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxEPerLane; j++) {
+      const int e = lane + 64 * j;
+      const bool cand = e < E && v[j] >= thr;
+      const uint64_t mk = __ballot(cand);
+      if (cand) {
+        const int c = C + __popcll(mk & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        cand_e[c] = e;
+        cand_v[c] = v[j];
+      }
+      C += __popcll(mk);
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int c = lane; c < C; c += 64) {
+      const float vc = cand_v[c];
+      const int ec = cand_e[c];
+      int rank = 0;
+      for (int c2 = 0; c2 < C; c2++) {
+        const float v2 = cand_v[c2];
+        rank += (v2 > vc || (v2 == vc && cand_e[c2] < ec)) ? 1 : 0;
+      }
+      if (rank < k) {
+        ids[(int64_t)wave * k + rank] = ec;
+        sel_v[rank] = vc;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const float myv = lane < k ? sel_v[lane] : 0.f;
+    const float vmax = __shfl(myv, 0);
+    const float ex = lane < k ? __expf(myv - vmax) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane < k) tw[(int64_t)wave * k + lane] = ex / sum;
   }
-  __syncthreads();
-  meta_body(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
+  __syncthreads();  // ids visible to the workgroup; the lists' LDS is free again
+  if (wave == 0)
+    meta_small(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv,
+               sched, lds);
 }
 
 // ---------------------------------------------------------------------------
