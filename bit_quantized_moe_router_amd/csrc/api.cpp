@@ -164,8 +164,11 @@ hipEvent_t get_event() {
     g_event_pool.pop_back();
     return e;
   }
+  // No system-scope fence on record: the profiling events must not flush the
+  // caches between the kernels they time (device-scope ordering suffices
+  // for timestamps read back with hipEventSynchronize).
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

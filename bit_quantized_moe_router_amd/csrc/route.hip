@@ -22,6 +22,7 @@ namespace moe {
 
 constexpr int kMaxEPerLane = 8;  // E <= 512
 constexpr int kSmallT = 8;
+constexpr int kMaxTileRows = 128;
 
 // bf16 bits -> fp16 bits of value / 256 (exact whenever the result is normal).
 __device__ __forceinline__ uint16_t f32_to_f16_scaled(uint16_t b) {
@@ -492,8 +493,10 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
                                int32_t* __restrict__ sched) {
   __shared__ int s_incl[5][kMaxE];         // inclusive scans: rows, tiles, active, full tiles, partial tiles
   __shared__ int s_wtot[kMaxE / 64][5];    // per-wave totals of those scans
+  __shared__ int s_pbin[kMaxTileRows + 1]; // partial tiles per row count, then their first slots
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i <= BM; i += blockDim.x) s_pbin[i] = 0;
   int nt = 0, act = 0, nfull = 0, npart = 0;
   if (tid < E) {
     nt = (tot + BM - 1) / BM;
@@ -532,11 +535,25 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     if (tid == E - 1) offsets[E] = s_incl[0][tid];
     if (act) active[s_incl[2][tid] - 1] = tid;
   }
-  // Routed tiles in (expert, row) order, one per thread; the schedule puts
-  // the shared expert's full tiles first, then the routed full tiles, the
-  // routed partial tiles and the shared expert's partial tile (longest first).
-  // Each slot holds (expert, first row, rows, first row in sorted order).
+  // Schedule: the shared expert's full tiles, the routed full tiles, then
+  // every partial tile (the shared expert's last one included) by row count,
+  // largest first, so that the longest work starts first.  Each slot holds
+  // (expert, first row, rows, first row in sorted order).  The order among
+  // partial tiles of equal size is arbitrary; it changes no result.
   const int sfull = with_shared ? T / BM : 0;
+  const int spart = with_shared && T % BM ? T % BM : 0;  // rows of the shared expert's partial tile
+  if (tid < E && npart) atomicAdd(&s_pbin[tot % BM], 1);
+  if (tid == 0 && spart) atomicAdd(&s_pbin[spart], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int run = sfull + full_total;
+    for (int r = BM - 1; r >= 1; r--) {
+      const int c = s_pbin[r];
+      s_pbin[r] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
   for (int j = tid; j < routed_tiles; j += blockDim.x) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
@@ -555,7 +572,7 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     tiles[3 * j + 2] = rows;
     if (sched) {
       const int nfull_e = tot_e / BM;
-      const int slot = r < nfull_e ? sfull + (s_incl[3][e] - nfull_e) + r : sfull + full_total + s_incl[4][e] - 1;
+      const int slot = r < nfull_e ? sfull + (s_incl[3][e] - nfull_e) + r : atomicAdd(&s_pbin[rows], 1);
       reinterpret_cast<int4*>(sched)[slot] = make_int4(e, r * BM, rows, off_e + r * BM);
     }
   }
@@ -565,7 +582,7 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     tiles[3 * (routed_tiles + r) + 1] = r * BM;
     tiles[3 * (routed_tiles + r) + 2] = min(BM, T - r * BM);
     if (sched)
-      reinterpret_cast<int4*>(sched)[r < sfull ? r : routed_tiles + nshared - 1] =
+      reinterpret_cast<int4*>(sched)[r < sfull ? r : atomicAdd(&s_pbin[spart], 1)] =
           make_int4(E, r * BM, min(BM, T - r * BM), T * k + r * BM);
   }
   if (tid == 0) {
