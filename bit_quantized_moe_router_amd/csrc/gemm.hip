@@ -54,7 +54,7 @@ constexpr int kTileRows = 128;                 // largest tile the kernel takes
 constexpr int kWaves = 8;
 constexpr int kARow = 144;                     // bytes per A row in LDS: 64 fp16 + 16 B pad
 constexpr int kABufBytes = kTileRows * kARow;  // one K group of A rows
-constexpr int kSmemMain = 4 * kABufBytes + kTileRows * 4;  // 2 buffers x 2 groups, + token per row
+constexpr int kSmemMain = 2 * kABufBytes + kTileRows * 4;  // + token per row
 constexpr int kGateUpColsPerWg = kWaves * 32;  // intermediate columns per workgroup
 constexpr int kDownColsPerWg = kWaves * 64;    // output columns per workgroup
 constexpr int kEpiRowGateUp = kGateUpColsPerWg * 2 + 16;  // LDS bytes per output row (fp16 + pad)
@@ -111,8 +111,8 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  uint8_t* at = smem;  // A: [2 buffers][2 groups][128 rows][kARow B]
-  int* tok = reinterpret_cast<int*>(smem + 4 * kABufBytes);
+  uint8_t* at = smem;  // A: [2][128 rows][kARow B]
+  int* tok = reinterpret_cast<int*>(smem + 2 * kABufBytes);
 
   // ---- the wave's 2 weight blocks: base of group 0 and stride per group ----
   // gate/up: block nb = 8 ct + wave of gate (b = 0) and of up (b = 1);
@@ -165,25 +165,18 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
     asrc1 = rowptr(arow0 + 64);
   }
   uint8_t* const adst = at + apart * 16 + arow0 * kARow;
-  // A of two consecutive groups g, g+1 moves as one unit (one register set:
-  // S0/S1 for g, S2/S3 for g+1); rows of fragments the tile does not use are
-  // not staged.
-#define MOE_LOAD_A2(g, S)                                                       \
-  do {                                                                          \
-    const int ga_ = (g) < G ? (g) : G - 1; /* past the end: a valid, unused group */ \
-    const int gb_ = (g) + 1 < G ? (g) + 1 : G - 1;                              \
-    S##0 = *reinterpret_cast<const uint4*>(asrc0 + ga_ * kGroup);              \
-    if (NF > 2) S##1 = *reinterpret_cast<const uint4*>(asrc1 + ga_ * kGroup);   \
-    S##2 = *reinterpret_cast<const uint4*>(asrc0 + gb_ * kGroup);              \
-    if (NF > 2) S##3 = *reinterpret_cast<const uint4*>(asrc1 + gb_ * kGroup);   \
+  // Rows of fragments the tile does not use are not staged.
+#define MOE_LOAD_A(g, S)                                                      \
+  do {                                                                        \
+    const int gg_ = (g) < G ? (g) : G - 1; /* past the end: a valid, unused group */ \
+    S##0 = *reinterpret_cast<const uint4*>(asrc0 + gg_ * kGroup);            \
+    if (NF > 2) S##1 = *reinterpret_cast<const uint4*>(asrc1 + gg_ * kGroup); \
   } while (0)
-#define MOE_STORE_A2(buf, S)                                                    \
-  do {                                                                          \
-    uint8_t* d_ = adst + (buf) * 2 * kABufBytes;                                \
-    *reinterpret_cast<uint4*>(d_) = S##0;                                       \
-    if (NF > 2) *reinterpret_cast<uint4*>(d_ + 64 * kARow) = S##1;              \
-    *reinterpret_cast<uint4*>(d_ + kABufBytes) = S##2;                          \
-    if (NF > 2) *reinterpret_cast<uint4*>(d_ + kABufBytes + 64 * kARow) = S##3; \
+#define MOE_STORE_A(buf, S)                                                   \
+  do {                                                                        \
+    uint8_t* d_ = adst + (buf) * kABufBytes;                                  \
+    *reinterpret_cast<uint4*>(d_) = S##0;                                     \
+    if (NF > 2) *reinterpret_cast<uint4*>(d_ + 64 * kARow) = S##1;            \
   } while (0)
 
   f32x16_t acc[NF][2];
@@ -246,33 +239,31 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
     }
   };
 
-  // Pipeline step of groups g, g+1 (g even; codes QA, QB; QN holds the
-  // codes of g+2; A in LDS buffer (g/2)%2): their MFMAs, A of g+2, g+3 into
-  // the other buffer, loads of A for g+4, g+5 and of the codes of g+4, g+5
-  // (into QA, QB, which are no longer needed).  One barrier per two groups.
-#define MOE_GEMM_STEP2(g, CUR, QA, QB, QN)                         \
-  do {                                                             \
-    if (wave_cols) {                                               \
-      compute(2 * (CUR), QA, QB, (g) < G, (g) + 1 < G);             \
-      compute(2 * (CUR) + 1, QB, QN, (g) + 1 < G, (g) + 2 < G);     \
-    }                                                              \
-    MOE_STORE_A2((CUR) ^ 1, as);                                   \
-    MOE_LOAD_A2((g) + 4, as);                                      \
-    load_q((g) + 4, QA);                                           \
-    load_q((g) + 5, QB);                                           \
-    __syncthreads();                                               \
+  // Pipeline step of group g: MFMAs of g (codes Q, A buffer g%2; QN holds
+  // the codes of g+1), A of g+1 into the other buffer, loads of A for g+3
+  // (register set AS) and of the codes of g+4 (into Q, which g no longer
+  // needs).
+#define MOE_GEMM_STEP(g, CUR, Q, QN, AS)                     \
+  do {                                                       \
+    if (wave_cols) compute(CUR, Q, QN, (g) < G, (g) + 1 < G);  \
+    MOE_STORE_A((CUR) ^ 1, AS);               \
+    MOE_LOAD_A((g) + 3, AS);                  \
+    load_q((g) + 4, Q);                       \
+    __syncthreads();                          \
   } while (0)
 
-  uint4 as0 = make_uint4(0, 0, 0, 0), as1 = as0, as2 = as0, as3 = as0;
-  // Prologue: the loads go out in the order of the steady state (A of a
-  // pair, then the codes of a pair) so that the loads in flight at the loop
-  // header line up with those at the back edge and the compiler's counts of
-  // loads to wait for are the steady-state ones.
-  MOE_LOAD_A2(0, as);
+  uint4 ae0 = make_uint4(0, 0, 0, 0), ae1 = ae0;
+  uint4 ao0 = ae0, ao1 = ae0;
+  // Prologue: the loads go out in the order of the steady state (A of j+3,
+  // then codes of j+4, for j = -3..-1) so that the loads in flight at the
+  // loop header line up with those at the back edge and the compiler's
+  // counts of loads to wait for are the steady-state ones.
+  MOE_LOAD_A(0, ae);
   load_q(1, q1);
-  MOE_STORE_A2(0, as);
-  MOE_LOAD_A2(2, as);
+  MOE_LOAD_A(1, ao);
   load_q(2, q2);
+  MOE_STORE_A(0, ae);
+  MOE_LOAD_A(2, ae);
   load_q(3, q3);
   if (wave_cols) {
     f16x2v_t s20, b20, s21, b21;
@@ -288,12 +279,14 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   // across the back edge instead of draining them at the loop header.
   const int Gp = (G + 3) & ~3;
   for (int g = 0; g < Gp; g += 4) {
-    MOE_GEMM_STEP2(g, 0, q0, q1, q2);
-    MOE_GEMM_STEP2(g + 2, 1, q2, q3, q0);
+    MOE_GEMM_STEP(g, 0, q0, q1, ao);
+    MOE_GEMM_STEP(g + 1, 1, q1, q2, ae);
+    MOE_GEMM_STEP(g + 2, 0, q2, q3, ao);
+    MOE_GEMM_STEP(g + 3, 1, q3, q0, ae);
   }
-#undef MOE_GEMM_STEP2
-#undef MOE_LOAD_A2
-#undef MOE_STORE_A2
+#undef MOE_GEMM_STEP
+#undef MOE_LOAD_A
+#undef MOE_STORE_A
 
   // ---- epilogue (the last step ended with a barrier: LDS is free) ----
   if (!kGateUp && T.shared) {
