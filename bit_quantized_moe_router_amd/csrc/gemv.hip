@@ -23,32 +23,42 @@ constexpr int kGuWaves = 8;    // gate/up workgroup: 8 waves split the H/64 grou
 constexpr int kGuPref = 4;     // groups per wave whose loads are issued together
 constexpr int kDnWaves = 16;   // down workgroup: 16 waves split the (expert, group) items
 constexpr int kDnPref = 4;
+constexpr int kMaxGroups = 128;              // H / 64 for H <= 8192
+constexpr int kMaxAssign = kGemvMaxRows * 16; // T * k on the GEMV path
+constexpr int kMaxSlots = kMaxAssign + 1;     // active experts + the shared expert
+constexpr int kDnStageMax = 120 * 1024;       // LDS for staged intermediate rows
 
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU.  grid = (expert slots: active experts, then the shared
 // expert; I/32 row blocks).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, ChunkArgs C) {
-  const int slot = blockIdx.x;
-  const int nact = *C.n_active;
-  const bool shared = slot == nact;
-  if (slot > nact || (shared && L.Is == 0)) return;
-  const int e = shared ? L.E : C.active[slot];
-  const int Iw = shared ? L.Is : L.I;
-  const int nb = blockIdx.y;
-  if (nb * 32 >= Iw) return;
-  const int rows = shared ? C.T : C.counts[e];
-  const int seg = shared ? 0 : C.offsets[e];
-  const int H = L.H, G = H / kGroup;
-  const uint8_t* wbase = expert_base(L, e) + (int64_t)nb * G * 2 * kBlockBytes;
-
-  extern __shared__ uint16_t xl[];  // [rows][H]
+  const int slot = blockIdx.x, nb = blockIdx.y;
+  const int T = C.T, H = L.H, G = H / kGroup;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, col = lane & 31;
+  extern __shared__ uint16_t xl[];  // [T][H]: every row of the chunk
+  __shared__ float xs[kGemvMaxRows * kMaxGroups];
   __shared__ int tok[kGemvMaxRows], orow[kGemvMaxRows];
   __shared__ float red[kGuWaves][kGemvMaxRows][2][32];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = lane >> 5, col = lane & 31;
 
-  // Issue this wave's first weight loads before anything else.
+  // Loads that do not depend on the routing go out first: the chunk's
+  // activation rows and their group sums (T <= 8 rows).  The slot's expert
+  // is read speculatively (clamped to a valid index) next to n_active.
+  const int H8 = H / 8;
+  for (int i = tid; i < T * H8; i += blockDim.x) reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(C.x)[i];
+  for (int i = tid; i < T * G; i += blockDim.x) xs[i] = C.xsum[i];
+  const int nact = *C.n_active;
+  const int e_spec = C.active[slot < L.E ? slot : L.E - 1];
+  const bool shared = slot == nact;
+  if (slot > nact || (shared && L.Is == 0)) return;  // workgroup-uniform, before any barrier
+  const int e = shared ? L.E : min(max(e_spec, 0), L.E - 1);
+  const int Iw = shared ? L.Is : L.I;
+  if (nb * 32 >= Iw) return;
+  const uint8_t* wbase = expert_base(L, e) + (int64_t)nb * G * 2 * kBlockBytes;
+
+  // This wave's first weight loads.
   uint4 cg[kGuPref], cu[kGuPref];
   uint32_t sbg[kGuPref], sbu[kGuPref];
   auto load = [&](int g0) {
@@ -66,16 +76,10 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
   };
   load(wave);
 
-  if (threadIdx.x < rows) {
-    const int r = threadIdx.x;
-    tok[r] = shared ? r : C.sorted[seg + r] / L.k;
-    orow[r] = shared ? C.Tk + r : seg + r;
-  }
-  __syncthreads();
-  const int H8 = H / 8;
-  for (int i = threadIdx.x; i < rows * H8; i += blockDim.x) {
-    const int r = i / H8, c = i - r * H8;
-    reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(C.x + (int64_t)tok[r] * H)[c];
+  const int rows = shared ? T : C.counts[e];
+  if (tid < rows) {
+    tok[tid] = shared ? tid : C.sorted[C.offsets[e] + tid] / L.k;
+    orow[tid] = shared ? C.Tk + tid : C.offsets[e] + tid;
   }
   __syncthreads();
 
@@ -103,7 +107,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
 #pragma unroll
       for (int j = 0; j < kGemvMaxRows; j++) {
         if (j < rows) {
-          const uint4* xp = reinterpret_cast<const uint4*>(xl + j * H + g * kGroup + h * 32);
+          const int t = tok[j];
+          const uint4* xp = reinterpret_cast<const uint4*>(xl + t * H + g * kGroup + h * 32);
           float dg = 0.f, du = 0.f;
 #pragma unroll
           for (int c = 0; c < 4; c++) {
@@ -116,9 +121,9 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
             }
           }
           // The group's activation sum covers both lane halves: fold it in once.
-          const float xs = h == 0 ? C.xsum[(int64_t)tok[j] * G + g] : 0.f;
-          accg[j] = fmaf(sg, dg, fmaf(bpg, xs, accg[j]));
-          accu[j] = fmaf(su, du, fmaf(bpu, xs, accu[j]));
+          const float xsv = h == 0 ? xs[t * G + g] : 0.f;
+          accg[j] = fmaf(sg, dg, fmaf(bpg, xsv, accg[j]));
+          accu[j] = fmaf(su, du, fmaf(bpu, xsv, accu[j]));
         }
       }
     }
@@ -162,59 +167,108 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
 // down + routing weight + shared add + combine.  grid = H/32 output row
 // blocks; the workgroup walks every (expert slot, group) item, waves taking
 // items round-robin with their loads issued in batches, and writes y for all
-// tokens of the chunk.
+// tokens of the chunk.  The routing tables (slot -> expert, segment, rows;
+// sorted position -> token, weight) and, when they fit, all intermediate rows
+// and their sums are staged in LDS first, so the item loop only waits for
+// the weight codes.  The first batch of codes is issued before the staging,
+// from a speculative read of the active list.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkArgs C) {
+__global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkArgs C, int staged) {
   const int nb = blockIdx.x;
-  const int nact = *C.n_active;
-  const int H = L.H, T = C.T;
+  const int H = L.H, T = C.T, Tk = C.Tk;
   const int hsw = C.Imax / 32;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
   const int Gi = L.I / kGroup, Gs = L.Is / kGroup;
-  const int nitems = nact * Gi + Gs;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];  // staged h rows, then their sums
+  __shared__ int s_e[kMaxSlots], s_seg[kMaxSlots], s_rows[kMaxSlots];
+  __shared__ int s_tok[kMaxAssign];
+  __shared__ float s_w[kMaxAssign];
   __shared__ float red[kDnWaves][kGemvMaxRows][32];
 
-  float acc[kGemvMaxRows];
-#pragma unroll
-  for (int t = 0; t < kGemvMaxRows; t++) acc[t] = 0.f;
+  const int nact = *C.n_active;
+  const int nspec = min(L.E, Tk);  // slots the active list can hold
+  // Item it -> (slot, group); the shared expert's items follow the routed ones.
+  auto item_expert = [&](int it, int na, int& g) -> int {
+    if (it < na * Gi) {
+      const int sl = it / Gi;
+      g = it - sl * Gi;
+      return min(max(C.active[min(sl, nspec - 1)], 0), L.E - 1);
+    }
+    g = it - na * Gi;
+    return L.E;
+  };
+  const int nitems = nact * Gi + Gs;
 
   uint4 cd[kDnPref];
   uint32_t sb[kDnPref];
   int pe[kDnPref], pg[kDnPref];
-  for (int it0 = wave; it0 < nitems; it0 += kDnPref * kDnWaves) {
+  auto load = [&](int it0) {
 #pragma unroll
     for (int p = 0; p < kDnPref; p++) {
       const int it = it0 + p * kDnWaves;
       pe[p] = -1;
       pg[p] = 0;
       if (it < nitems) {
-        int e, g;
-        if (it < nact * Gi) {
-          const int s = it / Gi;
-          e = C.active[s];
-          g = it - s * Gi;
-        } else {
-          e = L.E;
-          g = it - nact * Gi;
-        }
+        int g;
+        const int e = item_expert(it, nact, g);
         const bool sh = e == L.E;
         const int Gk = sh ? Gs : Gi;
         const uint8_t* blk = expert_base(L, e) + (sh ? L.shared_gateup_bytes : L.gateup_bytes) +
                              (int64_t)(nb * Gk + g) * kBlockBytes;
         cd[p] = *reinterpret_cast<const uint4*>(blk + lane * 16);
         sb[p] = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
-        pe[p] = e;
+        pe[p] = it < nact * Gi ? it / Gi : nact;  // slot
         pg[p] = g;
       }
     }
+  };
+  load(wave);
+
+  // ---- staging: routing tables, then (if staged) h rows and their sums ----
+  for (int a = tid; a < Tk; a += blockDim.x) {
+    const int as = C.sorted[a];
+    s_tok[a] = as / L.k;
+    s_w[a] = C.tw[as];
+  }
+  for (int sl = tid; sl <= nact; sl += blockDim.x) {
+    if (sl < nact) {
+      const int e = C.active[sl];
+      s_e[sl] = e;
+      s_seg[sl] = C.offsets[e];
+      s_rows[sl] = C.counts[e];
+    } else {
+      s_e[sl] = L.E;
+      s_seg[sl] = Tk;
+      s_rows[sl] = L.Is > 0 ? T : 0;
+    }
+  }
+  const int nrows = Tk + T;
+  uint16_t* hl = reinterpret_cast<uint16_t*>(dsm);
+  float* hsl = reinterpret_cast<float*>(dsm + (size_t)nrows * C.Imax * 2);
+  if (staged) {
+    const int n16 = nrows * C.Imax / 8;
+    for (int i = tid; i < n16; i += blockDim.x) reinterpret_cast<uint4*>(hl)[i] = reinterpret_cast<const uint4*>(C.hbuf)[i];
+    for (int i = tid; i < nrows * hsw; i += blockDim.x) hsl[i] = C.hsum[i];
+  }
+  __syncthreads();
+  const uint16_t* hb = staged ? hl : C.hbuf;
+  const float* hs = staged ? hsl : C.hsum;
+
+  float acc[kGemvMaxRows];
+#pragma unroll
+  for (int t = 0; t < kGemvMaxRows; t++) acc[t] = 0.f;
+
+  for (int it0 = wave; it0 < nitems; it0 += kDnPref * kDnWaves) {
+    if (it0 != wave) load(it0);
 #pragma unroll
     for (int p = 0; p < kDnPref; p++) {
       if (pe[p] < 0) break;
-      const int e = pe[p], g = pg[p];
-      const bool sh = e == L.E;
-      const int rows = sh ? T : C.counts[e];
-      const int seg = sh ? 0 : C.offsets[e];
+      const int sl = pe[p], g = pg[p];
+      const bool sh = sl == nact;
+      const int rows = s_rows[sl];
+      const int seg = s_seg[sl];
       uint32_t q[16];
       expand_codes(cd[p].x, q + 0);
       expand_codes(cd[p].y, q + 4);
@@ -222,18 +276,10 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkA
       expand_codes(cd[p].w, q + 12);
       const float s = bf16_bits_to_f32(sb[p] & 0xFFFFu), bp = bf16_bits_to_f32(sb[p] >> 16) - 128.f * s;
       for (int j = 0; j < rows; j++) {
-        const int64_t irow = sh ? C.Tk + j : seg + j;
-        int t;
-        float w;
-        if (sh) {
-          t = j;
-          w = 1.f;
-        } else {
-          const int a = C.sorted[seg + j];
-          t = a / L.k;
-          w = C.tw[a];
-        }
-        const uint4* hp = reinterpret_cast<const uint4*>(C.hbuf + irow * C.Imax + g * kGroup + h * 32);
+        const int irow = seg + j;
+        const int t = sh ? j : s_tok[irow];
+        const float w = sh ? 1.f : s_w[irow];
+        const uint4* hp = reinterpret_cast<const uint4*>(hb + (int64_t)irow * C.Imax + g * kGroup + h * 32);
         float d = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; c++) {
@@ -244,7 +290,7 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkA
           d = dot2_bf16(q[4 * c + 3], hv.w, d);
         }
         // hsum holds 32-column sums, so this lane half's own columns.
-        const float v = w * fmaf(s, d, bp * C.hsum[irow * hsw + 2 * g + h]);
+        const float v = w * fmaf(s, d, bp * hs[(int64_t)irow * hsw + 2 * g + h]);
 #pragma unroll
         for (int tt = 0; tt < kGemvMaxRows; tt++)
           if (tt == t) acc[tt] += v;
@@ -273,13 +319,30 @@ hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_
   const int Imax = L.I > L.Is ? L.I : L.Is;
   const int slots = (L.E < C.Tk ? L.E : C.Tk) + 1;
   dim3 grid(slots, Imax / 32);
+  static bool attr_set = false;
+  if (!attr_set) {  // activation rows: T * H * 2 <= 64 KB on this path, beside ~20 KB of static LDS
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_gateup),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   const size_t smem = (size_t)C.T * L.H * 2;
   k_gemv_gateup<<<grid, dim3(kGuWaves * 64), smem, s>>>(L, C);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s) {
-  k_gemv_down<<<dim3(L.H / 32), dim3(kDnWaves * 64), 0, s>>>(L, C);
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_down),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kDnStageMax);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const size_t rows = (size_t)C.Tk + C.T;
+  const size_t stage = rows * C.Imax * 2 + rows * (C.Imax / 32) * 4;
+  const int staged = stage <= (size_t)kDnStageMax ? 1 : 0;
+  k_gemv_down<<<dim3(L.H / 32), dim3(kDnWaves * 64), staged ? stage : 0, s>>>(L, C, staged);
   return hipGetLastError();
 }
 

@@ -17,22 +17,15 @@
 //    largest screened logit (k_route_exact).  Any expert of the exact top-k
 //    is inside that window, so the selection equals the all-float64 one.
 #include "launch.h"
+#include "small_route.h"
 
 namespace moe {
 
-constexpr int kMaxEPerLane = 8;  // E <= 512
-constexpr int kSmallT = 8;
 constexpr int kMaxTileRows = 128;
 
 // bf16 bits -> fp16 bits of value / 256 (exact whenever the result is normal).
 __device__ __forceinline__ uint16_t f32_to_f16_scaled(uint16_t b) {
   return __builtin_bit_cast(uint16_t, (_Float16)(bf16_bits_to_f32(b) * 0.00390625f));
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -46,51 +39,13 @@ __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict
                                                       float* __restrict__ logits,
                                                       float* __restrict__ xsum,
                                                       uint16_t* __restrict__ x16) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 4 + wave;
-  if (blockIdx.x == 0) {
-    const int G = H / kGroup;
-    for (int i = threadIdx.x; i < T * G; i += blockDim.x) {
-      const int t = i / G, g = i - t * G;
-      const uint16_t* p = x + (int64_t)t * H + g * kGroup;
-      float s = 0.f;
-      for (int j = 0; j < kGroup; j++) s += bf16_bits_to_f32(p[j]);
-      xsum[i] = s;
-    }
-  }
+  if (blockIdx.x == 0) group_sums(x, T, H, xsum, threadIdx.x, blockDim.x);
   if (blockIdx.x == (gridDim.x > 1 ? 1 : 0)) {
     for (int i = threadIdx.x; i < T * H; i += blockDim.x) x16[i] = f32_to_f16_scaled(x[i]);
   }
-  if (e >= E) return;
-  double acc[kSmallT];
-#pragma unroll
-  for (int t = 0; t < kSmallT; t++) acc[t] = 0.0;
-  const float* wrow = wr + (int64_t)e * H;
-  for (int h = 4 * lane; h < H; h += 256) {
-    const float4 w4 = *reinterpret_cast<const float4*>(wrow + h);
-#pragma unroll
-    for (int t = 0; t < kSmallT; t++) {
-      if (t < T) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + (int64_t)t * H + h);
-        acc[t] = fma((double)bf16_bits_to_f32(xv.x & 0xFFFFu), (double)w4.x, acc[t]);
-        acc[t] = fma((double)bf16_bits_to_f32(xv.x >> 16), (double)w4.y, acc[t]);
-        acc[t] = fma((double)bf16_bits_to_f32(xv.y & 0xFFFFu), (double)w4.z, acc[t]);
-        acc[t] = fma((double)bf16_bits_to_f32(xv.y >> 16), (double)w4.w, acc[t]);
-      }
-    }
-  }
-  const float b = bias ? bias[e] : 0.f;
-#pragma unroll
-  for (int t = 0; t < kSmallT; t++) {
-    if (t < T) {
-      const double s = wave_sum_f64(acc[t]);
-      if (lane == 0) {
-        float l = (float)s;
-        if (bias) l = l + b;
-        logits[(int64_t)t * E + e] = l;
-      }
-    }
-  }
+  if (e < E) logits_one_expert(x, T, H, wr, bias, E, e, logits);
 }
 
 // ---------------------------------------------------------------------------
@@ -458,29 +413,7 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
 // The scatter is therefore stable in flat id without any global atomics.
 // ---------------------------------------------------------------------------
 constexpr int kMetaWaves = 16;
-constexpr int kMaxE = 512;
 constexpr int kMetaBatch = 8;   // chunks per wave whose ids are loaded together
-
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
-
-// Lanes of this wave that are valid and hold the same expert e.
-__device__ __forceinline__ uint64_t match_mask(int e, bool valid, int nbits) {
-  uint64_t m = __ballot(valid);
-  for (int b = 0; b < nbits; b++) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t bb = __ballot(valid && bit);
-    m &= bit ? bb : ~bb;
-  }
-  return m;
-}
 
 // Scans over the experts given each expert's assignment count (thread e < E
 // holds tot for expert e; every thread of the 1024-thread workgroup calls
@@ -803,116 +736,6 @@ __global__ __launch_bounds__(256) void k_meta_scatter(const int32_t* __restrict_
   }
 }
 
-// Routing metadata for at most 128 assignments (T <= 8), computed by one
-// wave without workgroup barriers; same outputs and order as meta_body.
-// Lane l owns experts 8l .. 8l+7 for the scans.  lds: 2 * E ints.
-__device__ void meta_small(const int32_t* __restrict__ ids, int T, int k, int E, int BM, int with_shared,
-                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                           int32_t* __restrict__ sorted, int32_t* __restrict__ tiles,
-                           int32_t* __restrict__ n_tiles, int32_t* __restrict__ active,
-                           int32_t* __restrict__ n_active, int32_t* __restrict__ inv,
-                           int32_t* __restrict__ sched, int* __restrict__ lds) {
-  const int lane = threadIdx.x & 63;
-  const int N = T * k;
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int* cnt = lds;      // [E] counts
-  int* run = lds + E;  // [E] next free sorted position
-  for (int e = lane; e < E; e += 64) cnt[e] = 0;
-  __builtin_amdgcn_wave_barrier();
-  const int e0v = lane < N ? ids[lane] : 0;
-  const int e1v = lane + 64 < N ? ids[lane + 64] : 0;
-  uint64_t m0 = match_mask(e0v, lane < N, nbits), m1 = match_mask(e1v, lane + 64 < N, nbits);
-  if (lane < N && (m0 & lt_mask) == 0) atomicAdd(&cnt[e0v], __popcll(m0));
-  if (lane + 64 < N && (m1 & lt_mask) == 0) atomicAdd(&cnt[e1v], __popcll(m1));
-  __builtin_amdgcn_wave_barrier();
-
-  // Per lane: its 8 experts' counts, tiles, active flags, full / partial tiles.
-  int c[8], sum[5] = {0, 0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int e = 8 * lane + i;
-    c[i] = e < E ? cnt[e] : 0;
-    sum[0] += c[i];
-    sum[1] += (c[i] + BM - 1) / BM;
-    sum[2] += c[i] > 0 ? 1 : 0;
-    sum[3] += c[i] / BM;
-    sum[4] += (c[i] + BM - 1) / BM - c[i] / BM;
-  }
-  int excl[5], total[5];
-#pragma unroll
-  for (int q = 0; q < 5; q++) {
-    const int inc = wave_incl_scan(sum[q]);
-    excl[q] = inc - sum[q];
-    total[q] = __shfl(inc, 63);
-  }
-  const int routed_tiles = total[1], full_total = total[3];
-  const int sfull = with_shared ? T / BM : 0;
-  int off = excl[0], tl = excl[1], ac = excl[2], fu = excl[3], pa = excl[4];
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int e = 8 * lane + i;
-    if (e < E) {
-      counts[e] = c[i];
-      offsets[e] = off;
-      run[e] = off;
-      if (c[i] > 0) active[ac++] = e;
-      const int nt = (c[i] + BM - 1) / BM, nf = c[i] / BM;
-      for (int r = 0; r < nt; r++) {
-        const int rows = min(BM, c[i] - r * BM);
-        tiles[3 * (tl + r) + 0] = e;
-        tiles[3 * (tl + r) + 1] = r * BM;
-        tiles[3 * (tl + r) + 2] = rows;
-        if (sched) {
-          const int slot = r < nf ? sfull + fu + r : sfull + full_total + pa;
-          reinterpret_cast<int4*>(sched)[slot] = make_int4(e, r * BM, rows, off + r * BM);
-        }
-      }
-      tl += nt;
-      fu += nf;
-      pa += nt - nf;
-      off += c[i];
-    }
-  }
-  if (lane == 63) offsets[E] = total[0];
-  const int nshared = with_shared ? (T + BM - 1) / BM : 0;
-  for (int r = lane; r < nshared; r += 64) {
-    tiles[3 * (routed_tiles + r) + 0] = E;
-    tiles[3 * (routed_tiles + r) + 1] = r * BM;
-    tiles[3 * (routed_tiles + r) + 2] = min(BM, T - r * BM);
-    if (sched)
-      reinterpret_cast<int4*>(sched)[r < sfull ? r : routed_tiles + nshared - 1] =
-          make_int4(E, r * BM, min(BM, T - r * BM), T * k + r * BM);
-  }
-  if (lane == 0) {
-    n_tiles[0] = routed_tiles + nshared;
-    n_active[0] = total[2];
-  }
-  __builtin_amdgcn_wave_barrier();
-
-  // Stable scatter: chunk 0, then chunk 1; each group's leader takes the base.
-  {
-    const int rk = __popcll(m0 & lt_mask), ld = m0 ? __ffsll((unsigned long long)m0) - 1 : 0;
-    int b = 0;
-    if (lane < N && rk == 0) b = atomicAdd(&run[e0v], __popcll(m0));
-    b = __shfl(b, ld);
-    if (lane < N) {
-      sorted[b + rk] = lane;
-      if (inv) inv[lane] = b + rk;
-    }
-  }
-  if (N > 64) {
-    const int rk = __popcll(m1 & lt_mask), ld = m1 ? __ffsll((unsigned long long)m1) - 1 : 0;
-    int b = 0;
-    if (lane + 64 < N && rk == 0) b = atomicAdd(&run[e1v], __popcll(m1));
-    b = __shfl(b, ld);
-    if (lane + 64 < N) {
-      sorted[b + rk] = lane + 64;
-      if (inv) inv[lane + 64] = b + rk;
-    }
-  }
-}
-
 // Few tokens: top-k of the exact logits (wave t for token t) and the routing
 // metadata in one workgroup, so decode spends one launch on both.  The top-k
 // takes the k-th largest of the lanes' maxima as a threshold (at most the
@@ -929,67 +752,8 @@ __global__ __launch_bounds__(1024) void k_topk_meta(const float* __restrict__ lo
                                                     int32_t* __restrict__ inv, int32_t* __restrict__ sched) {
   __shared__ int lds[kTopkLds];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave < T) {
-    // Per token: candidate experts (E), their logits (E), selected logits (16).
-    int* cand_e = lds + wave * (2 * E + 16);
-    float* cand_v = reinterpret_cast<float*>(cand_e + E);
-    float* sel_v = cand_v + E;
-    const float* l = logits + (int64_t)wave * E;
-    float v[kMaxEPerLane];
-    float m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kMaxEPerLane; j++) {
-      const int e = lane + 64 * j;
-      v[j] = e < E ? l[e] : -INFINITY;
-      m = fmaxf(m, v[j]);
-    }
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const float o = __shfl_xor(m, stride);
-        const bool desc = (lane & size) == 0 || size == 64;
-        const bool upper = (lane & stride) != 0;
-        m = (desc != upper) ? fmaxf(m, o) : fminf(m, o);
-      }
-    }
-    const float thr = __shfl(m, k - 1);
-    int C = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxEPerLane; j++) {
-      const int e = lane + 64 * j;
-      const bool cand = e < E && v[j] >= thr;
-      const uint64_t mk = __ballot(cand);
-      if (cand) {
-        const int c = C + __popcll(mk & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-        cand_e[c] = e;
-        cand_v[c] = v[j];
-      }
-      C += __popcll(mk);
-    }
-    __builtin_amdgcn_wave_barrier();
-    for (int c = lane; c < C; c += 64) {
-      const float vc = cand_v[c];
-      const int ec = cand_e[c];
-      int rank = 0;
-      for (int c2 = 0; c2 < C; c2++) {
-        const float v2 = cand_v[c2];
-        rank += (v2 > vc || (v2 == vc && cand_e[c2] < ec)) ? 1 : 0;
-      }
-      if (rank < k) {
-        ids[(int64_t)wave * k + rank] = ec;
-        sel_v[rank] = vc;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    const float myv = lane < k ? sel_v[lane] : 0.f;
-    const float vmax = __shfl(myv, 0);
-    const float ex = lane < k ? __expf(myv - vmax) : 0.f;
-    float sum = ex;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-    if (lane < k) tw[(int64_t)wave * k + lane] = ex / sum;
-  }
+  if (wave < T)
+    topk_small(logits + (int64_t)wave * E, E, k, wave, ids, tw, lds + wave * (2 * E + 16));
   __syncthreads();  // ids visible to the workgroup; the lists' LDS is free again
   if (wave == 0)
     meta_small(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv,

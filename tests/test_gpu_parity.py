@@ -197,6 +197,34 @@ def test_smallrow_both_paths(M, T, gemv):
     check_close(y.cpu().numpy(), oracle_rows(case), f"smallrow T={T} gemv_max_rows={gemv}")
 
 
+EDGE_DECODE = [  # T, H, E, k, I, Is, seed, zipf
+    (5, 64, 4, 4, 64, 64, 61, None),      # k == E
+    (8, 192, 1, 1, 128, 0, 31, None),     # one expert, no shared expert
+    (7, 128, 8, 3, 64, 128, 21, 22),      # Is != I, zipf bias
+    (8, 320, 16, 8, 192, 64, 71, None),   # k == 8 of 16, odd group counts
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,I,Is,seed,zipf", EDGE_DECODE)
+def test_decode_gemv_edge_shapes(M, T, H, E, k, I, Is, seed, zipf):
+    """The GEMV path (forced for all T <= 8) on odd shapes; checks that it is the path that ran."""
+    from bit_quantized_moe_router_amd import (K_DOWN_GEMM, K_DOWN_GEMV, moe_profile_enable, moe_profile_read,
+                                              moe_profile_reset)
+    case = mi.small_layer(T, H, E, k, I, Is, seed, zipf)
+    lay = M.MoELayer(case["w"], k, max_tokens=T, gemv_max_rows=8)
+    moe_profile_reset()
+    moe_profile_enable((1 << K_DOWN_GEMV) | (1 << K_DOWN_GEMM))
+    try:
+        y = lay.forward_decode(dev(M, case["x"]), dev(M, case["bias"]))
+        torch.cuda.synchronize()
+        ran = (moe_profile_read(K_DOWN_GEMV)[1], moe_profile_read(K_DOWN_GEMM)[1])
+    finally:
+        moe_profile_enable(0)
+        moe_profile_reset()
+    assert ran == (1, 0), ran
+    check_close(y.cpu().numpy(), oracle_rows(case), f"edge {case['name']} GEMV decode")
+
+
 def _sample_tokens(case, n, seed):
     """Seeded sample that also holds tokens routed to the most loaded expert of each chunk."""
     rng = np.random.default_rng(seed)
