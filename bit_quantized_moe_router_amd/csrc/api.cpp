@@ -70,6 +70,14 @@ int64_t max_tiles_for(const moe_layer_desc* d, int64_t T) {
   return (tk + BM - 1) / BM + (E < tk ? E : tk) + (d->shared_inter > 0 ? (T + BM - 1) / BM : 0);
 }
 
+// Schedule entries: the tiles, plus one more for each tile of more than
+// BM/2 rows that the schedule may cut in two.
+int64_t max_sched_for(const moe_layer_desc* d, int64_t T) {
+  const int64_t mt = max_tiles_for(d, T), BM = tile_rows(d);
+  if (T <= 0 || BM < 64) return mt;
+  return mt + (T * d->top_k + (d->shared_inter > 0 ? T : 0)) / (BM / 2 + 1);
+}
+
 struct Blob {
   int64_t expert_bytes, gateup_bytes, shared_base, shared_gateup_bytes, total;
 };
@@ -109,7 +117,7 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   w.sorted = o; o += al(Tc * k * 4);
   w.inv = o; o += al(Tc * k * 4);
   w.tiles = o; o += al(max_tiles_for(d, Tc) * 3 * 4);
-  w.sched = o; o += al(max_tiles_for(d, Tc) * 16);  // int4 tile descriptor per slot
+  w.sched = o; o += al((1 + max_sched_for(d, Tc)) * 16);  // count, then an int4 descriptor per entry
   w.n_tiles = o; o += al(4);
   w.active = o; o += al(E * 4);
   w.n_active = o; o += al(4);
@@ -127,7 +135,8 @@ T* at(void* base, size_t off) {
 
 // ---- device check -------------------------------------------------------
 std::mutex g_dev_mu;
-int g_dev_ok[64];  // 0 = unknown, 1 = gfx950, -1 = other
+int g_dev_ok[64];   // 0 = unknown, 1 = gfx950, -1 = other
+int g_dev_cus[64];  // compute units
 
 moe_status check_device() {
   int dev = 0;
@@ -140,9 +149,19 @@ moe_status check_device() {
     e = hipGetDeviceProperties(&p, dev);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     g_dev_ok[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_dev_cus[dev] = p.multiProcessorCount;
   }
   if (g_dev_ok[dev] != 1) return fail(MOE_ERR_DEVICE_UNSUPPORTED, "device %d is not gfx950", dev);
   return MOE_OK;
+}
+
+// Long tiles the schedule keeps whole: one gate/up workgroup per compute unit
+// (after check_device on the current device).
+int max_long_tiles(const moe_layer_desc* d) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  return g_dev_cus[dev] / gateup_col_tiles(d->inter, d->shared_inter);
 }
 
 // ---- kernel timing (measurement mode) ----------------------------------------
@@ -241,8 +260,8 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
     return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.xsum, o.x16, s);
   }));
   TRY(timed(2, s, "routing metadata", [&] {
-    return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, o.counts, o.offsets,
-                       o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv, o.sched,
+    return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, max_long_tiles(d), o.counts,
+                       o.offsets, o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv, o.sched,
                        reinterpret_cast<int32_t*>(o.logits), s);  // the screened logits are dead by now
   }));
   return MOE_OK;
@@ -314,7 +333,7 @@ moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_
   const RouteOut o = ws_route(ws, w);
   TRY(run_route(d, x, Tc, wr, bias, o, s));
   const ChunkArgs C = chunk_args(d, x, Tc, o, ws, w, y);
-  const int mt = (int)max_tiles_for(d, Tc);
+  const int mt = (int)max_sched_for(d, Tc);
   TRY(timed(3, s, "gate/up GEMM", [&] { return launch_gateup_gemm(L, C, mt, s); }));
   TRY(timed(4, s, "down GEMM", [&] { return launch_down_gemm(L, C, mt, s); }));
   TRY(timed(7, s, "combine", [&] { return launch_combine(L, C, s); }));

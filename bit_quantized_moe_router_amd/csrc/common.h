@@ -68,8 +68,9 @@ struct ChunkArgs {
   const int32_t* inv;     // [T*k] inverse of sorted: position of assignment t*k+j
   const int32_t* tiles;   // [..][3]
   const int32_t* n_tiles; // [1]
-  const int32_t* sched;   // [n_tiles][4] tiles in execution order (longest first):
-                          // expert, first row, rows, first row in expert-sorted order
+  const int32_t* sched;   // [1 + n][4]: entry 0 = (n, 0, 0, 0), then n tiles (or pieces of
+                          // tiles) in execution order (longest first): expert, first row,
+                          // rows, first row in expert-sorted order
   const int32_t* active;  // [E] experts with rows, increasing
   const int32_t* n_active;// [1]
   uint16_t* hbuf;         // [T*k + T][Imax]: fp16(h / 256) on the GEMM path, bf16 h on the GEMV path

@@ -73,19 +73,27 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t m
 }
 
 // 8 codes of one packed dword -> 8 fp16 weights w = s*q + b in k order, as
-// four dwords of fp16 pairs.  Pair i of codes sits in nibbles i and 4+i, so
-// ((d >> 4i) & 0x000F000F) | 0x64006400 is the fp16 pair (1024 + q, 1024 + q')
-// (fp16 0x6400 = 1024 and its 10 mantissa bits step by 1); subtracting 1024 is
-// exact, and one packed fp16 FMA per pair rounds s*q + b once.
+// four dwords of fp16 pairs.  Pair i of codes sits in nibbles i and 4+i.  An
+// fp16 whose exponent is that of 1024 has a mantissa step of 1 in bits 0..3,
+// and one with the exponent of 64 has a step of 1 in bits 4..7, so
+//   (d & 0x000F000F) | 0x64006400 = (1024 + q0, 1024 + q4)
+//   (d & 0x00F000F0) | 0x54005400 = (  64 + q1,   64 + q5)
+// and the same on d >> 8 for pairs 2 and 3: one shift for 8 codes.  The
+// offset subtraction is exact, and one packed fp16 FMA per pair rounds s*q + b
+// once.
 __device__ __forceinline__ f16x8_t dequant8(uint32_t d, f16x2v_t s2, f16x2v_t b2) {
-  const f16x2v_t off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const f16x2v_t q = __builtin_bit_cast(f16x2v_t, and_or(d >> (4 * i), 0x000F000Fu, 0x64006400u)) + off;
-    w[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
-  }
-  return __builtin_bit_cast(f16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+  const f16x2v_t off_lo = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const f16x2v_t off_hi = {(_Float16)-64.0f, (_Float16)-64.0f};
+  const uint32_t d8 = d >> 8;
+  const f16x2v_t q0 = __builtin_bit_cast(f16x2v_t, and_or(d, 0x000F000Fu, 0x64006400u)) + off_lo;
+  const f16x2v_t q1 = __builtin_bit_cast(f16x2v_t, and_or(d, 0x00F000F0u, 0x54005400u)) + off_hi;
+  const f16x2v_t q2 = __builtin_bit_cast(f16x2v_t, and_or(d8, 0x000F000Fu, 0x64006400u)) + off_lo;
+  const f16x2v_t q3 = __builtin_bit_cast(f16x2v_t, and_or(d8, 0x00F000F0u, 0x54005400u)) + off_hi;
+  return __builtin_bit_cast(
+      f16x8_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q0, s2, b2)),
+                          __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q1, s2, b2)),
+                          __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q2, s2, b2)),
+                          __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q3, s2, b2))));
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
@@ -349,9 +357,10 @@ void k_expert_gemm(LayerArgs L, ChunkArgs C, int n_ct) {
   const int lin = blockIdx.x;
   const int xcd = lin & 7, m = lin >> 3;
   const int slot = (m / n_ct) * 8 + xcd, ct = m % n_ct;
-  // n_tiles and the slot's descriptor are read together (independent loads).
-  const int nt = *C.n_tiles;
-  const int4 d = reinterpret_cast<const int4*>(C.sched)[slot < nt ? slot : 0];
+  // The entry count and the slot's descriptor are read together (independent loads).
+  const int4* sc = reinterpret_cast<const int4*>(C.sched);
+  const int nt = sc[0].x;
+  const int4 d = sc[1 + (slot < nt ? slot : 0)];
   if (slot >= nt) return;
   Tile T;
   T.e = d.x;
@@ -413,8 +422,13 @@ __global__ __launch_bounds__(256) void k_combine(LayerArgs L, ChunkArgs C) {
 }
 
 // ---------------------------------------------------------------------------
+int gateup_col_tiles(int I, int Is) {
+  const int Imax = I > Is ? I : Is;
+  return (Imax + kGateUpColsPerWg - 1) / kGateUpColsPerWg;
+}
+
 template <bool kGateUp>
-static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s) {
+static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s) {
   constexpr int smem = kGateUp ? kSmemGateUp : kSmemDown;
   static bool attr_set = false;
   if (!attr_set) {
@@ -423,20 +437,18 @@ static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int Imax = L.I > L.Is ? L.I : L.Is;
-  const int n_ct = kGateUp ? (Imax + kGateUpColsPerWg - 1) / kGateUpColsPerWg
-                           : (L.H + kDownColsPerWg - 1) / kDownColsPerWg;
-  const int tiles8 = (max_tiles + 7) / 8 * 8;
+  const int n_ct = kGateUp ? gateup_col_tiles(L.I, L.Is) : (L.H + kDownColsPerWg - 1) / kDownColsPerWg;
+  const int tiles8 = (max_sched + 7) / 8 * 8;
   k_expert_gemm<kGateUp><<<dim3((unsigned)(tiles8 * n_ct)), dim3(kWaves * 64), smem, s>>>(L, C, n_ct);
   return hipGetLastError();
 }
 
-hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s) {
-  return launch_expert_gemm<true>(L, C, max_tiles, s);
+hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s) {
+  return launch_expert_gemm<true>(L, C, max_sched, s);
 }
 
-hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s) {
-  return launch_expert_gemm<false>(L, C, max_tiles, s);
+hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s) {
+  return launch_expert_gemm<false>(L, C, max_sched, s);
 }
 
 hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s) {

@@ -28,7 +28,9 @@ hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr,
 hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
                                float* xsum, uint16_t* x16, hipStream_t s);
-hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared,
+// max_long: tiles of more than BM/2 rows that the schedule keeps whole (the
+// rest are cut in two); 0 keeps every tile whole.
+hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared, int max_long,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
                        int32_t* sched, int32_t* scratch, hipStream_t s);
@@ -37,8 +39,11 @@ hipError_t launch_topk_meta(const float* logits, int T, int E, int k, int32_t* i
                             int with_shared, int32_t* counts, int32_t* offsets, int32_t* sorted,
                             int32_t* tiles, int32_t* n_tiles, int32_t* active, int32_t* n_active,
                             int32_t* inv, int32_t* sched, hipStream_t s);
-hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s);
-hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_tiles, hipStream_t s);
+// max_sched: upper bound of the schedule's entry count (sizes the grid).
+hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s);
+hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s);
+// Gate/up column tiles per row tile (the GEMM grid's second dimension).
+int gateup_col_tiles(int I, int Is);
 // y[t] += sum_j w_tj * routed output of assignment (t, j) (GEMM path).
 hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);
 hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);

@@ -419,17 +419,19 @@ constexpr int kMetaBatch = 8;   // chunks per wave whose ids are loaded together
 // holds tot for expert e; every thread of the 1024-thread workgroup calls
 // this): counts, offsets, active list, tile map and execution schedule.
 // Returns thread e's offset (its expert's first sorted position).
-__device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_shared,
+__device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_shared, int max_long,
                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                int32_t* __restrict__ sched) {
-  __shared__ int s_incl[5][kMaxE];         // inclusive scans: rows, tiles, active, full tiles, partial tiles
-  __shared__ int s_wtot[kMaxE / 64][5];    // per-wave totals of those scans
-  __shared__ int s_pbin[kMaxTileRows + 1]; // partial tiles per row count, then their first slots
+  __shared__ int s_incl[3][kMaxE];         // inclusive scans: rows, tiles, active
+  __shared__ int s_wtot[kMaxE / 64][3];    // per-wave totals of those scans
+  __shared__ int s_pbin[kMaxTileRows + 1]; // schedule entries per row count, then their next slots
+  __shared__ int s_keep[kMaxTileRows + 1]; // long tiles per row count that stay whole
+  __shared__ int s_extra[kMaxTileRows + 1];// pieces of cut tiles per row count
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i <= BM; i += blockDim.x) s_pbin[i] = 0;
+  for (int i = tid; i <= BM; i += blockDim.x) s_pbin[i] = s_keep[i] = s_extra[i] = 0;
   int nt = 0, act = 0, nfull = 0, npart = 0;
   if (tid < E) {
     nt = (tot + BM - 1) / BM;
@@ -438,19 +440,19 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     npart = nt - nfull;
   }
   const int nwe = (E + 63) / 64;  // waves that cover the experts
-  int sc[5] = {tot, nt, act, nfull, npart};
+  int sc[3] = {tot, nt, act};
   if (wave < nwe) {
 #pragma unroll
-    for (int q = 0; q < 5; q++) sc[q] = wave_incl_scan(sc[q]);
+    for (int q = 0; q < 3; q++) sc[q] = wave_incl_scan(sc[q]);
     if (lane == 63) {
 #pragma unroll
-      for (int q = 0; q < 5; q++) s_wtot[wave][q] = sc[q];
+      for (int q = 0; q < 3; q++) s_wtot[wave][q] = sc[q];
     }
   }
   __syncthreads();
   if (tid < E) {
 #pragma unroll
-    for (int q = 0; q < 5; q++) {
+    for (int q = 0; q < 3; q++) {
       int base = 0;
       for (int w = 0; w < wave; w++) base += s_wtot[w][q];
       s_incl[q][tid] = sc[q] + base;
@@ -458,7 +460,6 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
   }
   __syncthreads();
   const int routed_tiles = s_incl[1][E - 1];
-  const int full_total = s_incl[3][E - 1];
   int my_off = 0;
   if (tid < E) {
     const int off_e = s_incl[0][tid] - tot;
@@ -468,25 +469,72 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     if (tid == E - 1) offsets[E] = s_incl[0][tid];
     if (act) active[s_incl[2][tid] - 1] = tid;
   }
-  // Schedule: the shared expert's full tiles, the routed full tiles, then
-  // every partial tile (the shared expert's last one included) by row count,
-  // largest first, so that the longest work starts first.  Each slot holds
-  // (expert, first row, rows, first row in sorted order).  The order among
-  // partial tiles of equal size is arbitrary; it changes no result.
+  // Schedule (execution order of the GEMM workgroups): tiles by row count,
+  // largest first, so that the longest work starts first.  A tile of more
+  // than BM/2 rows is long; at most max_long of them stay whole (one round of
+  // the device's compute units), the others are cut into a BM/2-row piece and
+  // the rest, so that no long tile starts after the first round.  Each entry
+  // holds (expert, first row, rows, first row in sorted order); entry 0 holds
+  // the number of entries.  The order among pieces of equal size is
+  // arbitrary; it changes no result.
   const int sfull = with_shared ? T / BM : 0;
   const int spart = with_shared && T % BM ? T % BM : 0;  // rows of the shared expert's partial tile
+  const int half = (sched && max_long > 0 && BM >= 64) ? BM / 2 : 0;
+  if (tid < E && nfull) atomicAdd(&s_pbin[BM], nfull);
   if (tid < E && npart) atomicAdd(&s_pbin[tot % BM], 1);
+  if (tid == 0 && sfull) atomicAdd(&s_pbin[BM], sfull);
   if (tid == 0 && spart) atomicAdd(&s_pbin[spart], 1);
   __syncthreads();
-  if (tid == 0) {
-    int run = sfull + full_total;
-    for (int r = BM - 1; r >= 1; r--) {
-      const int c = s_pbin[r];
-      s_pbin[r] = run;
-      run += c;
+  if (wave == 0) {
+    // Wave 0 over the bins in decreasing row count: lane l has r = BM - l and
+    // BM - 64 - l (BM <= 128; r < 1 is no bin).  Long bins keep tiles up to
+    // max_long counted from the largest; the cut ones add a BM/2 piece and a
+    // rest piece.
+    const int ra = BM - lane, rb = BM - 64 - lane;
+    const int ca = ra >= 1 ? s_pbin[ra] : 0, cb = rb >= 1 ? s_pbin[rb] : 0;
+    int fa = ca, fb = cb;
+    if (half) {
+      const int la = ra > half ? ca : 0, lb = rb > half ? cb : 0;
+      const int ia = wave_incl_scan(la), ib = wave_incl_scan(lb);
+      const int ta = __shfl(ia, 63);
+      const int ka = ra > half ? min(ca, max(max_long - (ia - la), 0)) : 0;
+      const int kb = rb > half ? min(cb, max(max_long - (ta + ib - lb), 0)) : 0;
+      if (ra > half) {
+        s_keep[ra] = ka;
+        fa = ka;
+        if (ca > ka) atomicAdd(&s_extra[ra - half], ca - ka);
+      }
+      if (rb > half) {
+        s_keep[rb] = kb;
+        fb = kb;
+        if (cb > kb) atomicAdd(&s_extra[rb - half], cb - kb);
+      }
+      int cut = (ra > half ? ca - ka : 0) + (rb > half ? cb - kb : 0);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) cut += __shfl_xor(cut, off);
+      if (lane == 0) atomicAdd(&s_extra[half], cut);
+      __builtin_amdgcn_wave_barrier();
+      fa += ra >= 1 && ra <= half ? s_extra[ra] : 0;
+      fb += rb >= 1 && rb <= half ? s_extra[rb] : 0;
     }
+    // First entry of each bin: 1 + the entries of all larger bins.
+    const int ia = wave_incl_scan(fa), ib = wave_incl_scan(fb);
+    const int ta = __shfl(ia, 63), tb = __shfl(ib, 63);
+    if (ra >= 1) s_pbin[ra] = 1 + ia - fa;
+    if (rb >= 1) s_pbin[rb] = 1 + ta + ib - fb;
+    if (lane == 0 && sched) reinterpret_cast<int4*>(sched)[0] = make_int4(ta + tb, 0, 0, 0);
   }
   __syncthreads();
+  // One tile of e (rows at r0, sorted-order row rb) into the schedule.
+  auto place = [&](int e, int r0, int rows, int rb) {
+    int4* sc = reinterpret_cast<int4*>(sched);
+    if (half && rows > half && atomicSub(&s_keep[rows], 1) <= 0) {
+      sc[atomicAdd(&s_pbin[half], 1)] = make_int4(e, r0, half, rb);
+      sc[atomicAdd(&s_pbin[rows - half], 1)] = make_int4(e, r0 + half, rows - half, rb + half);
+    } else {
+      sc[atomicAdd(&s_pbin[rows], 1)] = make_int4(e, r0, rows, rb);
+    }
+  };
   for (int j = tid; j < routed_tiles; j += blockDim.x) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
@@ -503,20 +551,15 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     tiles[3 * j + 0] = e;
     tiles[3 * j + 1] = r * BM;
     tiles[3 * j + 2] = rows;
-    if (sched) {
-      const int nfull_e = tot_e / BM;
-      const int slot = r < nfull_e ? sfull + (s_incl[3][e] - nfull_e) + r : atomicAdd(&s_pbin[rows], 1);
-      reinterpret_cast<int4*>(sched)[slot] = make_int4(e, r * BM, rows, off_e + r * BM);
-    }
+    if (sched) place(e, r * BM, rows, off_e + r * BM);
   }
   const int nshared = with_shared ? (T + BM - 1) / BM : 0;
   for (int r = tid; r < nshared; r += blockDim.x) {
+    const int rows = min(BM, T - r * BM);
     tiles[3 * (routed_tiles + r) + 0] = E;
     tiles[3 * (routed_tiles + r) + 1] = r * BM;
-    tiles[3 * (routed_tiles + r) + 2] = min(BM, T - r * BM);
-    if (sched)
-      reinterpret_cast<int4*>(sched)[r < sfull ? r : atomicAdd(&s_pbin[spart], 1)] =
-          make_int4(E, r * BM, min(BM, T - r * BM), T * k + r * BM);
+    tiles[3 * (routed_tiles + r) + 2] = rows;
+    if (sched) place(E, r * BM, rows, T * k + r * BM);
   }
   if (tid == 0) {
     n_tiles[0] = routed_tiles + nshared;
@@ -527,7 +570,7 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
 }
 
 // cnt: caller's LDS, kMetaWaves * E ints ([wave][expert]: counts, then bases).
-__device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, int BM, int with_shared,
+__device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, int BM, int with_shared, int max_long,
                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                           int32_t* __restrict__ sorted, int32_t* __restrict__ tiles,
                           int32_t* __restrict__ n_tiles, int32_t* __restrict__ active,
@@ -569,7 +612,7 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
   int tot = 0;
   if (tid < E)
     for (int w = 0; w < kMetaWaves; w++) tot += cnt[w * E + tid];
-  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, counts, offsets, tiles, n_tiles, active,
+  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, counts, offsets, tiles, n_tiles, active,
                                     n_active, sched);
   if (tid < E) {
     int run = off_e;
@@ -618,14 +661,14 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
 }
 
 __global__ __launch_bounds__(1024) void k_meta(const int32_t* __restrict__ ids, int T, int k, int E,
-                                               int BM, int with_shared, int32_t* __restrict__ counts,
+                                               int BM, int with_shared, int max_long, int32_t* __restrict__ counts,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
                                                int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                                int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                                int32_t* __restrict__ inv, int32_t* __restrict__ sched) {
   __shared__ int cnt[kMetaWaves * kMaxE];
-  meta_body(ids, T, k, E, BM, with_shared, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched,
-            cnt);
+  meta_body(ids, T, k, E, BM, with_shared, max_long, counts, offsets, sorted, tiles, n_tiles, active, n_active, inv,
+            sched, cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -663,7 +706,8 @@ __global__ __launch_bounds__(256) void k_meta_count(const int32_t* __restrict__ 
   for (int e = tid; e < E; e += 256) segcnt[(int64_t)blockIdx.x * E + e] = c[e];
 }
 
-__global__ __launch_bounds__(1024) void k_meta_scan(int T, int k, int E, int BM, int with_shared, int nseg,
+__global__ __launch_bounds__(1024) void k_meta_scan(int T, int k, int E, int BM, int with_shared, int max_long,
+                                                    int nseg,
                                                     const int32_t* __restrict__ segcnt,
                                                     int32_t* __restrict__ segbase, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
@@ -673,7 +717,7 @@ __global__ __launch_bounds__(1024) void k_meta_scan(int T, int k, int E, int BM,
   int tot = 0;
   if (tid < E)
     for (int g = 0; g < nseg; g++) tot += segcnt[(int64_t)g * E + tid];
-  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, counts, offsets, tiles, n_tiles, active,
+  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, counts, offsets, tiles, n_tiles, active,
                                     n_active, sched);
   if (tid < E) {
     int run = off_e;
@@ -751,7 +795,7 @@ __global__ __launch_bounds__(1024) void k_topk_meta(const float* __restrict__ lo
                                                     int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                                     int32_t* __restrict__ inv, int32_t* __restrict__ sched) {
   __shared__ int lds[kTopkLds];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   if (wave < T)
     topk_small(logits + (int64_t)wave * E, E, k, wave, ids, tw, lds + wave * (2 * E + 16));
   __syncthreads();  // ids visible to the workgroup; the lists' LDS is free again
@@ -784,21 +828,21 @@ hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr,
   return hipGetLastError();
 }
 
-hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared,
+hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared, int max_long,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
                        int32_t* sched, int32_t* scratch, hipStream_t s) {
   const int N = T * k;
   const int nseg = (N + kSegAssign - 1) / kSegAssign;
   if (nseg <= 1) {  // one segment: the single-workgroup version
-    k_meta<<<dim3(1), dim3(1024), 0, s>>>(ids, T, k, E, BM, with_shared, counts, offsets, sorted,
+    k_meta<<<dim3(1), dim3(1024), 0, s>>>(ids, T, k, E, BM, with_shared, max_long, counts, offsets, sorted,
                                           tiles, n_tiles, active, n_active, inv, sched);
     return hipGetLastError();
   }
   int32_t* segcnt = scratch;
   int32_t* segbase = scratch + (size_t)nseg * E;
   k_meta_count<<<dim3(nseg), dim3(256), 0, s>>>(ids, N, E, segcnt);
-  k_meta_scan<<<dim3(1), dim3(1024), 0, s>>>(T, k, E, BM, with_shared, nseg, segcnt, segbase, counts, offsets,
+  k_meta_scan<<<dim3(1), dim3(1024), 0, s>>>(T, k, E, BM, with_shared, max_long, nseg, segcnt, segbase, counts, offsets,
                                               tiles, n_tiles, active, n_active, sched);
   k_meta_scatter<<<dim3(nseg), dim3(256), 0, s>>>(ids, N, E, segbase, sorted, inv);
   return hipGetLastError();

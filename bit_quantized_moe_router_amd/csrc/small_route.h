@@ -216,7 +216,7 @@ __device__ __forceinline__ void meta_small(const int32_t* __restrict__ ids, int 
         tiles[3 * (tl + r) + 1] = r * BM;
         tiles[3 * (tl + r) + 2] = rows;
         if (sched) {
-          const int slot = r < nf ? sfull + fu + r : sfull + full_total + pa;
+          const int slot = 1 + (r < nf ? sfull + fu + r : sfull + full_total + pa);
           reinterpret_cast<int4*>(sched)[slot] = make_int4(e, r * BM, rows, off + r * BM);
         }
       }
@@ -233,11 +233,12 @@ __device__ __forceinline__ void meta_small(const int32_t* __restrict__ ids, int 
     tiles[3 * (routed_tiles + r) + 1] = r * BM;
     tiles[3 * (routed_tiles + r) + 2] = min(BM, T - r * BM);
     if (sched)
-      reinterpret_cast<int4*>(sched)[r < sfull ? r : routed_tiles + nshared - 1] =
+      reinterpret_cast<int4*>(sched)[1 + (r < sfull ? r : routed_tiles + nshared - 1)] =
           make_int4(E, r * BM, min(BM, T - r * BM), T * k + r * BM);
   }
   if (lane == 0) {
     n_tiles[0] = routed_tiles + nshared;
+    if (sched) reinterpret_cast<int4*>(sched)[0] = make_int4(routed_tiles + nshared, 0, 0, 0);
     n_active[0] = total[2];
   }
   __builtin_amdgcn_wave_barrier();

@@ -278,6 +278,17 @@ def test_edge_layers(M, T, H, E, k, I, Is, seed, zipf, chunk, bm):
     check_route(r, ref, f"edge {case['name']}")
 
 
+def test_prefill_cut_long_tiles(M):
+    """Wide experts (8 gate/up column tiles each, so 32 long tiles stay whole on
+    256 compute units) with 48 long tiles: the schedule cuts 16 of them in two;
+    every output row is checked."""
+    case = mi.small_layer(2048, 64, 2, 2, 2048, 2048, 81, None)
+    lay = M.MoELayer(case["w"], 2, max_tokens=2048, tile_rows=128)
+    y = lay.forward_prefill(dev(M, case["x"]), None)
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), oracle_rows(case), "cut long tiles")
+
+
 def test_zero_tokens_is_noop(M):
     case = mi.make_case("tiny")
     lay = get_layer(M, case)
