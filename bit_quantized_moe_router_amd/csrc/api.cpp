@@ -257,7 +257,7 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
     });
   }
   TRY(timed(1, s, "top-k", [&] {
-    return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.xsum, o.x16, s);
+    return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.x16, s);
   }));
   TRY(timed(2, s, "routing metadata", [&] {
     return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, max_long_tiles(d), o.counts,

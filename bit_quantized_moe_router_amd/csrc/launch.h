@@ -27,7 +27,7 @@ hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr,
 // Top-k selection (exact recomputation of the screened candidates for T > 8).
 hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
-                               float* xsum, uint16_t* x16, hipStream_t s);
+                               uint16_t* x16, hipStream_t s);
 // max_long: tiles of more than BM/2 rows that the schedule keeps whole (the
 // rest are cut in two); 0 keeps every tile whole.
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared, int max_long,

@@ -68,6 +68,7 @@ constexpr int kScrSmem = 2 * 3 * kScrBuf;      // x, hi, lo; double buffered
 // screened logits, candidate experts and logits (E each), selected logits (16).
 __host__ __device__ constexpr int route_exact_smem_bytes(int H, int E) { return 256 + H * 2 + E * 12 + 64; }
 
+
 __global__ __launch_bounds__(256) void k_screen(const uint16_t* __restrict__ x, int T, int H,
                                                 const float* __restrict__ wr, int E,
                                                 float* __restrict__ approx, double* __restrict__ wsq) {
@@ -194,14 +195,17 @@ __global__ __launch_bounds__(256) void k_screen(const uint16_t* __restrict__ x, 
 }
 
 // ---------------------------------------------------------------------------
-// Many tokens, step 2: one wave per token.  With S = sum_h x w (exact), the
-// screened logit a = fp32(sum over slices in float64 + bias) and the exact
-// logit l = fp32(fp32(S) + bias) differ by at most
-//   B = (2^-17 + 1056 2^-24 + 2^-23) |x|_2 max_e |w_e|_2 + 2^-22 (max|a| + 1),
-// taken with a 2^-10 relative margin:
+// Many tokens, step 2: one workgroup per token.  With S = sum_h x w (exact),
+// the screened logit a = fp32(sum over slices in float64 + bias) and the
+// exact logit l = fp32(fp32(S) + bias) differ by at most
+//   B = (2^-17 + (n + 32) 2^-24 + 2^-23) |x|_2 max_e |w_e|_2 + 2^-22 (max|a| + 1),
+// taken with a 2^-10 relative margin, where n = 2 x (products of the longest
+// slice) = 128 ceil(G / kScreenSplit) (1024 at H = 2048):
 //  * |w - hi - lo| <= 2^-17 |w| (bf16 rounding of w, then of the exact rest);
-//  * each slice accumulates 2 x 512 exact products in fp32 (at most 1024
-//    roundings of 2^-24 relative to sum |x||w|, bounded by |x|_2 |w_e|_2);
+//  * each slice accumulates its hi and lo products, all exact, in fp32: at
+//    most n roundings of 2^-24 relative to sum |x||w| over the slice, and by
+//    Cauchy-Schwarz the slices together stay below n 2^-24 |x|_2 |w_e|_2 (the
+//    32 covers the higher-order terms);
 //  * the slices and the bias are summed in float64 (error negligible, covered
 //    by the rounding of the result to fp32, 2^-24 |a|);
 //  * the exact logit carries two fp32 roundings (2^-24 |S| and 2^-24 |l|).
@@ -209,8 +213,7 @@ __global__ __launch_bounds__(256) void k_screen(const uint16_t* __restrict__ x, 
 // the k-th largest screened logit (here the k-th largest of the per-lane
 // maxima), so only those experts are recomputed in float64 (one per half
 // wave) and the exact top-k is taken among them by rank.
-// Also writes the per-group activation sums and the fp16 activation copy of
-// the grouped GEMM.
+// Also writes the fp16 activation copy of the grouped GEMM.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict__ x, int T, int H,
                                                      const float* __restrict__ wr,
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
                                                      const float* __restrict__ approx,
                                                      const double* __restrict__ wsq,
                                                      int32_t* __restrict__ ids, float* __restrict__ tw,
-                                                     float* __restrict__ xsum, uint16_t* __restrict__ x16) {
+                                                     uint16_t* __restrict__ x16) {
   // One workgroup per token.  LDS: reduction slots, x row, screened logits,
   // candidate experts and their exact logits, selected logits.
   extern __shared__ __attribute__((aligned(16))) uint8_t rsm[];
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
   float* sel_v = cand_v + E;
   const uint16_t* xr = x + (int64_t)t * H;
 
-  // ---- x row (LDS copy, fp16 copy, per-group sums, |x|^2) and the screened
+  // ---- x row (LDS copy, fp16 copy, |x|^2) and the screened
   // logits (slices and bias summed in float64, rounded once); all loads are
   // independent of each other ----
   constexpr int kMaxXIter = 4;  // H <= 8192
@@ -268,20 +271,14 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
       *reinterpret_cast<uint4*>(xl + h) = v;
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       uint32_t c[4];
-      float s = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         c[j] = f32_to_f16_scaled(w[j] & 0xFFFFu) | ((uint32_t)f32_to_f16_scaled(w[j] >> 16) << 16);
         const float f0 = bf16_bits_to_f32(w[j] & 0xFFFFu), f1 = bf16_bits_to_f32(w[j] >> 16);
-        s += f0 + f1;
         xx = fma((double)f0, (double)f0, xx);
         xx = fma((double)f1, (double)f1, xx);
       }
       *reinterpret_cast<uint4*>(x16 + (int64_t)t * H + h) = make_uint4(c[0], c[1], c[2], c[3]);
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      if ((tid & 7) == 0) xsum[(int64_t)t * (H / kGroup) + h / kGroup] = s;
     }
   }
 #pragma unroll
@@ -327,7 +324,9 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
       }
     }
     const float ak = __shfl(m, k - 1);
-    const double c1 = 7.62939453125e-06 + 1056.0 * 5.9604644775390625e-08 + 1.1920928955078125e-07;
+    const int G = H / kGroup;
+    const double n_round = 128.0 * (double)((G + kScreenSplit - 1) / kScreenSplit);
+    const double c1 = 7.62939453125e-06 + (n_round + 32.0) * 5.9604644775390625e-08 + 1.1920928955078125e-07;
     const double B = (c1 * xnorm * (sqrt(w2m) * (1.0 + 1e-6)) + 2.384185791015625e-07 * (amx + 1.0)) *
                      (1.0 + 0.0009765625);
     const double lo = (double)ak - 2.0 * B;
@@ -713,17 +712,33 @@ __global__ __launch_bounds__(1024) void k_meta_scan(int T, int k, int E, int BM,
                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
                                                     int32_t* __restrict__ n_tiles, int32_t* __restrict__ active,
                                                     int32_t* __restrict__ n_active, int32_t* __restrict__ sched) {
+  // Segment counts are read kScanBatch at a time (independent loads), not
+  // one dependent load per segment.
+  constexpr int kScanBatch = 16;
   const int tid = threadIdx.x;
   int tot = 0;
-  if (tid < E)
-    for (int g = 0; g < nseg; g++) tot += segcnt[(int64_t)g * E + tid];
+  if (tid < E) {
+    for (int g0 = 0; g0 < nseg; g0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; i++) v[i] = g0 + i < nseg ? segcnt[(int64_t)(g0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; i++) tot += v[i];
+    }
+  }
   const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, counts, offsets, tiles, n_tiles, active,
                                     n_active, sched);
   if (tid < E) {
     int run = off_e;
-    for (int g = 0; g < nseg; g++) {
-      segbase[(int64_t)g * E + tid] = run;
-      run += segcnt[(int64_t)g * E + tid];
+    for (int g0 = 0; g0 < nseg; g0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; i++) v[i] = g0 + i < nseg ? segcnt[(int64_t)(g0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; i++) {
+        if (g0 + i < nseg) segbase[(int64_t)(g0 + i) * E + tid] = run;
+        run += v[i];
+      }
     }
   }
 }
@@ -821,10 +836,10 @@ hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr,
 
 hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
-                               float* xsum, uint16_t* x16, hipStream_t s) {
+                               uint16_t* x16, hipStream_t s) {
   if (T <= kSmallT) return hipSuccess;  // few tokens: k_topk_meta selects from the exact logits
   const size_t smem = (size_t)route_exact_smem_bytes(H, E);
-  k_route_exact<<<dim3(T), dim3(256), smem, s>>>(x, T, H, wr, bias, E, k, logits, wsq, ids, tw, xsum, x16);
+  k_route_exact<<<dim3(T), dim3(256), smem, s>>>(x, T, H, wr, bias, E, k, logits, wsq, ids, tw, x16);
   return hipGetLastError();
 }
 

@@ -316,6 +316,17 @@ def test_route_exact_ties(M, T):
     assert np.all(ref["topk_ids"][:, 0] % 2 == 0)
 
 
+def test_route_widest_hidden(M):
+    """H = 8192, the largest hidden size: the screen's slices hold 32 groups
+    each, and the error bound scales with them; routing stays bit-exact."""
+    case = mi.small_layer(200, 8192, 16, 4, 64, 64, seed=91, zipf_seed=92)
+    lay = M.MoELayer(case["w"], 4, max_tokens=200, tile_rows=32)
+    r = lay.route(dev(M, case["x"]), dev(M, case["bias"]))
+    torch.cuda.synchronize()
+    ref = orc.route(case["x"], case["w"]["router_w"], case["bias"], 4, 32, with_shared=True)
+    check_route(r, ref, "H=8192")
+
+
 @pytest.mark.parametrize("T", [3, 40])
 def test_route_zero_router_with_bias(M, T):
     case = mi.small_layer(T, 128, 24, 5, 64, 0, seed=81)
