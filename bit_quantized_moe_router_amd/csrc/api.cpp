@@ -191,7 +191,10 @@ hipEvent_t get_event() {
   return e;
 }
 
-// Launch `fn` (returning hipError_t), bracketed by events when timing is on.
+// Launch `fn(KTime)` (returning hipError_t).  When timing is on, the events
+// go to the launcher, which has its first kernel stamp the start and its last
+// kernel the end; both are also recorded just before, so a call that
+// enqueues nothing reads 0.
 template <class F>
 moe_status timed(int kid, hipStream_t s, const char* what, F fn) {
   Pending p{kid, nullptr, nullptr};
@@ -200,11 +203,18 @@ moe_status timed(int kid, hipStream_t s, const char* what, F fn) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     p.a = get_event();
     p.b = get_event();
-    if (p.a) (void)hipEventRecord(p.a, s);
+    if (p.a && p.b) {
+      (void)hipEventRecord(p.a, s);
+      (void)hipEventRecord(p.b, s);
+    }
   }
-  hipError_t e = fn();
+  KTime kt;
   if (on && p.a && p.b) {
-    (void)hipEventRecord(p.b, s);
+    kt.start = p.a;
+    kt.stop = p.b;
+  }
+  hipError_t e = fn(kt);
+  if (on && p.a && p.b) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_pending.push_back(p);
   }
@@ -245,24 +255,24 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
                      const float* bias, const RouteOut& o, hipStream_t s) {
   const int E = d->n_experts, k = d->top_k, H = d->hidden;
   bool two = false;
-  TRY(timed(0, s, "router logits", [&] {
-    return launch_route_logits(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.xsum, o.x16, s, &two);
+  TRY(timed(0, s, "router logits", [&](const KTime& kt) {
+    return launch_route_logits(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.xsum, o.x16, s, &two, kt);
   }));
   if (!two) {
     // Few tokens: exact logits are already there; top-k + metadata in one launch.
-    return timed(2, s, "top-k + routing metadata", [&] {
+    return timed(2, s, "top-k + routing metadata", [&](const KTime& kt) {
       return launch_topk_meta(o.logits, T, E, k, o.ids, o.tw, tile_rows(d), d->shared_inter > 0 ? 1 : 0,
                               o.counts, o.offsets, o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv,
-                              o.sched, s);
+                              o.sched, s, kt);
     });
   }
-  TRY(timed(1, s, "top-k", [&] {
-    return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.x16, s);
+  TRY(timed(1, s, "top-k", [&](const KTime& kt) {
+    return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.x16, s, kt);
   }));
-  TRY(timed(2, s, "routing metadata", [&] {
+  TRY(timed(2, s, "routing metadata", [&](const KTime& kt) {
     return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, max_long_tiles(d), o.counts,
                        o.offsets, o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv, o.sched,
-                       reinterpret_cast<int32_t*>(o.logits), s);  // the screened logits are dead by now
+                       reinterpret_cast<int32_t*>(o.logits), s, kt);  // the screened logits are dead by now
   }));
   return MOE_OK;
 }
@@ -334,9 +344,9 @@ moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_
   TRY(run_route(d, x, Tc, wr, bias, o, s));
   const ChunkArgs C = chunk_args(d, x, Tc, o, ws, w, y);
   const int mt = (int)max_sched_for(d, Tc);
-  TRY(timed(3, s, "gate/up GEMM", [&] { return launch_gateup_gemm(L, C, mt, s); }));
-  TRY(timed(4, s, "down GEMM", [&] { return launch_down_gemm(L, C, mt, s); }));
-  TRY(timed(7, s, "combine", [&] { return launch_combine(L, C, s); }));
+  TRY(timed(3, s, "gate/up GEMM", [&](const KTime& kt) { return launch_gateup_gemm(L, C, mt, s, kt); }));
+  TRY(timed(4, s, "down GEMM", [&](const KTime& kt) { return launch_down_gemm(L, C, mt, s, kt); }));
+  TRY(timed(7, s, "combine", [&](const KTime& kt) { return launch_combine(L, C, s, kt); }));
   return MOE_OK;
 }
 
@@ -472,8 +482,8 @@ moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, co
   const RouteOut o = ws_route(ws, w);
   TRY(run_route(desc, x, T, router_w, logit_bias, o, s));
   const ChunkArgs C = chunk_args(desc, x, T, o, ws, w, y);
-  TRY(timed(5, s, "gate/up GEMV", [&] { return launch_gemv_gateup(L, C, s); }));
-  TRY(timed(6, s, "down GEMV", [&] { return launch_gemv_down(L, C, s); }));
+  TRY(timed(5, s, "gate/up GEMV", [&](const KTime& kt) { return launch_gemv_gateup(L, C, s, kt); }));
+  TRY(timed(6, s, "down GEMV", [&](const KTime& kt) { return launch_gemv_down(L, C, s, kt); }));
   return MOE_OK;
 }
 

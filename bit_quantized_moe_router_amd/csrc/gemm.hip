@@ -428,7 +428,8 @@ int gateup_col_tiles(int I, int Is) {
 }
 
 template <bool kGateUp>
-static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s) {
+static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
+                                     const KTime& kt) {
   constexpr int smem = kGateUp ? kSmemGateUp : kSmemDown;
   static bool attr_set = false;
   if (!attr_set) {
@@ -439,20 +440,23 @@ static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int
   }
   const int n_ct = kGateUp ? gateup_col_tiles(L.I, L.Is) : (L.H + kDownColsPerWg - 1) / kDownColsPerWg;
   const int tiles8 = (max_sched + 7) / 8 * 8;
-  k_expert_gemm<kGateUp><<<dim3((unsigned)(tiles8 * n_ct)), dim3(kWaves * 64), smem, s>>>(L, C, n_ct);
+  MOE_LAUNCH(k_expert_gemm<kGateUp>, dim3((unsigned)(tiles8 * n_ct)), dim3(kWaves * 64), smem, s, kt.start, kt.stop,
+             L, C, n_ct);
   return hipGetLastError();
 }
 
-hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s) {
-  return launch_expert_gemm<true>(L, C, max_sched, s);
+hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
+                              const KTime& kt) {
+  return launch_expert_gemm<true>(L, C, max_sched, s, kt);
 }
 
-hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s) {
-  return launch_expert_gemm<false>(L, C, max_sched, s);
+hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
+                            const KTime& kt) {
+  return launch_expert_gemm<false>(L, C, max_sched, s, kt);
 }
 
-hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s) {
-  k_combine<<<dim3(C.T), dim3(256), 0, s>>>(L, C);
+hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt) {
+  MOE_LAUNCH(k_combine, dim3(C.T), dim3(256), 0, s, kt.start, kt.stop, L, C);
   return hipGetLastError();
 }
 

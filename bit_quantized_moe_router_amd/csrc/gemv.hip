@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkA
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_t s) {
+hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt) {
   const int Imax = L.I > L.Is ? L.I : L.Is;
   const int slots = (L.E < C.Tk ? L.E : C.Tk) + 1;
   dim3 grid(slots, Imax / 32);
@@ -327,11 +327,11 @@ hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_
     attr_set = true;
   }
   const size_t smem = (size_t)C.T * L.H * 2;
-  k_gemv_gateup<<<grid, dim3(kGuWaves * 64), smem, s>>>(L, C);
+  MOE_LAUNCH(k_gemv_gateup, grid, dim3(kGuWaves * 64), smem, s, kt.start, kt.stop, L, C);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s) {
+hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt) {
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_down),
@@ -342,7 +342,8 @@ hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t 
   const size_t rows = (size_t)C.Tk + C.T;
   const size_t stage = rows * C.Imax * 2 + rows * (C.Imax / 32) * 4;
   const int staged = stage <= (size_t)kDnStageMax ? 1 : 0;
-  k_gemv_down<<<dim3(L.H / 32), dim3(kDnWaves * 64), staged ? stage : 0, s>>>(L, C, staged);
+  MOE_LAUNCH(k_gemv_down, dim3(L.H / 32), dim3(kDnWaves * 64), staged ? stage : 0, s, kt.start, kt.stop, L, C,
+             staged);
   return hipGetLastError();
 }
 

@@ -1,9 +1,27 @@
 // Host-side launchers of the MoE kernels (one per kernel family).
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace moe {
+
+// Timing of one launcher call: the first kernel it enqueues stamps `start`
+// with its own start and the last one stamps `stop` with its own end
+// (hipExtLaunchKernel), so the interval holds the kernels and not the
+// dispatch gap before them.  Null events: a plain launch.
+struct KTime {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+#define MOE_LAUNCH(kernel, grid, block, smem, stream, ev0, ev1, ...)                                 \
+  do {                                                                                               \
+    if ((ev0) != nullptr || (ev1) != nullptr)                                                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, smem, stream, ev0, ev1, 0, __VA_ARGS__);            \
+    else                                                                                             \
+      kernel<<<grid, block, smem, stream>>>(__VA_ARGS__);                                            \
+  } while (0)
 
 struct PackArgs {
   const uint8_t* codes;
@@ -23,30 +41,32 @@ hipError_t launch_pack(const PackArgs& P, hipStream_t s);
 // *two_launches tells which.
 hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, float* logits, double* wsq, int32_t* ids, float* tw, float* xsum,
-                               uint16_t* x16, hipStream_t s, bool* two_launches);
+                               uint16_t* x16, hipStream_t s, bool* two_launches, const KTime& kt = KTime{});
 // Top-k selection (exact recomputation of the screened candidates for T > 8).
 hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
-                               uint16_t* x16, hipStream_t s);
+                               uint16_t* x16, hipStream_t s, const KTime& kt = KTime{});
 // max_long: tiles of more than BM/2 rows that the schedule keeps whole (the
 // rest are cut in two); 0 keeps every tile whole.
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared, int max_long,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
-                       int32_t* sched, int32_t* scratch, hipStream_t s);
+                       int32_t* sched, int32_t* scratch, hipStream_t s, const KTime& kt = KTime{});
 // T <= 8: top-k of exact logits and the metadata in one single-workgroup launch.
 hipError_t launch_topk_meta(const float* logits, int T, int E, int k, int32_t* ids, float* tw, int BM,
                             int with_shared, int32_t* counts, int32_t* offsets, int32_t* sorted,
                             int32_t* tiles, int32_t* n_tiles, int32_t* active, int32_t* n_active,
-                            int32_t* inv, int32_t* sched, hipStream_t s);
+                            int32_t* inv, int32_t* sched, hipStream_t s, const KTime& kt = KTime{});
 // max_sched: upper bound of the schedule's entry count (sizes the grid).
-hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s);
-hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s);
+hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
+                              const KTime& kt = KTime{});
+hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
+                            const KTime& kt = KTime{});
 // Gate/up column tiles per row tile (the GEMM grid's second dimension).
 int gateup_col_tiles(int I, int Is);
 // y[t] += sum_j w_tj * routed output of assignment (t, j) (GEMM path).
-hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);
-hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);
-hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s);
+hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
+hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
+hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
 
 }  // namespace moe

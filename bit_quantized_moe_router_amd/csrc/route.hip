@@ -822,53 +822,56 @@ __global__ __launch_bounds__(1024) void k_topk_meta(const float* __restrict__ lo
 // ---------------------------------------------------------------------------
 hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, float* logits, double* wsq, int32_t* ids, float* tw, float* xsum,
-                               uint16_t* x16, hipStream_t s, bool* two_launches) {
+                               uint16_t* x16, hipStream_t s, bool* two_launches, const KTime& kt) {
   if (T == 0) return hipSuccess;
   if (T <= kSmallT) {
-    k_logits_small<<<dim3((E + 3) / 4), dim3(256), 0, s>>>(x, T, H, wr, bias, E, logits, xsum, x16);
+    MOE_LAUNCH(k_logits_small, dim3((E + 3) / 4), dim3(256), 0, s, kt.start, kt.stop, x, T, H, wr, bias, E, logits,
+               xsum, x16);
     *two_launches = false;
     return hipGetLastError();
   }
-  k_screen<<<dim3((T + 63) / 64, (E + 63) / 64, kScreenSplit), dim3(256), 0, s>>>(x, T, H, wr, E, logits, wsq);
+  MOE_LAUNCH(k_screen, dim3((T + 63) / 64, (E + 63) / 64, kScreenSplit), dim3(256), 0, s, kt.start, kt.stop, x, T,
+             H, wr, E, logits, wsq);
   *two_launches = true;
   return hipGetLastError();
 }
 
 hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
-                               uint16_t* x16, hipStream_t s) {
+                               uint16_t* x16, hipStream_t s, const KTime& kt) {
   if (T <= kSmallT) return hipSuccess;  // few tokens: k_topk_meta selects from the exact logits
   const size_t smem = (size_t)route_exact_smem_bytes(H, E);
-  k_route_exact<<<dim3(T), dim3(256), smem, s>>>(x, T, H, wr, bias, E, k, logits, wsq, ids, tw, x16);
+  MOE_LAUNCH(k_route_exact, dim3(T), dim3(256), smem, s, kt.start, kt.stop, x, T, H, wr, bias, E, k, logits, wsq, ids,
+             tw, x16);
   return hipGetLastError();
 }
 
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared, int max_long,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
-                       int32_t* sched, int32_t* scratch, hipStream_t s) {
+                       int32_t* sched, int32_t* scratch, hipStream_t s, const KTime& kt) {
   const int N = T * k;
   const int nseg = (N + kSegAssign - 1) / kSegAssign;
   if (nseg <= 1) {  // one segment: the single-workgroup version
-    k_meta<<<dim3(1), dim3(1024), 0, s>>>(ids, T, k, E, BM, with_shared, max_long, counts, offsets, sorted,
-                                          tiles, n_tiles, active, n_active, inv, sched);
+    MOE_LAUNCH(k_meta, dim3(1), dim3(1024), 0, s, kt.start, kt.stop, ids, T, k, E, BM, with_shared, max_long,
+               counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
     return hipGetLastError();
   }
   int32_t* segcnt = scratch;
   int32_t* segbase = scratch + (size_t)nseg * E;
-  k_meta_count<<<dim3(nseg), dim3(256), 0, s>>>(ids, N, E, segcnt);
+  MOE_LAUNCH(k_meta_count, dim3(nseg), dim3(256), 0, s, kt.start, nullptr, ids, N, E, segcnt);
   k_meta_scan<<<dim3(1), dim3(1024), 0, s>>>(T, k, E, BM, with_shared, max_long, nseg, segcnt, segbase, counts, offsets,
                                               tiles, n_tiles, active, n_active, sched);
-  k_meta_scatter<<<dim3(nseg), dim3(256), 0, s>>>(ids, N, E, segbase, sorted, inv);
+  MOE_LAUNCH(k_meta_scatter, dim3(nseg), dim3(256), 0, s, nullptr, kt.stop, ids, N, E, segbase, sorted, inv);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_meta(const float* logits, int T, int E, int k, int32_t* ids, float* tw, int BM,
                             int with_shared, int32_t* counts, int32_t* offsets, int32_t* sorted,
                             int32_t* tiles, int32_t* n_tiles, int32_t* active, int32_t* n_active,
-                            int32_t* inv, int32_t* sched, hipStream_t s) {
-  k_topk_meta<<<dim3(1), dim3(1024), 0, s>>>(logits, T, E, k, ids, tw, BM, with_shared, counts, offsets,
-                                             sorted, tiles, n_tiles, active, n_active, inv, sched);
+                            int32_t* inv, int32_t* sched, hipStream_t s, const KTime& kt) {
+  MOE_LAUNCH(k_topk_meta, dim3(1), dim3(1024), 0, s, kt.start, kt.stop, logits, T, E, k, ids, tw, BM, with_shared,
+             counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
   return hipGetLastError();
 }
 
