@@ -480,9 +480,16 @@ moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, co
   const LayerArgs L = layer_args(desc, packed);
   const Ws w = ws_layout(desc, T);
   const RouteOut o = ws_route(ws, w);
-  TRY(run_route(desc, x, T, router_w, logit_bias, o, s));
+  // Exact logits, then the top-k and routing tables inside the gate/up GEMV.
+  bool two = false;
+  TRY(timed(0, s, "router logits", [&](const KTime& kt) {
+    return launch_route_logits(x, T, desc->hidden, router_w, logit_bias, desc->n_experts, desc->top_k, o.logits,
+                               o.wsq, o.ids, o.tw, nullptr, nullptr, s, &two, kt);
+  }));
   const ChunkArgs C = chunk_args(desc, x, T, o, ws, w, y);
-  TRY(timed(5, s, "gate/up GEMV", [&](const KTime& kt) { return launch_gemv_gateup(L, C, s, kt); }));
+  TRY(timed(5, s, "top-k + gate/up GEMV", [&](const KTime& kt) {
+    return launch_gemv_gateup(L, C, o.logits, tile_rows(desc), desc->shared_inter > 0 ? 1 : 0, s, kt);
+  }));
   TRY(timed(6, s, "down GEMV", [&](const KTime& kt) { return launch_gemv_down(L, C, s, kt); }));
   return MOE_OK;
 }

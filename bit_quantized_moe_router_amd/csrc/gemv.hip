@@ -15,50 +15,148 @@
 // shuffle, the waves of a workgroup through LDS.  No atomics: every output is
 // produced by exactly one workgroup, in a fixed order.
 #include "launch.h"
+#include "small_route.h"
 
 namespace moe {
 
 constexpr int kGemvMaxRows = 8;
 constexpr int kGuWaves = 8;    // gate/up workgroup: 8 waves split the H/64 groups
 constexpr int kGuPref = 4;     // groups per wave whose loads are issued together
-constexpr int kDnWaves = 16;   // down workgroup: 16 waves split the (expert, group) items
+constexpr int kDnWaves = 8;    // down workgroup: 8 waves split the (expert, group) items
 constexpr int kDnPref = 4;
 constexpr int kMaxGroups = 128;              // H / 64 for H <= 8192
 constexpr int kMaxAssign = kGemvMaxRows * 16; // T * k on the GEMV path
 constexpr int kMaxSlots = kMaxAssign + 1;     // active experts + the shared expert
 constexpr int kDnStageMax = 120 * 1024;       // LDS for staged intermediate rows
+constexpr int kGuSmemMax = 64 * 1024 + kGemvMaxRows * (2 * 512 + 16) * 4;  // x rows + top-k lists
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU.  grid = (expert slots: active experts, then the shared
-// expert; I/32 row blocks).
+// Top-k + gate/up + SwiGLU.  grid = (expert slots: active experts, then the
+// shared expert, then one metadata workgroup; I/32 row blocks).
+//
+// Routing is folded in, so decode needs no separate top-k launch between the
+// logits and the weights: every workgroup takes the top-k of the chunk's rows
+// from the exact logits itself (waves t < T, one row each), then wave 0 finds
+// the workgroup's expert (the slot-th smallest selected expert: a bitmap of
+// the selected experts and prefix popcounts over its words) and the expert's
+// rows in flat assignment order.  The last column of workgroups (row block 0
+// only) writes the routing tables the down kernel reads (ids, weights,
+// counts, offsets, sorted order, active list, ...) with meta_small.  The
+// activation rows are staged in LDS first, independent of the routing; their
+// per-group sums are taken there.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, ChunkArgs C) {
+__global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, ChunkArgs C, const float* logits,
+                                                               int BM, int with_shared) {
   const int slot = blockIdx.x, nb = blockIdx.y;
-  const int T = C.T, H = L.H, G = H / kGroup;
+  const int T = C.T, H = L.H, G = H / kGroup, E = L.E, k = L.k, N = T * k;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  extern __shared__ uint16_t xl[];  // [T][H]: every row of the chunk
+  const bool meta_wg = slot == (int)gridDim.x - 1;
+  if (meta_wg && nb != 0) return;  // workgroup-uniform, before any barrier
+  extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];  // [T][H] x rows, then [T][2E+16] top-k lists
+  uint16_t* xl = reinterpret_cast<uint16_t*>(gsm);
+  int* lists = reinterpret_cast<int*>(gsm + (size_t)T * H * 2);
   __shared__ float xs[kGemvMaxRows * kMaxGroups];
-  __shared__ int tok[kGemvMaxRows], orow[kGemvMaxRows];
+  __shared__ int s_ids[kMaxAssign];
+  __shared__ float s_tw[kMaxAssign];
+  __shared__ uint32_t s_bm[kMaxE / 32];
+  __shared__ int tok[kGemvMaxRows], orow[kGemvMaxRows], s_info[3];
   __shared__ float red[kGuWaves][kGemvMaxRows][2][32];
 
-  // Loads that do not depend on the routing go out first: the chunk's
-  // activation rows and their group sums (T <= 8 rows).  The slot's expert
-  // is read speculatively (clamped to a valid index) next to n_active.
+  // ---- loads independent of the routing: the chunk's activation rows ----
   const int H8 = H / 8;
-  for (int i = tid; i < T * H8; i += blockDim.x) reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(C.x)[i];
-  for (int i = tid; i < T * G; i += blockDim.x) xs[i] = C.xsum[i];
-  const int nact = *C.n_active;
-  const int e_spec = C.active[slot < L.E ? slot : L.E - 1];
-  const bool shared = slot == nact;
-  if (slot > nact || (shared && L.Is == 0)) return;  // workgroup-uniform, before any barrier
-  const int e = shared ? L.E : min(max(e_spec, 0), L.E - 1);
+  if (!meta_wg)
+    for (int i = tid; i < T * H8; i += blockDim.x) reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(C.x)[i];
+  // ---- top-k of each row ----
+  if (wave < T) topk_small(logits + (int64_t)wave * E, E, k, wave, s_ids, s_tw, lists + wave * (2 * E + 16));
+  if (tid < kMaxE / 32) s_bm[tid] = 0u;
+  __syncthreads();
+
+  if (meta_wg) {
+    // Routing tables of the chunk (workspace; the down kernel reads them).
+    int32_t* ids = const_cast<int32_t*>(C.ids);
+    float* tw = const_cast<float*>(C.tw);
+    for (int a = tid; a < N; a += blockDim.x) {
+      ids[a] = s_ids[a];
+      tw[a] = s_tw[a];
+    }
+    if (wave == 0)
+      meta_small(s_ids, T, k, E, BM, with_shared, const_cast<int32_t*>(C.counts), const_cast<int32_t*>(C.offsets),
+                 const_cast<int32_t*>(C.sorted), const_cast<int32_t*>(C.tiles), const_cast<int32_t*>(C.n_tiles),
+                 const_cast<int32_t*>(C.active), const_cast<int32_t*>(C.n_active), const_cast<int32_t*>(C.inv),
+                 const_cast<int32_t*>(C.sched), lists);
+    return;
+  }
+
+  // ---- this workgroup's expert and rows (wave 0) ----
+  if (wave == 0) {
+    const int id0 = lane < N ? s_ids[lane] : -1, id1 = lane + 64 < N ? s_ids[lane + 64] : -1;
+    if (id0 >= 0) atomicOr(&s_bm[id0 >> 5], 1u << (id0 & 31));
+    if (id1 >= 0) atomicOr(&s_bm[id1 >> 5], 1u << (id1 & 31));
+    __builtin_amdgcn_wave_barrier();
+    const int nw = (E + 31) / 32;
+    const uint32_t word = lane < nw ? s_bm[lane] : 0u;
+    const int cnt = __popc(word);
+    const int incl = wave_incl_scan(cnt);
+    const int nact = __shfl(incl, 63);
+    int e = -1;
+    if (slot < nact) {
+      // The word holding the slot-th set bit, then the bit inside it.
+      const bool here = incl > slot && incl - cnt <= slot;
+      const uint64_t hm = __ballot(here);
+      const int wl = __ffsll((unsigned long long)hm) - 1;
+      const uint32_t wv = __shfl(word, wl);
+      int r = slot - (__shfl(incl, wl) - __shfl(cnt, wl));
+      uint32_t v = wv;
+      for (; r > 0; r--) v &= v - 1;
+      e = wl * 32 + (__ffs(v) - 1);
+    }
+    const bool shared = slot == nact;
+    int rows = 0;
+    if (e >= 0) {
+      const int off = __popcll(__ballot(id0 >= 0 && id0 < e)) + __popcll(__ballot(id1 >= 0 && id1 < e));
+      const uint64_t m0 = __ballot(id0 == e), m1 = __ballot(id1 == e);
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      rows = __popcll(m0) + __popcll(m1);
+      if (id0 == e) {
+        const int r = __popcll(m0 & lt);
+        tok[r] = lane / k;
+        orow[r] = off + r;
+      }
+      if (id1 == e) {
+        const int r = __popcll(m0) + __popcll(m1 & lt);
+        tok[r] = (lane + 64) / k;
+        orow[r] = off + r;
+      }
+    } else if (shared && L.Is > 0) {
+      rows = T;
+      if (lane < T) {
+        tok[lane] = lane;
+        orow[lane] = N + lane;
+      }
+    }
+    if (lane == 0) {
+      s_info[0] = shared ? L.E : e;
+      s_info[1] = rows;
+      s_info[2] = nact;
+    }
+  }
+  // Per-group activation sums (sequential inside a group), from LDS.
+  for (int i = tid; i < T * G; i += blockDim.x) {
+    const int t = i / G, g = i - t * G;
+    const uint16_t* p = xl + t * H + g * kGroup;
+    float sm = 0.f;
+    for (int j = 0; j < kGroup; j++) sm += bf16_bits_to_f32(p[j]);
+    xs[i] = sm;
+  }
+  __syncthreads();
+  const int e = s_info[0], rows = s_info[1];
+  const bool shared = e == L.E;
   const int Iw = shared ? L.Is : L.I;
-  if (nb * 32 >= Iw) return;
+  if (rows == 0 || nb * 32 >= Iw) return;  // workgroup-uniform; no barrier before this point is pending
   const uint8_t* wbase = expert_base(L, e) + (int64_t)nb * G * 2 * kBlockBytes;
 
-  // This wave's first weight loads.
   uint4 cg[kGuPref], cu[kGuPref];
   uint32_t sbg[kGuPref], sbu[kGuPref];
   auto load = [&](int g0) {
@@ -74,21 +172,13 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
       }
     }
   };
-  load(wave);
-
-  const int rows = shared ? T : C.counts[e];
-  if (tid < rows) {
-    tok[tid] = shared ? tid : C.sorted[C.offsets[e] + tid] / L.k;
-    orow[tid] = shared ? C.Tk + tid : C.offsets[e] + tid;
-  }
-  __syncthreads();
 
   float accg[kGemvMaxRows], accu[kGemvMaxRows];
 #pragma unroll
   for (int j = 0; j < kGemvMaxRows; j++) accg[j] = accu[j] = 0.f;
 
   for (int g0 = wave; g0 < G; g0 += kGuPref * kGuWaves) {
-    if (g0 != wave) load(g0);
+    load(g0);
 #pragma unroll
     for (int p = 0; p < kGuPref; p++) {
       const int g = g0 + p * kGuWaves;
@@ -164,28 +254,34 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
 }
 
 // ---------------------------------------------------------------------------
-// down + routing weight + shared add + combine.  grid = H/32 output row
-// blocks; the workgroup walks every (expert slot, group) item, waves taking
-// items round-robin with their loads issued in batches, and writes y for all
-// tokens of the chunk.  The routing tables (slot -> expert, segment, rows;
-// sorted position -> token, weight) and, when they fit, all intermediate rows
-// and their sums are staged in LDS first, so the item loop only waits for
-// the weight codes.  The first batch of codes is issued before the staging,
-// from a speculative read of the active list.
+// down + routing weight + shared add + combine.  grid = H/8 workgroups of 8
+// output rows each.  A workgroup walks every (expert slot, group) item; the
+// items' 8-row slices of their 1152-byte blocks (two 128-byte runs of codes
+// and 32 bytes of scale/bias) are read by 16 lanes each, so a wave covers 4
+// items per load: lane l takes item l/16, row l%8 and K half (l/8)%2.  The
+// routing tables (slot -> expert, segment, rows; sorted position -> token,
+// weight) and, when they fit, all intermediate rows and their sums are staged
+// in LDS first; the first item loads go out before the staging, from a
+// speculative read of the active list.  Partial sums meet in registers (K
+// halves, items of a wave) and LDS (waves); every output has one owner.
 // ---------------------------------------------------------------------------
+constexpr int kDnRows = 8;                         // output rows per workgroup
+constexpr int kDnItemsPerLoad = kDnWaves * 4;      // items one load round covers
+
 __global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkArgs C, int staged) {
-  const int nb = blockIdx.x;
+  const int row0 = blockIdx.x * kDnRows;
   const int H = L.H, T = C.T, Tk = C.Tk;
   const int hsw = C.Imax / 32;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int h = lane >> 5, col = lane & 31;
+  const int sub = lane >> 4, hh = (lane >> 3) & 1, r = lane & 7;
+  const int rr = row0 % 32 + r, nb32 = row0 / 32;  // row inside its 32-row block, block index
   const int Gi = L.I / kGroup, Gs = L.Is / kGroup;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];  // staged h rows, then their sums
   __shared__ int s_e[kMaxSlots], s_seg[kMaxSlots], s_rows[kMaxSlots];
   __shared__ int s_tok[kMaxAssign];
   __shared__ float s_w[kMaxAssign];
-  __shared__ float red[kDnWaves][kGemvMaxRows][32];
+  __shared__ float red[kDnWaves][kGemvMaxRows][kDnRows];
 
   const int nact = *C.n_active;
   const int nspec = min(L.E, Tk);  // slots the active list can hold
@@ -204,10 +300,10 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkA
   uint4 cd[kDnPref];
   uint32_t sb[kDnPref];
   int pe[kDnPref], pg[kDnPref];
-  auto load = [&](int it0) {
+  auto load = [&](int base) {
 #pragma unroll
     for (int p = 0; p < kDnPref; p++) {
-      const int it = it0 + p * kDnWaves;
+      const int it = base + p * kDnItemsPerLoad + wave * 4 + sub;
       pe[p] = -1;
       pg[p] = 0;
       if (it < nitems) {
@@ -216,15 +312,15 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkA
         const bool sh = e == L.E;
         const int Gk = sh ? Gs : Gi;
         const uint8_t* blk = expert_base(L, e) + (sh ? L.shared_gateup_bytes : L.gateup_bytes) +
-                             (int64_t)(nb * Gk + g) * kBlockBytes;
-        cd[p] = *reinterpret_cast<const uint4*>(blk + lane * 16);
-        sb[p] = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
+                             (int64_t)(nb32 * Gk + g) * kBlockBytes;
+        cd[p] = *reinterpret_cast<const uint4*>(blk + (hh * 32 + rr) * 16);
+        sb[p] = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + rr * 4);
         pe[p] = it < nact * Gi ? it / Gi : nact;  // slot
         pg[p] = g;
       }
     }
   };
-  load(wave);
+  load(0);
 
   // ---- staging: routing tables, then (if staged) h rows and their sums ----
   for (int a = tid; a < Tk; a += blockDim.x) {
@@ -260,11 +356,11 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkA
 #pragma unroll
   for (int t = 0; t < kGemvMaxRows; t++) acc[t] = 0.f;
 
-  for (int it0 = wave; it0 < nitems; it0 += kDnPref * kDnWaves) {
-    if (it0 != wave) load(it0);
+  for (int base = 0; base < nitems; base += kDnPref * kDnItemsPerLoad) {
+    if (base != 0) load(base);
 #pragma unroll
     for (int p = 0; p < kDnPref; p++) {
-      if (pe[p] < 0) break;
+      if (pe[p] < 0) continue;
       const int sl = pe[p], g = pg[p];
       const bool sh = sl == nact;
       const int rows = s_rows[sl];
@@ -279,7 +375,7 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkA
         const int irow = seg + j;
         const int t = sh ? j : s_tok[irow];
         const float w = sh ? 1.f : s_w[irow];
-        const uint4* hp = reinterpret_cast<const uint4*>(hb + (int64_t)irow * C.Imax + g * kGroup + h * 32);
+        const uint4* hp = reinterpret_cast<const uint4*>(hb + (int64_t)irow * C.Imax + g * kGroup + hh * 32);
         float d = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; c++) {
@@ -289,45 +385,50 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkA
           d = dot2_bf16(q[4 * c + 2], hv.z, d);
           d = dot2_bf16(q[4 * c + 3], hv.w, d);
         }
-        // hsum holds 32-column sums, so this lane half's own columns.
-        const float v = w * fmaf(s, d, bp * hs[(int64_t)irow * hsw + 2 * g + h]);
+        // hsum holds 32-column sums, so this lane's K half.
+        const float v = w * fmaf(s, d, bp * hs[(int64_t)irow * hsw + 2 * g + hh]);
 #pragma unroll
         for (int tt = 0; tt < kGemvMaxRows; tt++)
           if (tt == t) acc[tt] += v;
       }
     }
   }
+  // K halves (lane bit 3) and the wave's 4 items (lane bits 4, 5), then waves.
 #pragma unroll
   for (int t = 0; t < kGemvMaxRows; t++) {
     if (t < T) {
+      acc[t] += __shfl_xor(acc[t], 8);
+      acc[t] += __shfl_xor(acc[t], 16);
       acc[t] += __shfl_xor(acc[t], 32);
-      if (h == 0) red[wave][t][col] = acc[t];
+      if (lane < kDnRows) red[wave][t][lane] = acc[t];
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < T * 32; i += blockDim.x) {
-    const int t = i >> 5, n = i & 31;
+  for (int i = tid; i < T * kDnRows; i += blockDim.x) {
+    const int t = i / kDnRows, n = i - t * kDnRows;
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kDnWaves; w++) v += red[w][t][n];
-    C.y[(int64_t)t * H + nb * 32 + n] = v;
+    C.y[(int64_t)t * H + row0 + n] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt) {
+hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, const float* logits, int BM,
+                              int with_shared, hipStream_t s, const KTime& kt) {
   const int Imax = L.I > L.Is ? L.I : L.Is;
   const int slots = (L.E < C.Tk ? L.E : C.Tk) + 1;
-  dim3 grid(slots, Imax / 32);
+  dim3 grid(slots + 1, Imax / 32);  // + the metadata workgroup
   static bool attr_set = false;
-  if (!attr_set) {  // activation rows: T * H * 2 <= 64 KB on this path, beside ~20 KB of static LDS
+  if (!attr_set) {  // rows T * H * 2 <= 64 KB on this path, lists <= 8 * 1040 * 4, beside ~26 KB of static LDS
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_gateup),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kGuSmemMax);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const size_t smem = (size_t)C.T * L.H * 2;
-  MOE_LAUNCH(k_gemv_gateup, grid, dim3(kGuWaves * 64), smem, s, kt.start, kt.stop, L, C);
+  const size_t smem = (size_t)C.T * L.H * 2 + (size_t)C.T * (2 * L.E + 16) * 4;
+  if (smem > (size_t)kGuSmemMax || C.T > kGemvMaxRows || C.Tk > kMaxAssign) return hipErrorInvalidValue;
+  MOE_LAUNCH(k_gemv_gateup, grid, dim3(kGuWaves * 64), smem, s, kt.start, kt.stop, L, C, logits, BM, with_shared);
   return hipGetLastError();
 }
 
@@ -342,8 +443,8 @@ hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t 
   const size_t rows = (size_t)C.Tk + C.T;
   const size_t stage = rows * C.Imax * 2 + rows * (C.Imax / 32) * 4;
   const int staged = stage <= (size_t)kDnStageMax ? 1 : 0;
-  MOE_LAUNCH(k_gemv_down, dim3(L.H / 32), dim3(kDnWaves * 64), staged ? stage : 0, s, kt.start, kt.stop, L, C,
-             staged);
+  MOE_LAUNCH(k_gemv_down, dim3(L.H / kDnRows), dim3(kDnWaves * 64), staged ? stage : 0, s, kt.start, kt.stop, L,
+             C, staged);
   return hipGetLastError();
 }
 

@@ -66,7 +66,10 @@ hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sche
 int gateup_col_tiles(int I, int Is);
 // y[t] += sum_j w_tj * routed output of assignment (t, j) (GEMM path).
 hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
-hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
+// Decode GEMV path: top-k of the exact logits (and the chunk's routing tables)
+// folded into the gate/up GEMV, then the down GEMV.
+hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, const float* logits, int BM, int with_shared,
+                              hipStream_t s, const KTime& kt = KTime{});
 hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
 
 }  // namespace moe

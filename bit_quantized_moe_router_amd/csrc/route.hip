@@ -30,8 +30,8 @@ __device__ __forceinline__ uint16_t f32_to_f16_scaled(uint16_t b) {
 
 // ---------------------------------------------------------------------------
 // Few tokens: all T x E logits in float64.  One wave per expert, lanes split h
-// in 16-byte slices of the router row.  Workgroup 0 also writes the per-group
-// activation sums used by the expert kernels.
+// in 16-byte slices of the router row.  Workgroups 0 and 1 also write the
+// per-group activation sums and the fp16 activation copy when asked (non-null).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict__ x, int T, int H,
                                                       const float* __restrict__ wr,
@@ -41,8 +41,8 @@ __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict
                                                       uint16_t* __restrict__ x16) {
   const int wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 4 + wave;
-  if (blockIdx.x == 0) group_sums(x, T, H, xsum, threadIdx.x, blockDim.x);
-  if (blockIdx.x == (gridDim.x > 1 ? 1 : 0)) {
+  if (xsum && blockIdx.x == 0) group_sums(x, T, H, xsum, threadIdx.x, blockDim.x);
+  if (x16 && blockIdx.x == (gridDim.x > 1 ? 1 : 0)) {
     for (int i = threadIdx.x; i < T * H; i += blockDim.x) x16[i] = f32_to_f16_scaled(x[i]);
   }
   if (e < E) logits_one_expert(x, T, H, wr, bias, E, e, logits);

@@ -1,6 +1,6 @@
 // Routing building blocks for few tokens (T <= 8), shared by the routing
-// kernels and the fused decode kernel ("Optimizing on-device inference for
-// Apple Silicon", section "Keep expert routing on the GPU").
+// kernels and the decode GEMV ("Optimizing on-device inference for Apple
+// Silicon", section "Keep expert routing on the GPU").
 #pragma once
 
 #include "common.h"
@@ -39,26 +39,45 @@ __device__ __forceinline__ uint64_t match_mask(int e, bool valid, int nbits) {
 }
 
 // Exact router logits of expert e for T <= 8 tokens, one wave: lanes split h
-// in 16-byte slices of the router row; every product x * Wr is exact in
-// float64, the sums are float64, rounded once to fp32, then the fp32 bias.
+// in 16-byte slices of the router row (lane l: columns 256 i + 4 l .. +3);
+// every product x * Wr is exact in float64, the sums are float64, rounded once
+// to fp32, then the fp32 bias.  The loads of 2048 columns of the router row
+// and of the rows' matching parts are issued before their sums, so the wave
+// waits for memory once per 2048 columns.
 __device__ __forceinline__ void logits_one_expert(const uint16_t* __restrict__ x, int T, int H,
                                                   const float* __restrict__ wr, const float* __restrict__ bias,
                                                   int E, int e, float* __restrict__ logits) {
+  constexpr int kIt = 8;
   const int lane = threadIdx.x & 63;
   double acc[kSmallT];
 #pragma unroll
   for (int t = 0; t < kSmallT; t++) acc[t] = 0.0;
   const float* wrow = wr + (int64_t)e * H;
-  for (int h = 4 * lane; h < H; h += 256) {
-    const float4 w4 = *reinterpret_cast<const float4*>(wrow + h);
+  for (int h0 = 0; h0 < H; h0 += 256 * kIt) {
+    float4 w4[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; i++) {
+      const int h = h0 + 256 * i + 4 * lane;
+      w4[i] = h < H ? *reinterpret_cast<const float4*>(wrow + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
     for (int t = 0; t < kSmallT; t++) {
       if (t < T) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + (int64_t)t * H + h);
-        acc[t] = fma((double)bf16_bits_to_f32(xv.x & 0xFFFFu), (double)w4.x, acc[t]);
-        acc[t] = fma((double)bf16_bits_to_f32(xv.x >> 16), (double)w4.y, acc[t]);
-        acc[t] = fma((double)bf16_bits_to_f32(xv.y & 0xFFFFu), (double)w4.z, acc[t]);
-        acc[t] = fma((double)bf16_bits_to_f32(xv.y >> 16), (double)w4.w, acc[t]);
+        uint2 xv[kIt];
+#pragma unroll
+        for (int i = 0; i < kIt; i++) {
+          const int h = h0 + 256 * i + 4 * lane;
+          xv[i] = h < H ? *reinterpret_cast<const uint2*>(x + (int64_t)t * H + h) : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < kIt; i++) {
+          if (h0 + 256 * i + 4 * lane < H) {
+            acc[t] = fma((double)bf16_bits_to_f32(xv[i].x & 0xFFFFu), (double)w4[i].x, acc[t]);
+            acc[t] = fma((double)bf16_bits_to_f32(xv[i].x >> 16), (double)w4[i].y, acc[t]);
+            acc[t] = fma((double)bf16_bits_to_f32(xv[i].y & 0xFFFFu), (double)w4[i].z, acc[t]);
+            acc[t] = fma((double)bf16_bits_to_f32(xv[i].y >> 16), (double)w4[i].w, acc[t]);
+          }
+        }
       }
     }
   }
