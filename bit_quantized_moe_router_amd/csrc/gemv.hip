@@ -64,12 +64,18 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
   __shared__ int tok[kGemvMaxRows], orow[kGemvMaxRows], s_info[3];
   __shared__ float red[kGuWaves][kGemvMaxRows][2][32];
 
-  // ---- loads independent of the routing: the chunk's activation rows ----
-  const int H8 = H / 8;
-  if (!meta_wg)
-    for (int i = tid; i < T * H8; i += blockDim.x) reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(C.x)[i];
+  // ---- loads independent of the routing: the chunk's activation rows, into
+  // registers first so that their latency overlaps the top-k's ----
+  const int H8 = H / 8, nx = meta_wg ? 0 : T * H8;
+  constexpr int kNt = kGuWaves * 64;
+  uint4 xr0 = make_uint4(0u, 0u, 0u, 0u), xr1 = xr0;
+  if (tid < nx) xr0 = reinterpret_cast<const uint4*>(C.x)[tid];
+  if (tid + kNt < nx) xr1 = reinterpret_cast<const uint4*>(C.x)[tid + kNt];
   // ---- top-k of each row ----
   if (wave < T) topk_small(logits + (int64_t)wave * E, E, k, wave, s_ids, s_tw, lists + wave * (2 * E + 16));
+  if (tid < nx) reinterpret_cast<uint4*>(xl)[tid] = xr0;
+  if (tid + kNt < nx) reinterpret_cast<uint4*>(xl)[tid + kNt] = xr1;
+  for (int i = tid + 2 * kNt; i < nx; i += kNt) reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(C.x)[i];
   if (tid < kMaxE / 32) s_bm[tid] = 0u;
   __syncthreads();
 
@@ -142,14 +148,6 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
       s_info[2] = nact;
     }
   }
-  // Per-group activation sums (sequential inside a group), from LDS.
-  for (int i = tid; i < T * G; i += blockDim.x) {
-    const int t = i / G, g = i - t * G;
-    const uint16_t* p = xl + t * H + g * kGroup;
-    float sm = 0.f;
-    for (int j = 0; j < kGroup; j++) sm += bf16_bits_to_f32(p[j]);
-    xs[i] = sm;
-  }
   __syncthreads();
   const int e = s_info[0], rows = s_info[1];
   const bool shared = e == L.E;
@@ -173,12 +171,32 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
     }
   };
 
+  load(wave);
+  // Per-group activation sums while the first codes are in flight: 8 lanes
+  // per group, 8 columns each, then a 3-step shuffle tree.
+  for (int i0 = 0; i0 < T * G * 8; i0 += blockDim.x) {
+    const int i = i0 + tid, gi = i >> 3, part = i & 7;
+    float sm = 0.f;
+    if (gi < T * G) {
+      const int t = gi / G, g = gi - t * G;
+      const uint4 v = *reinterpret_cast<const uint4*>(xl + t * H + g * kGroup + part * 8);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; j++) sm += bf16_bits_to_f32(w[j] & 0xFFFFu) + bf16_bits_to_f32(w[j] >> 16);
+    }
+    sm += __shfl_xor(sm, 1);
+    sm += __shfl_xor(sm, 2);
+    sm += __shfl_xor(sm, 4);
+    if (gi < T * G && part == 0) xs[gi] = sm;
+  }
+  __syncthreads();
+
   float accg[kGemvMaxRows], accu[kGemvMaxRows];
 #pragma unroll
   for (int j = 0; j < kGemvMaxRows; j++) accg[j] = accu[j] = 0.f;
 
   for (int g0 = wave; g0 < G; g0 += kGuPref * kGuWaves) {
-    load(g0);
+    if (g0 != wave) load(g0);
 #pragma unroll
     for (int p = 0; p < kGuPref; p++) {
       const int g = g0 + p * kGuWaves;

@@ -151,17 +151,33 @@ __device__ __forceinline__ void topk_small(const float* __restrict__ l, int E, i
     C += __popcll(mk);
   }
   __builtin_amdgcn_wave_barrier();
-  for (int c = lane; c < C; c += 64) {
-    const float vc = cand_v[c];
-    const int ec = cand_e[c];
+  if (C <= 64) {
+    // Candidates in lanes; the others are broadcast with v_readlane.
+    const float vc = lane < C ? cand_v[lane] : 0.f;
+    const int ec = lane < C ? cand_e[lane] : 0;
     int rank = 0;
     for (int c2 = 0; c2 < C; c2++) {
-      const float v2 = cand_v[c2];
-      rank += (v2 > vc || (v2 == vc && cand_e[c2] < ec)) ? 1 : 0;
+      const float v2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vc), c2));
+      const int e2 = __builtin_amdgcn_readlane(ec, c2);
+      rank += (v2 > vc || (v2 == vc && e2 < ec)) ? 1 : 0;
     }
-    if (rank < k) {
+    if (lane < C && rank < k) {
       ids[(int64_t)t * k + rank] = ec;
       sel_v[rank] = vc;
+    }
+  } else {
+    for (int c = lane; c < C; c += 64) {
+      const float vc = cand_v[c];
+      const int ec = cand_e[c];
+      int rank = 0;
+      for (int c2 = 0; c2 < C; c2++) {
+        const float v2 = cand_v[c2];
+        rank += (v2 > vc || (v2 == vc && cand_e[c2] < ec)) ? 1 : 0;
+      }
+      if (rank < k) {
+        ids[(int64_t)t * k + rank] = ec;
+        sel_v[rank] = vc;
+      }
     }
   }
   __builtin_amdgcn_wave_barrier();
