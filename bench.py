@@ -181,38 +181,79 @@ def main():
     d = kern_all["k_down_gemm"]
     down_tf = flop_down / (d["avg_us"] * 1e-6) / 1e12
 
-    # Decode T=1 (GEMV path) on the same layer copies.
-    dcase = mi.make_case("decode")
-    xd = to_dev(dcase["x"], dev)
-    yd = torch.empty((1, H), dtype=torch.float32, device=dev)
+    # Decode (GEMV path at T=1) on the same layer copies.  Every call takes
+    # another of 64 seeded token rows, so the experts change from call to call
+    # and the weights come from HBM, not from the Infinity Cache.
+    NX = 64
+    xd_all = to_dev(mi.gen_x(NX, H, 4242), dev)
+    xds = [xd_all[i:i + 1] for i in range(NX)]
+    yd = torch.empty((8, H), dtype=torch.float32, device=dev)
+
+    def decode_run(n, T=1):
+        for i in range(n):
+            j = (i * 8) % NX
+            xin = xds[j] if T == 1 else xd_all[j:j + T]
+            layers[i % len(layers)].forward_decode(xin, None, yd[:T])
+
+    def timed_decode(T=1):
+        decode_run(10, T)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        decode_run(a.decode_steps, T)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        return 1000.0 * d0.elapsed_time(d1) / a.decode_steps
+
     for lay in layers:
         lay.set_desc(gemv_max_rows=-1)
-    for i in range(10):
-        layers[i % len(layers)].forward_decode(xd, None, yd)
-    torch.cuda.synchronize()
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for i in range(a.decode_steps):
-        layers[i % len(layers)].forward_decode(xd, None, yd)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dec_us = 1000.0 * d0.elapsed_time(d1) / a.decode_steps
-
-    def decode_pass():
-        for i in range(a.decode_steps):
-            layers[i % len(layers)].forward_decode(xd, None, yd)
-
-    dkern = breakdown(decode_pass, [moe.K_LOGITS, moe.K_META, moe.K_GATEUP_GEMV, moe.K_DOWN_GEMV])
+    dec_us = timed_decode(1)
+    dkern = breakdown(lambda: decode_run(a.decode_steps), [moe.K_LOGITS, moe.K_META, moe.K_GATEUP_GEMV,
+                                                           moe.K_DOWN_GEMV])
     blk = 1152
     gu_bytes = 9 * (I // 32) * (H // 64) * 2 * blk          # 8 routed + shared, gate and up, packed
     dn_bytes = 9 * (H // 32) * (I // 64) * blk
     gemv_gu = dkern.get("k_gemv_gateup")
     gemv_dn = dkern.get("k_gemv_down")
+
+    # Reference for "achievable" at these sizes: a device-to-device copy of the
+    # same number of bytes (read + write counted), over rotating buffers.
+    def copy_gbs(nbytes):
+        n = nbytes // 2
+        srcs = [torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1) for _ in range(16)]
+        dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        for i in range(8):
+            dst.copy_(srcs[i % 16])
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for i in range(200):
+            dst.copy_(srcs[i % 16])
+        c1.record(stream)
+        torch.cuda.synchronize()
+        return round(2 * n * 2 / (c0.elapsed_time(c1) / 200 * 1e-3) / 1e9, 1)
+
     dec_roof = {
+        "gateup_gemv_bytes": gu_bytes,
         "gateup_gemv_GBs": round(gu_bytes / (gemv_gu["avg_us"] * 1e-6) / 1e9, 1) if gemv_gu else None,
+        "down_gemv_bytes": dn_bytes,
         "down_gemv_GBs": round(dn_bytes / (gemv_dn["avg_us"] * 1e-6) / 1e9, 1) if gemv_dn else None,
+        "copy_GBs_same_bytes_gateup": copy_gbs(gu_bytes),
+        "copy_GBs_same_bytes_down": copy_gbs(dn_bytes),
         "peak_GBs": PEAK_HBM_GBS,
     }
+    # Row-count sweep of both paths (GEMV forced, grouped GEMM forced): the
+    # evidence behind the default row threshold.
+    sweep = {}
+    for T_ in (1, 2, 3, 4, 5, 8):
+        row = {}
+        for name, r in (("gemv", 8), ("gemm", 0)):
+            for lay in layers:
+                lay.set_desc(gemv_max_rows=r)
+            row[name] = round(timed_decode(T_), 2)
+        sweep[str(T_)] = row
+    for lay in layers:
+        lay.set_desc(gemv_max_rows=-1)
 
     rec = {
         "metric": "MoE-layer tok/s @T=4096 prefill; µs/layer @T=1 decode; % HBM/MFMA roofline",
@@ -235,7 +276,8 @@ def main():
                      "traffic": traffic_from_profile(), "flop_per_launch": flop_gateup, "avg_us": g["avg_us"]},
         "kernels_us": dict(kern, **kern_all),
         "down_gemm_tflops": round(down_tf, 2),
-        "decode": {"us_per_layer": round(dec_us, 3), "T": 1, "kernels_us": dkern, "roofline": dec_roof},
+        "decode": {"us_per_layer": round(dec_us, 3), "T": 1, "kernels_us": dkern, "roofline": dec_roof,
+                   "sweep_us_per_layer": sweep, "default_gemv_max_rows": moe.moe_default_gemv_max_rows()},
     }
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, a.cpu_seconds)
