@@ -94,7 +94,7 @@ Blob blob_geom(const moe_layer_desc* d) {
 }
 
 struct Ws {
-  size_t logits, wnorm, xsum, x16, ids, tw, counts, offsets, sorted, inv, tiles, sched, n_tiles, active, n_active,
+  size_t logits, wnorm, xsum, x16, ids, tw, counts, offsets, sorted, inv, tiles, sched, n_tiles, active, n_active, segs,
       hbuf, hsum, obuf;
   size_t total;
 };
@@ -121,6 +121,7 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   w.n_tiles = o; o += al(4);
   w.active = o; o += al(E * 4);
   w.n_active = o; o += al(4);
+  w.segs = o; o += al(2 * ((Tc * k + kSegAssign - 1) / kSegAssign) * E * 4);  // per-segment counts, then bases
   w.hbuf = o; o += al(rows * Im * 2);
   w.hsum = o; o += al(rows * (Im / 32) * 4);
   w.obuf = o; o += al(Tc * k * H * 2);
@@ -245,7 +246,7 @@ LayerArgs layer_args(const moe_layer_desc* d, const void* packed) {
 }
 
 struct RouteOut {
-  int32_t *ids, *counts, *offsets, *sorted, *inv, *tiles, *sched, *n_tiles, *active, *n_active;
+  int32_t *ids, *counts, *offsets, *sorted, *inv, *tiles, *sched, *n_tiles, *active, *n_active, *segs;
   float *tw, *logits, *xsum;
   double* wsq;
   uint16_t* x16;
@@ -256,7 +257,8 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
   const int E = d->n_experts, k = d->top_k, H = d->hidden;
   bool two = false;
   TRY(timed(0, s, "router logits", [&](const KTime& kt) {
-    return launch_route_logits(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.xsum, o.x16, s, &two, kt);
+    return launch_route_logits(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.xsum, o.x16, o.segs, s,
+                               &two, kt);
   }));
   if (!two) {
     // Few tokens: exact logits are already there; top-k + metadata in one launch.
@@ -267,12 +269,12 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
     });
   }
   TRY(timed(1, s, "top-k", [&](const KTime& kt) {
-    return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.x16, s, kt);
+    return launch_route_select(x, T, H, wr, bias, E, k, o.logits, o.wsq, o.ids, o.tw, o.x16, o.segs, s, kt);
   }));
   TRY(timed(2, s, "routing metadata", [&](const KTime& kt) {
     return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, max_long_tiles(d), o.counts,
-                       o.offsets, o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv, o.sched,
-                       reinterpret_cast<int32_t*>(o.logits), s, kt);  // the screened logits are dead by now
+                       o.offsets, o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv, o.sched, o.segs,
+                       true, s, kt);  // segment counts taken by the exact top-k
   }));
   return MOE_OK;
 }
@@ -294,6 +296,7 @@ RouteOut ws_route(void* ws, const Ws& w) {
   o.n_tiles = at<int32_t>(ws, w.n_tiles);
   o.active = at<int32_t>(ws, w.active);
   o.n_active = at<int32_t>(ws, w.n_active);
+  o.segs = at<int32_t>(ws, w.segs);
   return o;
 }
 
@@ -484,7 +487,7 @@ moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, co
   bool two = false;
   TRY(timed(0, s, "router logits", [&](const KTime& kt) {
     return launch_route_logits(x, T, desc->hidden, router_w, logit_bias, desc->n_experts, desc->top_k, o.logits,
-                               o.wsq, o.ids, o.tw, nullptr, nullptr, s, &two, kt);
+                               o.wsq, o.ids, o.tw, nullptr, nullptr, nullptr, s, &two, kt);
   }));
   const ChunkArgs C = chunk_args(desc, x, T, o, ws, w, y);
   TRY(timed(5, s, "top-k + gate/up GEMV", [&](const KTime& kt) {

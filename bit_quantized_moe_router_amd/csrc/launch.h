@@ -11,6 +11,9 @@ namespace moe {
 // with its own start and the last one stamps `stop` with its own end
 // (hipExtLaunchKernel), so the interval holds the kernels and not the
 // dispatch gap before them.  Null events: a plain launch.
+// Assignments per segment of the many-token routing metadata.
+constexpr int kSegAssign = 1024;
+
 struct KTime {
   hipEvent_t start = nullptr, stop = nullptr;
 };
@@ -41,17 +44,18 @@ hipError_t launch_pack(const PackArgs& P, hipStream_t s);
 // *two_launches tells which.
 hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, float* logits, double* wsq, int32_t* ids, float* tw, float* xsum,
-                               uint16_t* x16, hipStream_t s, bool* two_launches, const KTime& kt = KTime{});
+                               uint16_t* x16, int32_t* segcnt, hipStream_t s, bool* two_launches,
+                               const KTime& kt = KTime{});
 // Top-k selection (exact recomputation of the screened candidates for T > 8).
 hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
-                               uint16_t* x16, hipStream_t s, const KTime& kt = KTime{});
+                               uint16_t* x16, int32_t* segcnt, hipStream_t s, const KTime& kt = KTime{});
 // max_long: tiles of more than BM/2 rows that the schedule keeps whole (the
 // rest are cut in two); 0 keeps every tile whole.
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared, int max_long,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
-                       int32_t* sched, int32_t* scratch, hipStream_t s, const KTime& kt = KTime{});
+                       int32_t* sched, int32_t* seg, bool seg_counted, hipStream_t s, const KTime& kt = KTime{});
 // T <= 8: top-k of exact logits and the metadata in one single-workgroup launch.
 hipError_t launch_topk_meta(const float* logits, int T, int E, int k, int32_t* ids, float* tw, int BM,
                             int with_shared, int32_t* counts, int32_t* offsets, int32_t* sorted,

@@ -71,9 +71,13 @@ __host__ __device__ constexpr int route_exact_smem_bytes(int H, int E) { return 
 
 __global__ __launch_bounds__(256) void k_screen(const uint16_t* __restrict__ x, int T, int H,
                                                 const float* __restrict__ wr, int E,
-                                                float* __restrict__ approx, double* __restrict__ wsq) {
+                                                float* __restrict__ approx, double* __restrict__ wsq,
+                                                int32_t* __restrict__ segcnt, int n_segcnt) {
   __shared__ __attribute__((aligned(16))) uint8_t sm[kScrSmem];
   const int tid = threadIdx.x;
+  // The per-segment expert counters that k_route_exact fills start at zero.
+  if (segcnt && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = tid; i < n_segcnt; i += 256) segcnt[i] = 0;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, c32 = lane & 31;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
                                                      const float* __restrict__ approx,
                                                      const double* __restrict__ wsq,
                                                      int32_t* __restrict__ ids, float* __restrict__ tw,
-                                                     uint16_t* __restrict__ x16) {
+                                                     uint16_t* __restrict__ x16, int32_t* __restrict__ segcnt) {
   // One workgroup per token.  LDS: reduction slots, x row, screened logits,
   // candidate experts and their exact logits, selected logits.
   extern __shared__ __attribute__((aligned(16))) uint8_t rsm[];
@@ -382,6 +386,9 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
     if (rank < k) {
       ids[(int64_t)t * k + rank] = ec;
       sel_v[rank] = vc;
+      // Expert histogram of the assignment's segment (the routing metadata's
+      // first step, taken here instead of in a launch of its own).
+      if (segcnt) atomicAdd(&segcnt[(((int64_t)t * k + rank) / kSegAssign) * E + ec], 1);
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -681,7 +688,6 @@ __global__ __launch_bounds__(1024) void k_meta(const int32_t* __restrict__ ids, 
 //  k_meta_scatter: per segment, per-wave bases from the wave counts, then the
 //                  leader-based stable scatter of meta_body's phase 3.
 // ---------------------------------------------------------------------------
-constexpr int kSegAssign = 1024;
 constexpr int kSegWaves = 4;
 constexpr int kSegChunks = kSegAssign / (64 * kSegWaves);  // chunks per wave
 
@@ -822,7 +828,8 @@ __global__ __launch_bounds__(1024) void k_topk_meta(const float* __restrict__ lo
 // ---------------------------------------------------------------------------
 hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, float* logits, double* wsq, int32_t* ids, float* tw, float* xsum,
-                               uint16_t* x16, hipStream_t s, bool* two_launches, const KTime& kt) {
+                               uint16_t* x16, int32_t* segcnt, hipStream_t s, bool* two_launches,
+                               const KTime& kt) {
   if (T == 0) return hipSuccess;
   if (T <= kSmallT) {
     MOE_LAUNCH(k_logits_small, dim3((E + 3) / 4), dim3(256), 0, s, kt.start, kt.stop, x, T, H, wr, bias, E, logits,
@@ -830,26 +837,27 @@ hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr,
     *two_launches = false;
     return hipGetLastError();
   }
+  const int n_segcnt = segcnt ? (T * k + kSegAssign - 1) / kSegAssign * E : 0;
   MOE_LAUNCH(k_screen, dim3((T + 63) / 64, (E + 63) / 64, kScreenSplit), dim3(256), 0, s, kt.start, kt.stop, x, T,
-             H, wr, E, logits, wsq);
+             H, wr, E, logits, wsq, segcnt, n_segcnt);
   *two_launches = true;
   return hipGetLastError();
 }
 
 hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                                int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
-                               uint16_t* x16, hipStream_t s, const KTime& kt) {
+                               uint16_t* x16, int32_t* segcnt, hipStream_t s, const KTime& kt) {
   if (T <= kSmallT) return hipSuccess;  // few tokens: k_topk_meta selects from the exact logits
   const size_t smem = (size_t)route_exact_smem_bytes(H, E);
   MOE_LAUNCH(k_route_exact, dim3(T), dim3(256), smem, s, kt.start, kt.stop, x, T, H, wr, bias, E, k, logits, wsq, ids,
-             tw, x16);
+             tw, x16, segcnt);
   return hipGetLastError();
 }
 
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared, int max_long,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
-                       int32_t* sched, int32_t* scratch, hipStream_t s, const KTime& kt) {
+                       int32_t* sched, int32_t* seg, bool seg_counted, hipStream_t s, const KTime& kt) {
   const int N = T * k;
   const int nseg = (N + kSegAssign - 1) / kSegAssign;
   if (nseg <= 1) {  // one segment: the single-workgroup version
@@ -857,11 +865,11 @@ hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with
                counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
     return hipGetLastError();
   }
-  int32_t* segcnt = scratch;
-  int32_t* segbase = scratch + (size_t)nseg * E;
-  MOE_LAUNCH(k_meta_count, dim3(nseg), dim3(256), 0, s, kt.start, nullptr, ids, N, E, segcnt);
-  k_meta_scan<<<dim3(1), dim3(1024), 0, s>>>(T, k, E, BM, with_shared, max_long, nseg, segcnt, segbase, counts, offsets,
-                                              tiles, n_tiles, active, n_active, sched);
+  int32_t* segcnt = seg;
+  int32_t* segbase = seg + (size_t)nseg * E;
+  if (!seg_counted) MOE_LAUNCH(k_meta_count, dim3(nseg), dim3(256), 0, s, kt.start, nullptr, ids, N, E, segcnt);
+  MOE_LAUNCH(k_meta_scan, dim3(1), dim3(1024), 0, s, seg_counted ? kt.start : nullptr, nullptr, T, k, E, BM,
+             with_shared, max_long, nseg, segcnt, segbase, counts, offsets, tiles, n_tiles, active, n_active, sched);
   MOE_LAUNCH(k_meta_scatter, dim3(nseg), dim3(256), 0, s, nullptr, kt.stop, ids, N, E, segbase, sorted, inv);
   return hipGetLastError();
 }
