@@ -156,13 +156,13 @@ moe_status check_device() {
   return MOE_OK;
 }
 
-// Long tiles the schedule keeps whole: one gate/up workgroup per compute unit
-// (after check_device on the current device).
+// Long tiles the schedule keeps whole: one round of gate/up workgroups over
+// the device (after check_device on the current device).
 int max_long_tiles(const moe_layer_desc* d) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   std::lock_guard<std::mutex> lk(g_dev_mu);
-  return g_dev_cus[dev] / gateup_col_tiles(d->inter, d->shared_inter);
+  return g_dev_cus[dev] * gemm_wgs_per_cu() / gateup_col_tiles(d->inter, d->shared_inter);
 }
 
 // ---- kernel timing (measurement mode) ----------------------------------------

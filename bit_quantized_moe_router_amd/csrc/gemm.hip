@@ -5,8 +5,9 @@
 //   gate/up: per tile of routed rows, h = silu(x Wg^T) * (x Wu^T)
 //   down:    y[token] += routing weight * (h Wd^T), the shared expert with 1
 //
-// Workgroup = 8 waves (two per SIMD) over a tile of up to 128 rows of one
-// expert.  Each wave owns 2 weight blocks of 32 columns (gate/up: one block
+// Workgroup = 4 waves (one per SIMD) over a tile of up to 128 rows of one
+// expert; two workgroups share a compute unit, so one's prologue and
+// epilogue run under the other's MFMAs.  Each wave owns 2 weight blocks of 32 columns (gate/up: one block
 // of gate and the same block of up; down: 2 output blocks) and all rows of
 // the tile: up to 4 x 2 accumulators of v_mfma_f32_32x32x16_f16 (fp32).  The
 // kernel is instantiated per number of 32-row fragments the tile needs
@@ -22,7 +23,8 @@
 // Activations (gathered token rows for gate/up, the expert's contiguous rows
 // of the intermediate for down) are shared by the 8 waves through LDS: per K
 // group the workgroup stages 128 rows x 64 columns (double buffered, one
-// barrier per group); the loads run three groups ahead.  Rows past the tile's
+// barrier per group); each thread moves four 16-byte pieces, loaded one group
+// ahead into one register set.  Rows past the tile's
 // count reuse a valid row and are never stored.
 //
 // Results leave through LDS: the workgroup's output tile is assembled there
@@ -51,7 +53,7 @@
 namespace moe {
 
 constexpr int kTileRows = 128;                 // largest tile the kernel takes
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;                      // two workgroups per compute unit
 constexpr int kARow = 144;                     // bytes per A row in LDS: 64 fp16 + 16 B pad
 constexpr int kABufBytes = kTileRows * kARow;  // one K group of A rows
 constexpr int kSmemMain = 2 * kABufBytes + kTileRows * 4;  // + token per row
@@ -162,15 +164,17 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   }
 
   // ---- A staging: thread t moves 16-byte part t%8 of rows t/8 and t/8 + 64 ----
-  const int apart = tid & 7, arow0 = tid >> 3;
-  const uint16_t *asrc0, *asrc1;
+  const int apart = tid & 7, arow0 = tid >> 3;   // rows arow0 + 32 j, j < 4
+  const uint16_t *asrc0, *asrc1, *asrc2, *asrc3;
   {
     auto rowptr = [&](int r) {
       const int rr = r < T.rows ? r : T.rows - 1;
       return (kGateUp ? C.x16 + (int64_t)tok[rr] * H : C.hbuf + (int64_t)(T.rowbase + rr) * C.Imax) + apart * 8;
     };
     asrc0 = rowptr(arow0);
-    asrc1 = rowptr(arow0 + 64);
+    asrc1 = rowptr(arow0 + 32);
+    asrc2 = rowptr(arow0 + 64);
+    asrc3 = rowptr(arow0 + 96);
   }
   uint8_t* const adst = at + apart * 16 + arow0 * kARow;
   // Rows of fragments the tile does not use are not staged.
@@ -178,13 +182,17 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   do {                                                                        \
     const int gg_ = (g) < G ? (g) : G - 1; /* past the end: a valid, unused group */ \
     S##0 = *reinterpret_cast<const uint4*>(asrc0 + gg_ * kGroup);            \
-    if (NF > 2) S##1 = *reinterpret_cast<const uint4*>(asrc1 + gg_ * kGroup); \
+    if (NF > 1) S##1 = *reinterpret_cast<const uint4*>(asrc1 + gg_ * kGroup); \
+    if (NF > 2) S##2 = *reinterpret_cast<const uint4*>(asrc2 + gg_ * kGroup); \
+    if (NF > 3) S##3 = *reinterpret_cast<const uint4*>(asrc3 + gg_ * kGroup); \
   } while (0)
 #define MOE_STORE_A(buf, S)                                                   \
   do {                                                                        \
     uint8_t* d_ = adst + (buf) * kABufBytes;                                  \
     *reinterpret_cast<uint4*>(d_) = S##0;                                     \
-    if (NF > 2) *reinterpret_cast<uint4*>(d_ + 64 * kARow) = S##1;            \
+    if (NF > 1) *reinterpret_cast<uint4*>(d_ + 32 * kARow) = S##1;            \
+    if (NF > 2) *reinterpret_cast<uint4*>(d_ + 64 * kARow) = S##2;            \
+    if (NF > 3) *reinterpret_cast<uint4*>(d_ + 96 * kARow) = S##3;            \
   } while (0)
 
   f32x16_t acc[NF][2];
@@ -254,25 +262,21 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
 #define MOE_GEMM_STEP(g, CUR, Q, QN, AS)                     \
   do {                                                       \
     if (wave_cols) compute(CUR, Q, QN, (g) < G, (g) + 1 < G);  \
-    MOE_STORE_A((CUR) ^ 1, AS);               \
-    MOE_LOAD_A((g) + 3, AS);                  \
+    MOE_STORE_A((CUR) ^ 1, as);               \
+    MOE_LOAD_A((g) + 2, as);                  \
     load_q((g) + 4, Q);                       \
     __syncthreads();                          \
   } while (0)
 
-  uint4 ae0 = make_uint4(0, 0, 0, 0), ae1 = ae0;
-  uint4 ao0 = ae0, ao1 = ae0;
-  // Prologue: the loads go out in the order of the steady state (A of j+3,
-  // then codes of j+4, for j = -3..-1) so that the loads in flight at the
-  // loop header line up with those at the back edge and the compiler's
-  // counts of loads to wait for are the steady-state ones.
-  MOE_LOAD_A(0, ae);
+  uint4 as0 = make_uint4(0, 0, 0, 0), as1 = as0, as2 = as0, as3 = as0;
+  // Prologue: A of group 0 into LDS, A of group 1 in registers, codes of
+  // groups 1..3 in flight.
+  MOE_LOAD_A(0, as);
   load_q(1, q1);
-  MOE_LOAD_A(1, ao);
   load_q(2, q2);
-  MOE_STORE_A(0, ae);
-  MOE_LOAD_A(2, ae);
   load_q(3, q3);
+  MOE_STORE_A(0, as);
+  MOE_LOAD_A(1, as);
   if (wave_cols) {
     f16x2v_t s20, b20, s21, b21;
     sbpair(q0.s0, true, s20, b20);
@@ -422,6 +426,8 @@ __global__ __launch_bounds__(256) void k_combine(LayerArgs L, ChunkArgs C) {
 }
 
 // ---------------------------------------------------------------------------
+int gemm_wgs_per_cu() { return 8 / kWaves; }  // 8 waves, two per SIMD, per compute unit
+
 int gateup_col_tiles(int I, int Is) {
   const int Imax = I > Is ? I : Is;
   return (Imax + kGateUpColsPerWg - 1) / kGateUpColsPerWg;

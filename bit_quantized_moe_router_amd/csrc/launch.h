@@ -68,6 +68,8 @@ hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sche
                             const KTime& kt = KTime{});
 // Gate/up column tiles per row tile (the GEMM grid's second dimension).
 int gateup_col_tiles(int I, int Is);
+// Grouped-GEMM workgroups resident per compute unit.
+int gemm_wgs_per_cu();
 // y[t] += sum_j w_tj * routed output of assignment (t, j) (GEMM path).
 hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
 // Decode GEMV path: top-k of the exact logits (and the chunk's routing tables)
