@@ -33,7 +33,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 }
 
 constexpr int kDefaultTileRows = 128;
-constexpr int kDefaultGemvMaxRows = 5;  // measured crossover: GEMV faster for T <= 5, GEMM at T = 8
+constexpr int kDefaultGemvMaxRows = 4;  // measured crossover: GEMV faster for T <= 4, grouped GEMM from T = 5
 constexpr int kMaxRowsDecode = 8;
 
 moe_status validate_desc(const moe_layer_desc* d) {
