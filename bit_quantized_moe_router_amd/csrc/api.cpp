@@ -121,7 +121,7 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   w.n_tiles = o; o += al(4);
   w.active = o; o += al(E * 4);
   w.n_active = o; o += al(4);
-  w.segs = o; o += al(2 * ((Tc * k + kSegAssign - 1) / kSegAssign) * E * 4);  // per-segment counts, then bases
+  w.segs = o; o += al(((Tc * k + kSegAssign - 1) / kSegAssign) * E * 4);  // per-segment expert counts
   w.hbuf = o; o += al(rows * Im * 2);
   w.hsum = o; o += al(rows * (Im / 32) * 4);
   w.obuf = o; o += al(Tc * k * H * 2);
@@ -274,7 +274,7 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
   TRY(timed(2, s, "routing metadata", [&](const KTime& kt) {
     return launch_meta(o.ids, T, k, E, tile_rows(d), d->shared_inter > 0 ? 1 : 0, max_long_tiles(d), o.counts,
                        o.offsets, o.sorted, o.tiles, o.n_tiles, o.active, o.n_active, o.inv, o.sched, o.segs,
-                       true, s, kt);  // segment counts taken by the exact top-k
+                       s, kt);  // segment counts taken by the exact top-k
   }));
   return MOE_OK;
 }

@@ -51,11 +51,13 @@ hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr,
                                int k, const float* logits, const double* wsq, int32_t* ids, float* tw,
                                uint16_t* x16, int32_t* segcnt, hipStream_t s, const KTime& kt = KTime{});
 // max_long: tiles of more than BM/2 rows that the schedule keeps whole (the
-// rest are cut in two); 0 keeps every tile whole.
+// rest are cut in two); 0 keeps every tile whole.  segcnt: per-segment expert
+// counts of the assignments (kSegAssign ids a segment), taken by the exact
+// top-k; used when there is more than one segment.
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared, int max_long,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
-                       int32_t* sched, int32_t* seg, bool seg_counted, hipStream_t s, const KTime& kt = KTime{});
+                       int32_t* sched, const int32_t* segcnt, hipStream_t s, const KTime& kt = KTime{});
 // T <= 8: top-k of exact logits and the metadata in one single-workgroup launch.
 hipError_t launch_topk_meta(const float* logits, int T, int E, int k, int32_t* ids, float* tw, int BM,
                             int with_shared, int32_t* counts, int32_t* offsets, int32_t* sorted,

@@ -425,7 +425,7 @@ constexpr int kMetaBatch = 8;   // chunks per wave whose ids are loaded together
 // holds tot for expert e; every thread of the 1024-thread workgroup calls
 // this): counts, offsets, active list, tile map and execution schedule.
 // Returns thread e's offset (its expert's first sorted position).
-__device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_shared, int max_long,
+__device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_shared, int max_long, bool out,
                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                int32_t* __restrict__ active, int32_t* __restrict__ n_active,
@@ -467,9 +467,10 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
   __syncthreads();
   const int routed_tiles = s_incl[1][E - 1];
   int my_off = 0;
+  if (tid < E) my_off = s_incl[0][tid] - tot;
+  if (!out) return my_off;  // workgroup-uniform: offsets only, nothing written
   if (tid < E) {
-    const int off_e = s_incl[0][tid] - tot;
-    my_off = off_e;
+    const int off_e = my_off;
     counts[tid] = tot;
     offsets[tid] = off_e;
     if (tid == E - 1) offsets[E] = s_incl[0][tid];
@@ -618,7 +619,7 @@ __device__ void meta_body(const int32_t* __restrict__ ids, int T, int k, int E, 
   int tot = 0;
   if (tid < E)
     for (int w = 0; w < kMetaWaves; w++) tot += cnt[w * E + tid];
-  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, counts, offsets, tiles, n_tiles, active,
+  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, true, counts, offsets, tiles, n_tiles, active,
                                     n_active, sched);
   if (tid < E) {
     int run = off_e;
@@ -679,125 +680,77 @@ __global__ __launch_bounds__(1024) void k_meta(const int32_t* __restrict__ ids, 
 
 // ---------------------------------------------------------------------------
 // Routing metadata for many tokens: the same computation spread over
-// workgroups.  The flat assignment range is cut into segments of
-// kSegAssign ids (one workgroup each, 4 waves x 4 chunks of 64).
-//  k_meta_count:   per-segment expert counts -> segcnt[seg][E];
-//  k_meta_scan:    one workgroup: totals, the scans and tiles of
-//                  meta_scan_tiles, and per-(segment, expert) bases
-//                  segbase[seg][e] = offset[e] + counts of e in earlier segments;
-//  k_meta_scatter: per segment, per-wave bases from the wave counts, then the
-//                  leader-based stable scatter of meta_body's phase 3.
+// workgroups.  The flat assignment range is cut into segments of kSegAssign
+// ids, one 1024-thread workgroup each (16 waves x one chunk of 64).  The
+// per-(segment, expert) counts segcnt[seg][E] are already there (taken by the
+// exact top-k).  Every workgroup
+//  * sums the counts per expert and takes the expert offsets (the scans of
+//    meta_scan_tiles; workgroup 0 also writes counts, offsets, the active
+//    list, the tile map and the schedule);
+//  * bases its segment's experts at offset[e] + counts of e in earlier
+//    segments, then per wave from the wave counts;
+//  * scatters its segment stably with the leader atomics of meta_body.
 // ---------------------------------------------------------------------------
-constexpr int kSegWaves = 4;
-constexpr int kSegChunks = kSegAssign / (64 * kSegWaves);  // chunks per wave
+constexpr int kSegWaves = kSegAssign / 64;  // one chunk of 64 per wave
 
-__global__ __launch_bounds__(256) void k_meta_count(const int32_t* __restrict__ ids, int N, int E,
-                                                    int32_t* __restrict__ segcnt) {
-  __shared__ int c[kMaxE];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) c[e] = 0;
-  __syncthreads();
-  const int a0 = blockIdx.x * kSegAssign;
-  int ev[kSegAssign / 256];
-#pragma unroll
-  for (int i = 0; i < kSegAssign / 256; i++) {
-    const int a = a0 + tid + 256 * i;
-    ev[i] = a < N ? ids[a] : -1;
-  }
-#pragma unroll
-  for (int i = 0; i < kSegAssign / 256; i++)
-    if (ev[i] >= 0) atomicAdd(&c[ev[i]], 1);
-  __syncthreads();
-  for (int e = tid; e < E; e += 256) segcnt[(int64_t)blockIdx.x * E + e] = c[e];
-}
-
-__global__ __launch_bounds__(1024) void k_meta_scan(int T, int k, int E, int BM, int with_shared, int max_long,
-                                                    int nseg,
-                                                    const int32_t* __restrict__ segcnt,
-                                                    int32_t* __restrict__ segbase, int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
-                                                    int32_t* __restrict__ n_tiles, int32_t* __restrict__ active,
-                                                    int32_t* __restrict__ n_active, int32_t* __restrict__ sched) {
-  // Segment counts are read kScanBatch at a time (independent loads), not
-  // one dependent load per segment.
+__global__ __launch_bounds__(1024) void k_meta_segments(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                        int BM, int with_shared, int max_long, int nseg,
+                                                        const int32_t* __restrict__ segcnt,
+                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
+                                                        int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+                                                        int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                                        int32_t* __restrict__ sched) {
+  // Segment counts are read kScanBatch at a time (independent loads).
   constexpr int kScanBatch = 16;
-  const int tid = threadIdx.x;
-  int tot = 0;
+  __shared__ int wc[kSegWaves][kMaxE];  // per-wave counts, then per-wave bases
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int seg = blockIdx.x, N = T * k;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // The segment's ids go out first.
+  const int a = seg * kSegAssign + tid;
+  const int ev = a < N ? ids[a] : -1;
+  int tot = 0, pre = 0;
   if (tid < E) {
-    for (int g0 = 0; g0 < nseg; g0 += kScanBatch) {
-      int v[kScanBatch];
-#pragma unroll
-      for (int i = 0; i < kScanBatch; i++) v[i] = g0 + i < nseg ? segcnt[(int64_t)(g0 + i) * E + tid] : 0;
-#pragma unroll
-      for (int i = 0; i < kScanBatch; i++) tot += v[i];
-    }
-  }
-  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, counts, offsets, tiles, n_tiles, active,
-                                    n_active, sched);
-  if (tid < E) {
-    int run = off_e;
     for (int g0 = 0; g0 < nseg; g0 += kScanBatch) {
       int v[kScanBatch];
 #pragma unroll
       for (int i = 0; i < kScanBatch; i++) v[i] = g0 + i < nseg ? segcnt[(int64_t)(g0 + i) * E + tid] : 0;
 #pragma unroll
       for (int i = 0; i < kScanBatch; i++) {
-        if (g0 + i < nseg) segbase[(int64_t)(g0 + i) * E + tid] = run;
-        run += v[i];
+        tot += v[i];
+        pre += g0 + i < seg ? v[i] : 0;
       }
     }
   }
-}
-
-__global__ __launch_bounds__(256) void k_meta_scatter(const int32_t* __restrict__ ids, int N, int E,
-                                                      const int32_t* __restrict__ segbase,
-                                                      int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
-  __shared__ int wc[kSegWaves][kMaxE];  // per-wave counts, then per-wave bases
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i = tid; i < kSegWaves * E; i += 256) (&wc[0][0])[(i / E) * kMaxE + i % E] = 0;
-  const int a0 = blockIdx.x * kSegAssign + wave * (64 * kSegChunks);
-  int ev[kSegChunks];
-#pragma unroll
-  for (int i = 0; i < kSegChunks; i++) {
-    const int a = a0 + 64 * i + lane;
-    ev[i] = a < N ? ids[a] : -1;
-  }
+  for (int i = tid; i < kSegWaves * E; i += blockDim.x) wc[i / E][i % E] = 0;
+  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, seg == 0, counts, offsets, tiles,
+                                    n_tiles, active, n_active, sched);
+  // (meta_scan_tiles ends with a barrier: wc is cleared.)
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kSegChunks; i++)
-    if (ev[i] >= 0) atomicAdd(&wc[wave][ev[i]], 1);
+  if (ev >= 0) atomicAdd(&wc[wave][ev], 1);
   __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    int run = segbase[(int64_t)blockIdx.x * E + e];
+  if (tid < E) {
+    int run = off_e + pre;
 #pragma unroll
     for (int w = 0; w < kSegWaves; w++) {
-      const int c = wc[w][e];
-      wc[w][e] = run;
+      const int c = wc[w][tid];
+      wc[w][tid] = run;
       run += c;
     }
   }
   __syncthreads();
-  int rk[kSegChunks], ld[kSegChunks], bs[kSegChunks];
-#pragma unroll
-  for (int i = 0; i < kSegChunks; i++) {
-    const bool valid = ev[i] >= 0;
-    const uint64_t m = match_mask(valid ? ev[i] : 0, valid, nbits);
-    rk[i] = __popcll(m & lt_mask);
-    ld[i] = m ? __ffsll((unsigned long long)m) - 1 : 0;
-    bs[i] = 0;
-    if (valid && rk[i] == 0) bs[i] = atomicAdd(&wc[wave][ev[i]], __popcll(m));
-  }
-#pragma unroll
-  for (int i = 0; i < kSegChunks; i++) {
-    const int base = __shfl(bs[i], ld[i]);
-    if (ev[i] >= 0) {
-      const int a = a0 + 64 * i + lane;
-      const int pos = base + rk[i];
-      sorted[pos] = a;
-      if (inv) inv[a] = pos;
-    }
+  const uint64_t m = match_mask(ev >= 0 ? ev : 0, ev >= 0, nbits);
+  const int rk = __popcll(m & lt_mask);
+  const int ld = m ? __ffsll((unsigned long long)m) - 1 : 0;
+  int bs = 0;
+  if (ev >= 0 && rk == 0) bs = atomicAdd(&wc[wave][ev], __popcll(m));
+  const int base = __shfl(bs, ld);
+  if (ev >= 0) {
+    const int pos = base + rk;
+    sorted[pos] = a;
+    if (inv) inv[a] = pos;
   }
 }
 
@@ -857,20 +810,16 @@ hipError_t launch_route_select(const uint16_t* x, int T, int H, const float* wr,
 hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with_shared, int max_long,
                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* tiles,
                        int32_t* n_tiles, int32_t* active, int32_t* n_active, int32_t* inv,
-                       int32_t* sched, int32_t* seg, bool seg_counted, hipStream_t s, const KTime& kt) {
+                       int32_t* sched, const int32_t* segcnt, hipStream_t s, const KTime& kt) {
   const int N = T * k;
   const int nseg = (N + kSegAssign - 1) / kSegAssign;
-  if (nseg <= 1) {  // one segment: the single-workgroup version
+  if (nseg <= 1) {  // one segment: the single-workgroup version (counts its own histogram)
     MOE_LAUNCH(k_meta, dim3(1), dim3(1024), 0, s, kt.start, kt.stop, ids, T, k, E, BM, with_shared, max_long,
                counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
     return hipGetLastError();
   }
-  int32_t* segcnt = seg;
-  int32_t* segbase = seg + (size_t)nseg * E;
-  if (!seg_counted) MOE_LAUNCH(k_meta_count, dim3(nseg), dim3(256), 0, s, kt.start, nullptr, ids, N, E, segcnt);
-  MOE_LAUNCH(k_meta_scan, dim3(1), dim3(1024), 0, s, seg_counted ? kt.start : nullptr, nullptr, T, k, E, BM,
-             with_shared, max_long, nseg, segcnt, segbase, counts, offsets, tiles, n_tiles, active, n_active, sched);
-  MOE_LAUNCH(k_meta_scatter, dim3(nseg), dim3(256), 0, s, nullptr, kt.stop, ids, N, E, segbase, sorted, inv);
+  MOE_LAUNCH(k_meta_segments, dim3(nseg), dim3(kSegAssign), 0, s, kt.start, kt.stop, ids, T, k, E, BM, with_shared,
+             max_long, nseg, segcnt, counts, offsets, sorted, inv, tiles, n_tiles, active, n_active, sched);
   return hipGetLastError();
 }
 
