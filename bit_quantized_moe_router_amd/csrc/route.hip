@@ -316,18 +316,7 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
     }
     // Lower bound of the k-th largest screened logit: the k-th largest of the
     // lanes' maxima (those are k distinct logits, all at least that large).
-    // Bitonic sort of the 64 lane maxima, descending.
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const float o = __shfl_xor(m, stride);
-        const bool desc = (lane & size) == 0 || size == 64;
-        const bool upper = (lane & stride) != 0;
-        m = (desc != upper) ? fmaxf(m, o) : fminf(m, o);
-      }
-    }
-    const float ak = __shfl(m, k - 1);
+    const float ak = wave_kth_largest(m, k);
     const int G = H / kGroup;
     const double n_round = 128.0 * (double)((G + kScreenSplit - 1) / kScreenSplit);
     const double c1 = 7.62939453125e-06 + (n_round + 32.0) * 5.9604644775390625e-08 + 1.1920928955078125e-07;
@@ -379,9 +368,17 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
     const float vc = cand_v[c];
     const int ec = cand_e[c];
     int rank = 0;
-    for (int c2 = 0; c2 < C; c2++) {
-      const float v2 = cand_v[c2];
-      rank += (v2 > vc || (v2 == vc && cand_e[c2] < ec)) ? 1 : 0;
+    if (C <= 64) {  // every candidate in a lane: the others broadcast with v_readlane
+      for (int c2 = 0; c2 < C; c2++) {
+        const float v2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vc), c2));
+        const int e2 = __builtin_amdgcn_readlane(ec, c2);
+        rank += (v2 > vc || (v2 == vc && e2 < ec)) ? 1 : 0;
+      }
+    } else {
+      for (int c2 = 0; c2 < C; c2++) {
+        const float v2 = cand_v[c2];
+        rank += (v2 > vc || (v2 == vc && cand_e[c2] < ec)) ? 1 : 0;
+      }
     }
     if (rank < k) {
       ids[(int64_t)t * k + rank] = ec;

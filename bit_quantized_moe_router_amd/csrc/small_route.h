@@ -27,6 +27,23 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// k-th largest of the 64 lanes' values m (k <= 64; -inf for lanes without
+// one), by a radix select over order-preserving integer keys: from the top
+// bit down, keep the bit set if at least k lanes are at or above the prefix
+// with it.  One ballot per bit, no cross-lane data movement.
+__device__ __forceinline__ float wave_kth_largest(float m, int k) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, m);
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; b--) {
+    const uint32_t c = t | (1u << b);
+    if (__popcll(__ballot(key >= c)) >= k) t = c;
+  }
+  const uint32_t v = (t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t;
+  return __builtin_bit_cast(float, v);
+}
+
 // Lanes of this wave that are valid and hold the same expert e.
 __device__ __forceinline__ uint64_t match_mask(int e, bool valid, int nbits) {
   uint64_t m = __ballot(valid);
@@ -109,9 +126,10 @@ __device__ __forceinline__ void group_sums(const uint16_t* __restrict__ x, int T
 }
 
 // Top-k of one token's exact logits, one wave: the k-th largest of the lanes'
-// maxima is a threshold at most the k-th largest logit; the logits at or
-// above it are listed and ranked exactly (larger first, equal logits towards
-// the lower expert), then the softmax over the k selected.  lds: 2 E + 16 ints.
+// maxima (k distinct logits at least that large) is a threshold at most the
+// k-th largest logit; the logits at or above it are listed and ranked exactly
+// (larger first, equal logits towards the lower expert), then the softmax
+// over the k selected.  lds: 2 E + 16 ints.
 __device__ __forceinline__ void topk_small(const float* __restrict__ l, int E, int k, int t,
                                            int32_t* __restrict__ ids, float* __restrict__ tw, int* lds) {
   const int lane = threadIdx.x & 63;
@@ -126,17 +144,7 @@ __device__ __forceinline__ void topk_small(const float* __restrict__ l, int E, i
     v[j] = e < E ? l[e] : -INFINITY;
     m = fmaxf(m, v[j]);
   }
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const float o = __shfl_xor(m, stride);
-      const bool desc = (lane & size) == 0 || size == 64;
-      const bool upper = (lane & stride) != 0;
-      m = (desc != upper) ? fmaxf(m, o) : fminf(m, o);
-    }
-  }
-  const float thr = __shfl(m, k - 1);
+  const float thr = wave_kth_largest(m, k);
   int C = 0;
 #pragma unroll
   for (int j = 0; j < kMaxEPerLane; j++) {
