@@ -179,16 +179,20 @@ const char *moe_status_str(moe_status s);
 const char *moe_last_error(void);
 
 /*
- * Kernel timing for measurement tools.  moe_profile_enable(mask) makes the
- * library record a HIP event pair, on the launch stream, around every launch
- * of the kernels whose bit is set in `mask` (bit i = kernel id i; 0 turns
- * timing off).  moe_profile_read synchronises on those events and returns the
- * summed duration (ms) and launch count of kernel `kernel_id` since the last
- * reset.  Never needed on the forward path.  Not thread-safe.
+ * Kernel timing for measurement tools.  moe_profile_enable(mask) makes every
+ * launch of the kernels whose bit is set in `mask` (bit i = kernel id i; 0
+ * turns timing off) stamp a HIP event pair on the launch stream: the first
+ * kernel of the step stamps its own start and the last its own end
+ * (hipExtLaunchKernel).  A stamped launch costs a few microseconds more than
+ * a plain one, so time whole steps with timing off.  moe_profile_read
+ * synchronises on those events and returns the summed duration (ms) and
+ * launch count of kernel `kernel_id` since the last reset.  Never needed on
+ * the forward path.  Not thread-safe.
  *   0 = router logits (screen, or exact for T <= 8), 1 = exact top-k
- *   selection (T > 8), 2 = routing metadata (with top-k for T <= 8),
- *   3 = gate/up grouped GEMM, 4 = down grouped GEMM, 5 = gate/up GEMV,
- *   6 = down GEMV, 7 = per-token combine of the grouped-GEMM path
+ *   selection (T > 8), 2 = routing metadata (with top-k for T <= 8 outside
+ *   the decode GEMV path), 3 = gate/up grouped GEMM, 4 = down grouped GEMM,
+ *   5 = top-k + gate/up GEMV (decode GEMV path), 6 = down GEMV, 7 = per-token
+ *   combine of the grouped-GEMM path
  */
 moe_status moe_profile_enable(int32_t mask);
 moe_status moe_profile_reset(void);
