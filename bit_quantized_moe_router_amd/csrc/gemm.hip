@@ -437,13 +437,9 @@ template <bool kGateUp>
 static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
                                      const KTime& kt) {
   constexpr int smem = kGateUp ? kSmemGateUp : kSmemDown;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm<kGateUp>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_expert_gemm<kGateUp>), smem, lds_set);
+  if (e != hipSuccess) return e;
   const int n_ct = kGateUp ? gateup_col_tiles(L.I, L.Is) : (L.H + kDownColsPerWg - 1) / kDownColsPerWg;
   const int tiles8 = (max_sched + 7) / 8 * 8;
   MOE_LAUNCH(k_expert_gemm<kGateUp>, dim3((unsigned)(tiles8 * n_ct)), dim3(kWaves * 64), smem, s, kt.start, kt.stop,

@@ -437,13 +437,10 @@ hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, const floa
   const int Imax = L.I > L.Is ? L.I : L.Is;
   const int slots = (L.E < C.Tk ? L.E : C.Tk) + 1;
   dim3 grid(slots + 1, Imax / 32);  // + the metadata workgroup
-  static bool attr_set = false;
-  if (!attr_set) {  // rows T * H * 2 <= 64 KB on this path, lists <= 8 * 1040 * 4, beside ~26 KB of static LDS
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_gateup),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kGuSmemMax);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // rows T * H * 2 <= 64 KB on this path, lists <= 8 * 1040 * 4, beside ~22 KB of static LDS
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_gemv_gateup), kGuSmemMax, lds_set);
+  if (e != hipSuccess) return e;
   const size_t smem = (size_t)C.T * L.H * 2 + (size_t)C.T * (2 * L.E + 16) * 4;
   if (smem > (size_t)kGuSmemMax || C.T > kGemvMaxRows || C.Tk > kMaxAssign) return hipErrorInvalidValue;
   MOE_LAUNCH(k_gemv_gateup, grid, dim3(kGuWaves * 64), smem, s, kt.start, kt.stop, L, C, logits, BM, with_shared);
@@ -451,13 +448,9 @@ hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, const floa
 }
 
 hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_down),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kDnStageMax);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_gemv_down), kDnStageMax, lds_set);
+  if (e != hipSuccess) return e;
   const size_t rows = (size_t)C.Tk + C.T;
   const size_t stage = rows * C.Imax * 2 + rows * (C.Imax / 32) * 4;
   const int staged = stage <= (size_t)kDnStageMax ? 1 : 0;

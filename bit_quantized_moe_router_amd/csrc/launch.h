@@ -3,6 +3,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "common.h"
 
 namespace moe {
@@ -11,6 +13,21 @@ namespace moe {
 // with its own start and the last one stamps `stop` with its own end
 // (hipExtLaunchKernel), so the interval holds the kernels and not the
 // dispatch gap before them.  Null events: a plain launch.
+// A kernel's dynamic-LDS limit (needed above 64 KB), set once per device on
+// the current device; `done` holds one bit per device.
+inline hipError_t lds_limit_once(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  done.fetch_or(bit, std::memory_order_acq_rel);
+  return hipSuccess;
+}
+
 // Assignments per segment of the many-token routing metadata.
 constexpr int kSegAssign = 1024;
 
