@@ -221,10 +221,12 @@ def main():
     dkern = breakdown(lambda: decode_run(a.decode_steps), [moe.K_LOGITS, moe.K_META, moe.K_GATEUP_GEMV,
                                                            moe.K_DOWN_GEMV])
     blk = 1152
-    gu_bytes = 9 * (I // 32) * (H // 64) * 2 * blk          # 8 routed + shared, gate and up, packed
-    dn_bytes = 9 * (H // 32) * (I // 64) * blk
-    gemv_gu = dkern.get("k_gemv_gateup")
-    gemv_dn = dkern.get("k_gemv_down")
+    # The experts kernel streams gate/up and down of the 8 routed experts and
+    # the shared one; the reduce kernel reads the partial output rows.
+    ex_bytes = 9 * ((I // 32) * (H // 64) * 2 + (H // 32) * (I // 64)) * blk
+    red_bytes = (k + 1) * (I // 32) * H * 4 + H * 4
+    gemv_ex = dkern.get("k_gemv_experts")
+    gemv_red = dkern.get("k_gemv_reduce")
 
     # Reference for "achievable" at these sizes: a device-to-device copy of the
     # same number of bytes (read + write counted), over rotating buffers.
@@ -244,18 +246,19 @@ def main():
         return round(2 * n * 2 / (c0.elapsed_time(c1) / 200 * 1e-3) / 1e9, 1)
 
     dec_roof = {
-        "gateup_gemv_bytes": gu_bytes,
-        "gateup_gemv_GBs": round(gu_bytes / (gemv_gu["avg_us"] * 1e-6) / 1e9, 1) if gemv_gu else None,
-        "down_gemv_bytes": dn_bytes,
-        "down_gemv_GBs": round(dn_bytes / (gemv_dn["avg_us"] * 1e-6) / 1e9, 1) if gemv_dn else None,
-        "copy_GBs_same_bytes_gateup": copy_gbs(gu_bytes),
-        "copy_GBs_same_bytes_down": copy_gbs(dn_bytes),
+        "experts_gemv_bytes": ex_bytes,
+        "experts_gemv_GBs": round(ex_bytes / (gemv_ex["avg_us"] * 1e-6) / 1e9, 1) if gemv_ex else None,
+        "reduce_bytes": red_bytes,
+        "reduce_GBs": round(red_bytes / (gemv_red["avg_us"] * 1e-6) / 1e9, 1) if gemv_red else None,
+        "copy_GBs_same_bytes_experts": copy_gbs(ex_bytes),
+        "layer_bytes": ex_bytes + 4 * E * H + red_bytes + 2 * H,
+        "layer_GBs": round((ex_bytes + 4 * E * H + red_bytes + 2 * H) / (dec_us * 1e-6) / 1e9, 1),
         "peak_GBs": PEAK_HBM_GBS,
     }
     # Row-count sweep of both paths (GEMV forced, grouped GEMM forced): the
     # evidence behind the default row threshold.
     sweep = {}
-    for T_ in (1, 2, 3, 4, 5, 8):
+    for T_ in (1, 2, 3, 4, 5, 6, 7, 8):
         row = {}
         for name, r in (("gemv", 8), ("gemm", 0)):
             for lay in layers:

@@ -20,7 +20,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED_SH
 K_LOGITS, K_TOPK, K_META, K_GATEUP_GEMM, K_DOWN_GEMM, K_GATEUP_GEMV, K_DOWN_GEMV, K_COMBINE = range(8)
 KERNEL_NAMES = {K_LOGITS: "k_screen|k_logits_small", K_TOPK: "k_route_exact", K_META: "k_meta|k_topk_meta",
                 K_GATEUP_GEMM: "k_gateup_gemm", K_DOWN_GEMM: "k_down_gemm",
-                K_GATEUP_GEMV: "k_gemv_gateup", K_DOWN_GEMV: "k_gemv_down", K_COMBINE: "k_combine"}
+                K_GATEUP_GEMV: "k_gemv_experts", K_DOWN_GEMV: "k_gemv_reduce", K_COMBINE: "k_combine"}
 
 
 class MoEError(RuntimeError):

@@ -33,7 +33,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 }
 
 constexpr int kDefaultTileRows = 128;
-constexpr int kDefaultGemvMaxRows = 4;  // measured crossover: GEMV faster for T <= 4, grouped GEMM from T = 5
+constexpr int kDefaultGemvMaxRows = 6;  // measured crossover: GEMV faster for T <= 6, grouped GEMM from T = 7
 constexpr int kMaxRowsDecode = 8;
 
 moe_status validate_desc(const moe_layer_desc* d) {
@@ -95,7 +95,7 @@ Blob blob_geom(const moe_layer_desc* d) {
 
 struct Ws {
   size_t logits, wnorm, xsum, x16, ids, tw, counts, offsets, sorted, inv, tiles, sched, n_tiles, active, n_active, segs,
-      hbuf, hsum, obuf;
+      hbuf, obuf, dpart;
   size_t total;
 };
 
@@ -123,8 +123,13 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   w.n_active = o; o += al(4);
   w.segs = o; o += al(((Tc * k + kSegAssign - 1) / kSegAssign) * E * 4);  // per-segment expert counts
   w.hbuf = o; o += al(rows * Im * 2);
-  w.hsum = o; o += al(rows * (Im / 32) * 4);
-  w.obuf = o; o += al(Tc * k * H * 2);
+  // obuf (grouped-GEMM path) and dpart (decode GEMV path: partial outputs
+  // [T*k + T][Imax/32][H] fp32, T <= 8) are never live together: one region.
+  const int64_t Td = Tc < kMaxRowsDecode ? Tc : kMaxRowsDecode;
+  const int64_t dpart_bytes = (Td * k + Td) * (Im / 32) * H * 4;
+  w.obuf = o;
+  w.dpart = o;
+  o += al(Tc * k * H * 2 > dpart_bytes ? Tc * k * H * 2 : dpart_bytes);
   w.total = o;
   return w;
 }
@@ -320,7 +325,6 @@ ChunkArgs chunk_args(const moe_layer_desc* d, const uint16_t* x, int Tc, const R
   C.active = o.active;
   C.n_active = o.n_active;
   C.hbuf = at<uint16_t>(ws, w.hbuf);
-  C.hsum = at<float>(ws, w.hsum);
   C.obuf = at<uint16_t>(ws, w.obuf);
   C.y = y;
   C.Imax = imax(d);
@@ -483,17 +487,19 @@ moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, co
   const LayerArgs L = layer_args(desc, packed);
   const Ws w = ws_layout(desc, T);
   const RouteOut o = ws_route(ws, w);
-  // Exact logits, then the top-k and routing tables inside the gate/up GEMV.
+  // Exact logits; then the top-k, gate/up and split down projection; then the
+  // fixed-order sum of the partial outputs.
   bool two = false;
+  float* part = at<float>(ws, w.dpart);
   TRY(timed(0, s, "router logits", [&](const KTime& kt) {
     return launch_route_logits(x, T, desc->hidden, router_w, logit_bias, desc->n_experts, desc->top_k, o.logits,
                                o.wsq, o.ids, o.tw, nullptr, nullptr, nullptr, s, &two, kt);
   }));
   const ChunkArgs C = chunk_args(desc, x, T, o, ws, w, y);
-  TRY(timed(5, s, "top-k + gate/up GEMV", [&](const KTime& kt) {
-    return launch_gemv_gateup(L, C, o.logits, tile_rows(desc), desc->shared_inter > 0 ? 1 : 0, s, kt);
+  TRY(timed(5, s, "top-k + gate/up + split down GEMV", [&](const KTime& kt) {
+    return launch_gemv_experts(L, C, o.logits, part, s, kt);
   }));
-  TRY(timed(6, s, "down GEMV", [&](const KTime& kt) { return launch_gemv_down(L, C, s, kt); }));
+  TRY(timed(6, s, "partial-output sum", [&](const KTime& kt) { return launch_gemv_reduce(L, C, part, s, kt); }));
   return MOE_OK;
 }
 

@@ -73,8 +73,7 @@ struct ChunkArgs {
                           // rows, first row in expert-sorted order
   const int32_t* active;  // [E] experts with rows, increasing
   const int32_t* n_active;// [1]
-  uint16_t* hbuf;         // [T*k + T][Imax]: fp16(h / 256) on the GEMM path, bf16 h on the GEMV path
-  float* hsum;            // [T*k + T][Imax/32] GEMV path: sums of bf16(h) over 32-column halves of a group
+  uint16_t* hbuf;         // [T*k + T][Imax]: fp16(h / 256), grouped-GEMM path
   uint16_t* obuf;         // [T*k][H] GEMM path: fp16(routed expert output / 256) per sorted position
   float* y;               // [T][H]
   int Imax;               // row stride of hbuf

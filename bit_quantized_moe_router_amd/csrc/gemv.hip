@@ -4,56 +4,105 @@
 // "Reduce intermediate and state traffic" for the two fused chains).
 //
 // With one to a few rows the layer is bound by weight bytes, so each expert's
-// packed weights are streamed once: a wave reads one 1152-byte block (32
-// output rows x one 64-column group) with a single 16-byte load per lane, so a
-// lane holds 32 codes of one output row.  Every wave issues the loads of
-// several blocks before it computes, so most of the working set is in flight
-// at once.  Codes expand to bf16 pairs (128 + q) and meet the activation pairs
-// in v_dot2_f32_bf16; the per-group affine fold is
+// packed weights are streamed once.  A wave reads one 1152-byte gate or up
+// block (32 output rows x one 64-column group) with a single 16-byte load per
+// lane, so a lane holds 32 codes of one output row; every wave issues the
+// loads of all its blocks before it computes.  Codes expand to bf16 pairs
+// (128 + q) and meet the activation pairs in v_dot2_f32_bf16; the per-group
+// affine fold is
 //   acc += s * dot + (b - 128 s) * sum(x over the group).
-// The two lanes that share an output row are combined with one cross-half
-// shuffle, the waves of a workgroup through LDS.  No atomics: every output is
-// produced by exactly one workgroup, in a fixed order.
+// The down projection is split along the intermediate: the workgroup that
+// produced 32 columns of h applies the matching 32 columns of the down matrix
+// (half of each down block, loaded in the same round as gate/up) and writes a
+// partial output row; a second kernel sums the partials of each token in a
+// fixed order.  No atomics touch the outputs.
 #include "launch.h"
 #include "small_route.h"
 
 namespace moe {
 
 constexpr int kGemvMaxRows = 8;
-constexpr int kGuWaves = 8;    // gate/up workgroup: 8 waves split the H/64 groups
-constexpr int kGuPref = 4;     // groups per wave whose loads are issued together
-constexpr int kDnWaves = 8;    // down workgroup: 8 waves split the (expert, group) items
-constexpr int kDnPref = 4;
+constexpr int kGuPref = 4;     // groups per wave whose gate/up loads are issued together
 constexpr int kMaxGroups = 128;              // H / 64 for H <= 8192
 constexpr int kMaxAssign = kGemvMaxRows * 16; // T * k on the GEMV path
-constexpr int kMaxSlots = kMaxAssign + 1;     // active experts + the shared expert
-constexpr int kDnStageMax = 120 * 1024;       // LDS for staged intermediate rows
 constexpr int kGuSmemMax = 64 * 1024 + kGemvMaxRows * (2 * 512 + 16) * 4;  // x rows + top-k lists
 
 // ---------------------------------------------------------------------------
-// Top-k + gate/up + SwiGLU.  grid = (expert slots: active experts, then the
-// shared expert, then one metadata workgroup; I/32 row blocks).
-//
-// Routing is folded in, so decode needs no separate top-k launch between the
-// logits and the weights: every workgroup takes the top-k of the chunk's rows
-// from the exact logits itself (waves t < T, one row each), then wave 0 finds
-// the workgroup's expert (the slot-th smallest selected expert: a bitmap of
-// the selected experts and prefix popcounts over its words) and the expert's
-// rows in flat assignment order.  The last column of workgroups (row block 0
-// only) writes the routing tables the down kernel reads (ids, weights,
-// counts, offsets, sorted order, active list, ...) with meta_small.  The
-// activation rows are staged in LDS first, independent of the routing; their
-// per-group sums are taken there.
+// Decode, experts step: top-k, gate/up + SwiGLU, and the down projection
+// split along its reduction axis (the intermediate), so that each workgroup
+// applies the down matrix to the 32 intermediate columns it has just produced
+// and the down weights stream in the same round as gate/up.  grid (1D) =
+// n_slots x nbs workgroups (slot: active expert, then the shared expert; nb:
+// 32-column block of the intermediate).  For each of its rows (assignment
+// a = t*k + j, or T*k + t for the shared expert) a workgroup writes the
+// routing-weighted partial output of its 32 columns, part[a][nb][0..H).
+// k_gemv_reduce sums them.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, ChunkArgs C, const float* logits,
-                                                               int BM, int with_shared) {
-  const int slot = blockIdx.x, nb = blockIdx.y;
+constexpr int kFuWaves = 8;
+constexpr int kFuThreads = kFuWaves * 64;
+constexpr int kRedCols = 64;                 // output columns per reduce workgroup
+constexpr int kRedGroups = kFuThreads / 16;  // term groups of a reduce workgroup (16 float4 columns each)
+constexpr int kFuDn = 4;                     // down outputs per thread per load round
+constexpr int kFuBatch = 8;                  // partials a reduce thread loads together
+
+// y[t][64 columns] = sum of token t's partials in a fixed order (routed
+// assignments j = 0..k-1 with blocks nb ascending, then the shared expert's
+// blocks), so y does not depend on the order in which workgroups ran.
+// grid = T x H/64.
+__global__ __launch_bounds__(kFuThreads) void k_gemv_reduce(LayerArgs L, ChunkArgs C, const float* __restrict__ part,
+                                                           int nbs) {
+  __shared__ float4 red4[kRedGroups][16];
+  const int tid = threadIdx.x;
+  const int H = L.H, k = L.k, Tk = C.Tk;
+  const int nslice = H / kRedCols;
+  const int t = (int)blockIdx.x / nslice, sl = (int)blockIdx.x - t * nslice;
+  const int c4 = tid & 15, tg = tid >> 4;
+  const int col = sl * kRedCols + c4 * 4;
+  const int nI = L.I / 32, nS = L.Is / 32;
+  const int nrt = k * nI, nterm = nrt + nS;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = tg; i0 < nterm; i0 += kFuBatch * kRedGroups) {
+    float4 v[kFuBatch];
+#pragma unroll
+    for (int p = 0; p < kFuBatch; p++) {
+      const int i = i0 + p * kRedGroups;
+      v[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < nterm) {
+        const int a = i < nrt ? t * k + i / nI : Tk + t;
+        const int nb = i < nrt ? i % nI : i - nrt;
+        v[p] = *reinterpret_cast<const float4*>(part + ((int64_t)a * nbs + nb) * H + col);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kFuBatch; p++) {
+      acc.x += v[p].x;
+      acc.y += v[p].y;
+      acc.z += v[p].z;
+      acc.w += v[p].w;
+    }
+  }
+  red4[tg][c4] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float4 sm = red4[0][tid];
+    for (int g = 1; g < kRedGroups; g++) {
+      const float4 v = red4[g][tid];
+      sm.x += v.x;
+      sm.y += v.y;
+      sm.z += v.z;
+      sm.w += v.w;
+    }
+    *reinterpret_cast<float4*>(C.y + (int64_t)t * H + sl * kRedCols + tid * 4) = sm;
+  }
+}
+
+__global__ __launch_bounds__(kFuThreads) void k_gemv_experts(LayerArgs L, ChunkArgs C, const float* logits,
+                                                            float* __restrict__ part, int nbs) {
+  const int slot = (int)blockIdx.x / nbs, nb = (int)blockIdx.x - slot * nbs;
   const int T = C.T, H = L.H, G = H / kGroup, E = L.E, k = L.k, N = T * k;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  const bool meta_wg = slot == (int)gridDim.x - 1;
-  if (meta_wg && nb != 0) return;  // workgroup-uniform, before any barrier
   extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];  // [T][H] x rows, then [T][2E+16] top-k lists
   uint16_t* xl = reinterpret_cast<uint16_t*>(gsm);
   int* lists = reinterpret_cast<int*>(gsm + (size_t)T * H * 2);
@@ -61,41 +110,28 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
   __shared__ int s_ids[kMaxAssign];
   __shared__ float s_tw[kMaxAssign];
   __shared__ uint32_t s_bm[kMaxE / 32];
-  __shared__ int tok[kGemvMaxRows], orow[kGemvMaxRows], s_info[3];
-  __shared__ float red[kGuWaves][kGemvMaxRows][2][32];
+  __shared__ int tok[kGemvMaxRows], arow[kGemvMaxRows], s_info[2];
+  __shared__ float wgt[kGemvMaxRows], s_hs[kGemvMaxRows];
+  __shared__ __attribute__((aligned(16))) uint32_t s_h[kGemvMaxRows][16];  // bf16 h of the 32 columns, as pairs
+  __shared__ float red[kFuWaves][kGemvMaxRows][2][32];
 
-  // ---- loads independent of the routing: the chunk's activation rows, into
-  // registers first so that their latency overlaps the top-k's ----
-  const int H8 = H / 8, nx = meta_wg ? 0 : T * H8;
-  constexpr int kNt = kGuWaves * 64;
+  // ---- activation rows into registers (their latency overlaps the top-k) ----
+  const int H8 = H / 8, nx = T * H8;
   uint4 xr0 = make_uint4(0u, 0u, 0u, 0u), xr1 = xr0;
   if (tid < nx) xr0 = reinterpret_cast<const uint4*>(C.x)[tid];
-  if (tid + kNt < nx) xr1 = reinterpret_cast<const uint4*>(C.x)[tid + kNt];
+  if (tid + kFuThreads < nx) xr1 = reinterpret_cast<const uint4*>(C.x)[tid + kFuThreads];
   // ---- top-k of each row ----
   if (wave < T) topk_small(logits + (int64_t)wave * E, E, k, wave, s_ids, s_tw, lists + wave * (2 * E + 16));
   if (tid < nx) reinterpret_cast<uint4*>(xl)[tid] = xr0;
-  if (tid + kNt < nx) reinterpret_cast<uint4*>(xl)[tid + kNt] = xr1;
-  for (int i = tid + 2 * kNt; i < nx; i += kNt) reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(C.x)[i];
+  if (tid + kFuThreads < nx) reinterpret_cast<uint4*>(xl)[tid + kFuThreads] = xr1;
+  for (int i = tid + 2 * kFuThreads; i < nx; i += kFuThreads)
+    reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(C.x)[i];
   if (tid < kMaxE / 32) s_bm[tid] = 0u;
   __syncthreads();
 
-  if (meta_wg) {
-    // Routing tables of the chunk (workspace; the down kernel reads them).
-    int32_t* ids = const_cast<int32_t*>(C.ids);
-    float* tw = const_cast<float*>(C.tw);
-    for (int a = tid; a < N; a += blockDim.x) {
-      ids[a] = s_ids[a];
-      tw[a] = s_tw[a];
-    }
-    if (wave == 0)
-      meta_small(s_ids, T, k, E, BM, with_shared, const_cast<int32_t*>(C.counts), const_cast<int32_t*>(C.offsets),
-                 const_cast<int32_t*>(C.sorted), const_cast<int32_t*>(C.tiles), const_cast<int32_t*>(C.n_tiles),
-                 const_cast<int32_t*>(C.active), const_cast<int32_t*>(C.n_active), const_cast<int32_t*>(C.inv),
-                 const_cast<int32_t*>(C.sched), lists);
-    return;
-  }
-
-  // ---- this workgroup's expert and rows (wave 0) ----
+  // ---- this workgroup's expert (the slot-th smallest selected one, or the
+  // shared expert at slot = number of selected experts) and its rows in flat
+  // assignment order (wave 0) ----
   if (wave == 0) {
     const int id0 = lane < N ? s_ids[lane] : -1, id1 = lane + 64 < N ? s_ids[lane + 64] : -1;
     if (id0 >= 0) atomicOr(&s_bm[id0 >> 5], 1u << (id0 & 31));
@@ -108,7 +144,6 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
     const int nact = __shfl(incl, 63);
     int e = -1;
     if (slot < nact) {
-      // The word holding the slot-th set bit, then the bit inside it.
       const bool here = incl > slot && incl - cnt <= slot;
       const uint64_t hm = __ballot(here);
       const int wl = __ffsll((unsigned long long)hm) - 1;
@@ -121,46 +156,49 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
     const bool shared = slot == nact;
     int rows = 0;
     if (e >= 0) {
-      const int off = __popcll(__ballot(id0 >= 0 && id0 < e)) + __popcll(__ballot(id1 >= 0 && id1 < e));
       const uint64_t m0 = __ballot(id0 == e), m1 = __ballot(id1 == e);
       const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       rows = __popcll(m0) + __popcll(m1);
       if (id0 == e) {
         const int r = __popcll(m0 & lt);
         tok[r] = lane / k;
-        orow[r] = off + r;
+        arow[r] = lane;
+        wgt[r] = s_tw[lane];
       }
       if (id1 == e) {
         const int r = __popcll(m0) + __popcll(m1 & lt);
         tok[r] = (lane + 64) / k;
-        orow[r] = off + r;
+        arow[r] = lane + 64;
+        wgt[r] = s_tw[lane + 64];
       }
     } else if (shared && L.Is > 0) {
       rows = T;
       if (lane < T) {
         tok[lane] = lane;
-        orow[lane] = N + lane;
+        arow[lane] = N + lane;
+        wgt[lane] = 1.f;
       }
     }
     if (lane == 0) {
       s_info[0] = shared ? L.E : e;
       s_info[1] = rows;
-      s_info[2] = nact;
     }
   }
   __syncthreads();
   const int e = s_info[0], rows = s_info[1];
   const bool shared = e == L.E;
   const int Iw = shared ? L.Is : L.I;
-  if (rows == 0 || nb * 32 >= Iw) return;  // workgroup-uniform; no barrier before this point is pending
-  const uint8_t* wbase = expert_base(L, e) + (int64_t)nb * G * 2 * kBlockBytes;
+  if (rows == 0 || nb * 32 >= Iw) return;  // workgroup-uniform
+  const uint8_t* ebase = expert_base(L, e);
+  const uint8_t* wbase = ebase + (int64_t)nb * G * 2 * kBlockBytes;
 
+  // ---- gate/up codes of the wave's groups, and the first down outputs' codes ----
   uint4 cg[kGuPref], cu[kGuPref];
   uint32_t sbg[kGuPref], sbu[kGuPref];
   auto load = [&](int g0) {
 #pragma unroll
     for (int p = 0; p < kGuPref; p++) {
-      const int g = g0 + p * kGuWaves;
+      const int g = g0 + p * kFuWaves;
       if (g < G) {
         const uint8_t* blk = wbase + (int64_t)g * 2 * kBlockBytes;
         cg[p] = *reinterpret_cast<const uint4*>(blk + lane * 16);
@@ -170,16 +208,34 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
       }
     }
   };
-
+  // Down matrix: output row n sits in block (n / 32, nb / 2) as row n % 32;
+  // this workgroup's 32 columns are the lane half nb % 2 of that block.
+  const int Gd = Iw / kGroup, hh = nb & 1;
+  const uint8_t* dbase = ebase + (shared ? L.shared_gateup_bytes : L.gateup_bytes) + (int64_t)(nb >> 1) * kBlockBytes;
+  uint4 dq[kFuDn];
+  uint32_t dsb[kFuDn];
+  auto load_dn = [&](int c) {
+#pragma unroll
+    for (int p = 0; p < kFuDn; p++) {
+      const int n = tid + kFuThreads * (p + kFuDn * c);
+      if (n < H) {
+        const uint8_t* blk = dbase + (int64_t)(n >> 5) * Gd * kBlockBytes;
+        dq[p] = *reinterpret_cast<const uint4*>(blk + (hh * 32 + (n & 31)) * 16);
+        dsb[p] = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + (n & 31) * 4);
+      }
+    }
+  };
   load(wave);
-  // Per-group activation sums while the first codes are in flight: 8 lanes
-  // per group, 8 columns each, then a 3-step shuffle tree.
-  for (int i0 = 0; i0 < T * G * 8; i0 += blockDim.x) {
-    const int i = i0 + tid, gi = i >> 3, part = i & 7;
+  load_dn(0);
+
+  // Per-group activation sums while the codes are in flight: 8 lanes per
+  // group, 8 columns each, then a 3-step shuffle tree.
+  for (int i0 = 0; i0 < T * G * 8; i0 += kFuThreads) {
+    const int i = i0 + tid, gi = i >> 3, part8 = i & 7;
     float sm = 0.f;
     if (gi < T * G) {
       const int t = gi / G, g = gi - t * G;
-      const uint4 v = *reinterpret_cast<const uint4*>(xl + t * H + g * kGroup + part * 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(xl + t * H + g * kGroup + part8 * 8);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; j++) sm += bf16_bits_to_f32(w[j] & 0xFFFFu) + bf16_bits_to_f32(w[j] >> 16);
@@ -187,19 +243,19 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
     sm += __shfl_xor(sm, 1);
     sm += __shfl_xor(sm, 2);
     sm += __shfl_xor(sm, 4);
-    if (gi < T * G && part == 0) xs[gi] = sm;
+    if (gi < T * G && part8 == 0) xs[gi] = sm;
   }
   __syncthreads();
 
+  // ---- gate/up dot products ----
   float accg[kGemvMaxRows], accu[kGemvMaxRows];
 #pragma unroll
   for (int j = 0; j < kGemvMaxRows; j++) accg[j] = accu[j] = 0.f;
-
-  for (int g0 = wave; g0 < G; g0 += kGuPref * kGuWaves) {
+  for (int g0 = wave; g0 < G; g0 += kGuPref * kFuWaves) {
     if (g0 != wave) load(g0);
 #pragma unroll
     for (int p = 0; p < kGuPref; p++) {
-      const int g = g0 + p * kGuWaves;
+      const int g = g0 + p * kFuWaves;
       if (g >= G) break;
       uint32_t qg[16], qu[16];
       expand_codes(cg[p].x, qg + 0);
@@ -228,7 +284,6 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
               du = dot2_bf16(qu[4 * c + i], xw[i], du);
             }
           }
-          // The group's activation sum covers both lane halves: fold it in once.
           const float xsv = h == 0 ? xs[t * G + g] : 0.f;
           accg[j] = fmaf(sg, dg, fmaf(bpg, xsv, accg[j]));
           accu[j] = fmaf(su, du, fmaf(bpu, xsv, accu[j]));
@@ -248,14 +303,15 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
     }
   }
   __syncthreads();
-  // Thread 32*j + n finishes row j, column n.
-  for (int base = 0; base < kGemvMaxRows * 32; base += blockDim.x) {
-    const int j = (base + threadIdx.x) >> 5, n = threadIdx.x & 31;
+  // ---- SwiGLU: thread 32*j + n finishes row j, column n; h is rounded to
+  // bf16 and its 32-column sum taken for the down fold ----
+  if (tid < kGemvMaxRows * 32) {
+    const int j = tid >> 5, n = tid & 31;
     const bool ok = j < rows;
     float gs = 0.f, us = 0.f;
     if (ok) {
 #pragma unroll
-      for (int w = 0; w < kGuWaves; w++) {
+      for (int w = 0; w < kFuWaves; w++) {
         gs += red[w][j][0][n];
         us += red[w][j][1][n];
       }
@@ -265,197 +321,58 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gemv_gateup(LayerArgs L, Chun
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) hs += __shfl_xor(hs, off);
     if (ok) {
-      C.hbuf[(int64_t)orow[j] * C.Imax + nb * 32 + n] = hb;
-      if (n == 0) C.hsum[(int64_t)orow[j] * (C.Imax / 32) + nb] = hs;
+      reinterpret_cast<uint16_t*>(s_h[j])[n] = hb;
+      if (n == 0) s_hs[j] = hs;
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// down + routing weight + shared add + combine.  grid = H/8 workgroups of 8
-// output rows each.  A workgroup walks every (expert slot, group) item; the
-// items' 8-row slices of their 1152-byte blocks (two 128-byte runs of codes
-// and 32 bytes of scale/bias) are read by 16 lanes each, so a wave covers 4
-// items per load: lane l takes item l/16, row l%8 and K half (l/8)%2.  The
-// routing tables (slot -> expert, segment, rows; sorted position -> token,
-// weight) and, when they fit, all intermediate rows and their sums are staged
-// in LDS first; the first item loads go out before the staging, from a
-// speculative read of the active list.  Partial sums meet in registers (K
-// halves, items of a wave) and LDS (waves); every output has one owner.
-// ---------------------------------------------------------------------------
-constexpr int kDnRows = 8;                         // output rows per workgroup
-constexpr int kDnItemsPerLoad = kDnWaves * 4;      // items one load round covers
-
-__global__ __launch_bounds__(kDnWaves * 64) void k_gemv_down(LayerArgs L, ChunkArgs C, int staged) {
-  const int row0 = blockIdx.x * kDnRows;
-  const int H = L.H, T = C.T, Tk = C.Tk;
-  const int hsw = C.Imax / 32;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int sub = lane >> 4, hh = (lane >> 3) & 1, r = lane & 7;
-  const int rr = row0 % 32 + r, nb32 = row0 / 32;  // row inside its 32-row block, block index
-  const int Gi = L.I / kGroup, Gs = L.Is / kGroup;
-  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];  // staged h rows, then their sums
-  __shared__ int s_e[kMaxSlots], s_seg[kMaxSlots], s_rows[kMaxSlots];
-  __shared__ int s_tok[kMaxAssign];
-  __shared__ float s_w[kMaxAssign];
-  __shared__ float red[kDnWaves][kGemvMaxRows][kDnRows];
-
-  const int nact = *C.n_active;
-  const int nspec = min(L.E, Tk);  // slots the active list can hold
-  // Item it -> (slot, group); the shared expert's items follow the routed ones.
-  auto item_expert = [&](int it, int na, int& g) -> int {
-    if (it < na * Gi) {
-      const int sl = it / Gi;
-      g = it - sl * Gi;
-      return min(max(C.active[min(sl, nspec - 1)], 0), L.E - 1);
-    }
-    g = it - na * Gi;
-    return L.E;
-  };
-  const int nitems = nact * Gi + Gs;
-
-  uint4 cd[kDnPref];
-  uint32_t sb[kDnPref];
-  int pe[kDnPref], pg[kDnPref];
-  auto load = [&](int base) {
-#pragma unroll
-    for (int p = 0; p < kDnPref; p++) {
-      const int it = base + p * kDnItemsPerLoad + wave * 4 + sub;
-      pe[p] = -1;
-      pg[p] = 0;
-      if (it < nitems) {
-        int g;
-        const int e = item_expert(it, nact, g);
-        const bool sh = e == L.E;
-        const int Gk = sh ? Gs : Gi;
-        const uint8_t* blk = expert_base(L, e) + (sh ? L.shared_gateup_bytes : L.gateup_bytes) +
-                             (int64_t)(nb32 * Gk + g) * kBlockBytes;
-        cd[p] = *reinterpret_cast<const uint4*>(blk + (hh * 32 + rr) * 16);
-        sb[p] = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + rr * 4);
-        pe[p] = it < nact * Gi ? it / Gi : nact;  // slot
-        pg[p] = g;
-      }
-    }
-  };
-  load(0);
-
-  // ---- staging: routing tables, then (if staged) h rows and their sums ----
-  for (int a = tid; a < Tk; a += blockDim.x) {
-    const int as = C.sorted[a];
-    s_tok[a] = as / L.k;
-    s_w[a] = C.tw[as];
-  }
-  for (int sl = tid; sl <= nact; sl += blockDim.x) {
-    if (sl < nact) {
-      const int e = C.active[sl];
-      s_e[sl] = e;
-      s_seg[sl] = C.offsets[e];
-      s_rows[sl] = C.counts[e];
-    } else {
-      s_e[sl] = L.E;
-      s_seg[sl] = Tk;
-      s_rows[sl] = L.Is > 0 ? T : 0;
-    }
-  }
-  const int nrows = Tk + T;
-  uint16_t* hl = reinterpret_cast<uint16_t*>(dsm);
-  float* hsl = reinterpret_cast<float*>(dsm + (size_t)nrows * C.Imax * 2);
-  if (staged) {
-    const int n16 = nrows * C.Imax / 8;
-    for (int i = tid; i < n16; i += blockDim.x) reinterpret_cast<uint4*>(hl)[i] = reinterpret_cast<const uint4*>(C.hbuf)[i];
-    for (int i = tid; i < nrows * hsw; i += blockDim.x) hsl[i] = C.hsum[i];
   }
   __syncthreads();
-  const uint16_t* hb = staged ? hl : C.hbuf;
-  const float* hs = staged ? hsl : C.hsum;
 
-  float acc[kGemvMaxRows];
+  // ---- down projection of the 32 columns: partial outputs, weighted ----
+  const int nrounds = (H + kFuThreads * kFuDn - 1) / (kFuThreads * kFuDn);
+  for (int c = 0; c < nrounds; c++) {
+    if (c != 0) load_dn(c);
 #pragma unroll
-  for (int t = 0; t < kGemvMaxRows; t++) acc[t] = 0.f;
-
-  for (int base = 0; base < nitems; base += kDnPref * kDnItemsPerLoad) {
-    if (base != 0) load(base);
-#pragma unroll
-    for (int p = 0; p < kDnPref; p++) {
-      if (pe[p] < 0) continue;
-      const int sl = pe[p], g = pg[p];
-      const bool sh = sl == nact;
-      const int rows = s_rows[sl];
-      const int seg = s_seg[sl];
+    for (int p = 0; p < kFuDn; p++) {
+      const int n = tid + kFuThreads * (p + kFuDn * c);
+      if (n >= H) break;
       uint32_t q[16];
-      expand_codes(cd[p].x, q + 0);
-      expand_codes(cd[p].y, q + 4);
-      expand_codes(cd[p].z, q + 8);
-      expand_codes(cd[p].w, q + 12);
-      const float s = bf16_bits_to_f32(sb[p] & 0xFFFFu), bp = bf16_bits_to_f32(sb[p] >> 16) - 128.f * s;
+      expand_codes(dq[p].x, q + 0);
+      expand_codes(dq[p].y, q + 4);
+      expand_codes(dq[p].z, q + 8);
+      expand_codes(dq[p].w, q + 12);
+      const float s = bf16_bits_to_f32(dsb[p] & 0xFFFFu), bp = bf16_bits_to_f32(dsb[p] >> 16) - 128.f * s;
       for (int j = 0; j < rows; j++) {
-        const int irow = seg + j;
-        const int t = sh ? j : s_tok[irow];
-        const float w = sh ? 1.f : s_w[irow];
-        const uint4* hp = reinterpret_cast<const uint4*>(hb + (int64_t)irow * C.Imax + g * kGroup + hh * 32);
         float d = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-          const uint4 hv = hp[c];
-          d = dot2_bf16(q[4 * c + 0], hv.x, d);
-          d = dot2_bf16(q[4 * c + 1], hv.y, d);
-          d = dot2_bf16(q[4 * c + 2], hv.z, d);
-          d = dot2_bf16(q[4 * c + 3], hv.w, d);
-        }
-        // hsum holds 32-column sums, so this lane's K half.
-        const float v = w * fmaf(s, d, bp * hs[(int64_t)irow * hsw + 2 * g + hh]);
-#pragma unroll
-        for (int tt = 0; tt < kGemvMaxRows; tt++)
-          if (tt == t) acc[tt] += v;
+        for (int i = 0; i < 16; i++) d = dot2_bf16(q[i], s_h[j][i], d);
+        part[((int64_t)arow[j] * nbs + nb) * H + n] = wgt[j] * fmaf(s, d, bp * s_hs[j]);
       }
     }
-  }
-  // K halves (lane bit 3) and the wave's 4 items (lane bits 4, 5), then waves.
-#pragma unroll
-  for (int t = 0; t < kGemvMaxRows; t++) {
-    if (t < T) {
-      acc[t] += __shfl_xor(acc[t], 8);
-      acc[t] += __shfl_xor(acc[t], 16);
-      acc[t] += __shfl_xor(acc[t], 32);
-      if (lane < kDnRows) red[wave][t][lane] = acc[t];
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < T * kDnRows; i += blockDim.x) {
-    const int t = i / kDnRows, n = i - t * kDnRows;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDnWaves; w++) v += red[w][t][n];
-    C.y[(int64_t)t * H + row0 + n] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, const float* logits, int BM,
-                              int with_shared, hipStream_t s, const KTime& kt) {
+hipError_t launch_gemv_experts(const LayerArgs& L, const ChunkArgs& C, const float* logits, float* part,
+                               hipStream_t s, const KTime& kt) {
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  const int slots = (L.E < C.Tk ? L.E : C.Tk) + 1;
-  dim3 grid(slots + 1, Imax / 32);  // + the metadata workgroup
-  // rows T * H * 2 <= 64 KB on this path, lists <= 8 * 1040 * 4, beside ~22 KB of static LDS
+  const int n_slots = (L.E < C.Tk ? L.E : C.Tk) + 1;
+  const int nbs = Imax / 32;
   static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_gemv_gateup), kGuSmemMax, lds_set);
+  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_gemv_experts), kGuSmemMax, lds_set);
   if (e != hipSuccess) return e;
   const size_t smem = (size_t)C.T * L.H * 2 + (size_t)C.T * (2 * L.E + 16) * 4;
   if (smem > (size_t)kGuSmemMax || C.T > kGemvMaxRows || C.Tk > kMaxAssign) return hipErrorInvalidValue;
-  MOE_LAUNCH(k_gemv_gateup, grid, dim3(kGuWaves * 64), smem, s, kt.start, kt.stop, L, C, logits, BM, with_shared);
+  MOE_LAUNCH(k_gemv_experts, dim3((unsigned)(n_slots * nbs)), dim3(kFuThreads), smem, s, kt.start, kt.stop, L, C,
+             logits, part, nbs);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt) {
-  static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_gemv_down), kDnStageMax, lds_set);
-  if (e != hipSuccess) return e;
-  const size_t rows = (size_t)C.Tk + C.T;
-  const size_t stage = rows * C.Imax * 2 + rows * (C.Imax / 32) * 4;
-  const int staged = stage <= (size_t)kDnStageMax ? 1 : 0;
-  MOE_LAUNCH(k_gemv_down, dim3(L.H / kDnRows), dim3(kDnWaves * 64), staged ? stage : 0, s, kt.start, kt.stop, L,
-             C, staged);
+hipError_t launch_gemv_reduce(const LayerArgs& L, const ChunkArgs& C, const float* part, hipStream_t s,
+                              const KTime& kt) {
+  const int Imax = L.I > L.Is ? L.I : L.Is;
+  if (L.H % kRedCols != 0) return hipErrorInvalidValue;
+  MOE_LAUNCH(k_gemv_reduce, dim3((unsigned)(C.T * (L.H / kRedCols))), dim3(kFuThreads), 0, s, kt.start, kt.stop, L,
+             C, part, Imax / 32);
   return hipGetLastError();
 }
 

@@ -91,10 +91,11 @@ int gateup_col_tiles(int I, int Is);
 int gemm_wgs_per_cu();
 // y[t] += sum_j w_tj * routed output of assignment (t, j) (GEMM path).
 hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
-// Decode GEMV path: top-k of the exact logits (and the chunk's routing tables)
-// folded into the gate/up GEMV, then the down GEMV.
-hipError_t launch_gemv_gateup(const LayerArgs& L, const ChunkArgs& C, const float* logits, int BM, int with_shared,
-                              hipStream_t s, const KTime& kt = KTime{});
-hipError_t launch_gemv_down(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
+// Decode GEMV path: top-k, gate/up + SwiGLU and the down projection split
+// over the intermediate (partial outputs in `part`), then their fixed-order sum.
+hipError_t launch_gemv_experts(const LayerArgs& L, const ChunkArgs& C, const float* logits, float* part,
+                               hipStream_t s, const KTime& kt = KTime{});
+hipError_t launch_gemv_reduce(const LayerArgs& L, const ChunkArgs& C, const float* part, hipStream_t s,
+                              const KTime& kt = KTime{});
 
 }  // namespace moe

@@ -166,6 +166,11 @@ moe_status moe_forward_prefill(const moe_layer_desc *desc, const void *packed,
 /*
  * Same layer for a few rows (1 <= T <= 8): the row-parallel GEMV path when
  * T <= gemv_max_rows, otherwise the grouped GEMM path of moe_forward_prefill.
+ * The GEMV path is three launches: exact router logits; top-k, gate/up +
+ * SwiGLU and the down projection of each workgroup's 32 intermediate columns
+ * (partial output rows in the workspace); the sum of each token's partials in
+ * a fixed order.  y is written once per element, with no atomics, so repeated
+ * calls give identical bits.
  */
 moe_status moe_forward_decode(const moe_layer_desc *desc, const void *packed,
                               const float *router_w, const float *logit_bias,
@@ -191,8 +196,9 @@ const char *moe_last_error(void);
  *   0 = router logits (screen, or exact for T <= 8), 1 = exact top-k
  *   selection (T > 8), 2 = routing metadata (with top-k for T <= 8 outside
  *   the decode GEMV path), 3 = gate/up grouped GEMM, 4 = down grouped GEMM,
- *   5 = top-k + gate/up GEMV (decode GEMV path), 6 = down GEMV, 7 = per-token
- *   combine of the grouped-GEMM path
+ *   5 = top-k + gate/up GEMV + split down GEMV (decode GEMV path), 6 = sum of
+ *   the decode path's partial outputs, 7 = per-token combine of the
+ *   grouped-GEMM path
  */
 moe_status moe_profile_enable(int32_t mask);
 moe_status moe_profile_reset(void);

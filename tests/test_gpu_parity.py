@@ -208,16 +208,16 @@ EDGE_DECODE = [  # T, H, E, k, I, Is, seed, zipf
 @pytest.mark.parametrize("T,H,E,k,I,Is,seed,zipf", EDGE_DECODE)
 def test_decode_gemv_edge_shapes(M, T, H, E, k, I, Is, seed, zipf):
     """The GEMV path (forced for all T <= 8) on odd shapes; checks that it is the path that ran."""
-    from bit_quantized_moe_router_amd import (K_DOWN_GEMM, K_DOWN_GEMV, moe_profile_enable, moe_profile_read,
+    from bit_quantized_moe_router_amd import (K_DOWN_GEMM, K_GATEUP_GEMV, moe_profile_enable, moe_profile_read,
                                               moe_profile_reset)
     case = mi.small_layer(T, H, E, k, I, Is, seed, zipf)
     lay = M.MoELayer(case["w"], k, max_tokens=T, gemv_max_rows=8)
     moe_profile_reset()
-    moe_profile_enable((1 << K_DOWN_GEMV) | (1 << K_DOWN_GEMM))
+    moe_profile_enable((1 << K_GATEUP_GEMV) | (1 << K_DOWN_GEMM))
     try:
         y = lay.forward_decode(dev(M, case["x"]), dev(M, case["bias"]))
         torch.cuda.synchronize()
-        ran = (moe_profile_read(K_DOWN_GEMV)[1], moe_profile_read(K_DOWN_GEMM)[1])
+        ran = (moe_profile_read(K_GATEUP_GEMV)[1], moe_profile_read(K_DOWN_GEMM)[1])
     finally:
         moe_profile_enable(0)
         moe_profile_reset()
