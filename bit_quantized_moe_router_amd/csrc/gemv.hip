@@ -132,7 +132,27 @@ __global__ __launch_bounds__(kFuThreads) void k_gemv_experts(LayerArgs L, ChunkA
   // ---- this workgroup's expert (the slot-th smallest selected one, or the
   // shared expert at slot = number of selected experts) and its rows in flat
   // assignment order (wave 0) ----
-  if (wave == 0) {
+  if (wave == 0 && T == 1) {
+    // One row: its k experts are distinct, the slot-th smallest is found by rank.
+    const int id = lane < k ? s_ids[lane] : 0x7fffffff;
+    int rank = 0;
+    for (int i = 0; i < k; i++) rank += __builtin_amdgcn_readlane(id, i) < id ? 1 : 0;
+    if (lane < k && rank == slot) {
+      tok[0] = 0;
+      arow[0] = lane;
+      wgt[0] = s_tw[lane];
+      s_info[0] = id;
+      s_info[1] = 1;
+    }
+    if (lane == 0 && slot >= k) {
+      const bool sh = slot == k && L.Is > 0;
+      tok[0] = 0;
+      arow[0] = N;
+      wgt[0] = 1.f;
+      s_info[0] = slot == k ? L.E : -1;
+      s_info[1] = sh ? 1 : 0;
+    }
+  } else if (wave == 0) {
     const int id0 = lane < N ? s_ids[lane] : -1, id1 = lane + 64 < N ? s_ids[lane + 64] : -1;
     if (id0 >= 0) atomicOr(&s_bm[id0 >> 5], 1u << (id0 & 31));
     if (id1 >= 0) atomicOr(&s_bm[id1 >> 5], 1u << (id1 & 31));

@@ -29,21 +29,23 @@ __device__ __forceinline__ uint16_t f32_to_f16_scaled(uint16_t b) {
 }
 
 // ---------------------------------------------------------------------------
-// Few tokens: all T x E logits in float64.  One wave per expert, lanes split h
-// in 16-byte slices of the router row.  Workgroups 0 and 1 also write the
-// per-group activation sums and the fp16 activation copy when asked (non-null).
+// Few tokens: all T x E logits in float64.  One single-wave workgroup per
+// expert (the router rows spread over every compute unit), lanes split h in
+// 16-byte slices of the router row.  When asked (non-null), the grid also
+// writes the per-group activation sums and the fp16 activation copy, each
+// thread taking a strided share.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict__ x, int T, int H,
-                                                      const float* __restrict__ wr,
-                                                      const float* __restrict__ bias, int E,
-                                                      float* __restrict__ logits,
-                                                      float* __restrict__ xsum,
-                                                      uint16_t* __restrict__ x16) {
-  const int wave = threadIdx.x >> 6;
-  const int e = blockIdx.x * 4 + wave;
-  if (xsum && blockIdx.x == 0) group_sums(x, T, H, xsum, threadIdx.x, blockDim.x);
-  if (x16 && blockIdx.x == (gridDim.x > 1 ? 1 : 0)) {
-    for (int i = threadIdx.x; i < T * H; i += blockDim.x) x16[i] = f32_to_f16_scaled(x[i]);
+__global__ __launch_bounds__(64) void k_logits_small(const uint16_t* __restrict__ x, int T, int H,
+                                                     const float* __restrict__ wr,
+                                                     const float* __restrict__ bias, int E,
+                                                     float* __restrict__ logits,
+                                                     float* __restrict__ xsum,
+                                                     uint16_t* __restrict__ x16) {
+  const int e = blockIdx.x;
+  const int gt = blockIdx.x * 64 + threadIdx.x, gn = gridDim.x * 64;
+  if (xsum) group_sums(x, T, H, xsum, gt, gn);
+  if (x16) {
+    for (int i = gt; i < T * H; i += gn) x16[i] = f32_to_f16_scaled(x[i]);
   }
   if (e < E) logits_one_expert(x, T, H, wr, bias, E, e, logits);
 }
@@ -782,8 +784,8 @@ hipError_t launch_route_logits(const uint16_t* x, int T, int H, const float* wr,
                                const KTime& kt) {
   if (T == 0) return hipSuccess;
   if (T <= kSmallT) {
-    MOE_LAUNCH(k_logits_small, dim3((E + 3) / 4), dim3(256), 0, s, kt.start, kt.stop, x, T, H, wr, bias, E, logits,
-               xsum, x16);
+    MOE_LAUNCH(k_logits_small, dim3(E), dim3(64), 0, s, kt.start, kt.stop, x, T, H, wr, bias, E, logits, xsum,
+               x16);
     *two_launches = false;
     return hipGetLastError();
   }

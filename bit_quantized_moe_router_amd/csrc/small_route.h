@@ -44,6 +44,25 @@ __device__ __forceinline__ float wave_kth_largest(float m, int k) {
   return __builtin_bit_cast(float, v);
 }
 
+// A lower bound of the k-th largest of the 64 lanes' values: the same radix
+// select, stopped as soon as exactly k lanes lie at or above the prefix (the
+// candidates above it are then the lanes holding the k largest values).
+__device__ __forceinline__ float wave_kth_lower_bound(float m, int k) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, m);
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  uint32_t t = 0;
+  for (int b = 31; b >= 0; b--) {
+    const uint32_t c = t | (1u << b);
+    const int n = __popcll(__ballot(key >= c));
+    if (n >= k) {
+      t = c;
+      if (n == k) break;
+    }
+  }
+  const uint32_t v = (t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t;
+  return __builtin_bit_cast(float, v);
+}
+
 // Lanes of this wave that are valid and hold the same expert e.
 __device__ __forceinline__ uint64_t match_mask(int e, bool valid, int nbits) {
   uint64_t m = __ballot(valid);
@@ -125,9 +144,10 @@ __device__ __forceinline__ void group_sums(const uint16_t* __restrict__ x, int T
   }
 }
 
-// Top-k of one token's exact logits, one wave: the k-th largest of the lanes'
-// maxima (k distinct logits at least that large) is a threshold at most the
-// k-th largest logit; the logits at or above it are listed and ranked exactly
+// Top-k of one token's exact logits, one wave: a lower bound of the k-th
+// largest of the lanes' maxima (k distinct logits lie at or above it) is a
+// threshold at most the k-th largest logit; the logits at or above it (float
+// comparison, a superset of the key comparison) are listed and ranked exactly
 // (larger first, equal logits towards the lower expert), then the softmax
 // over the k selected.  lds: 2 E + 16 ints.
 __device__ __forceinline__ void topk_small(const float* __restrict__ l, int E, int k, int t,
@@ -144,7 +164,7 @@ __device__ __forceinline__ void topk_small(const float* __restrict__ l, int E, i
     v[j] = e < E ? l[e] : -INFINITY;
     m = fmaxf(m, v[j]);
   }
-  const float thr = wave_kth_largest(m, k);
+  const float thr = wave_kth_lower_bound(m, k);
   int C = 0;
 #pragma unroll
   for (int j = 0; j < kMaxEPerLane; j++) {
