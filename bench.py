@@ -15,8 +15,9 @@ GEMM) event-stamped on its launch stream, gives that kernel's average
 duration for the roofline.
 
 Also reported on the same line: the T=1 decode layer (GEMV path) in
-microseconds per layer, per-kernel averages from extra passes, and the CPU
-oracle timed on a bounded sample on this host.
+microseconds per layer, eager and replayed from a HIP graph, per-kernel
+averages from extra passes, and the CPU oracle timed on a bounded sample on
+this host.
 """
 from __future__ import annotations
 
@@ -182,6 +183,23 @@ def main():
 
     kern_all = breakdown(prefill_pass, [moe.K_LOGITS, moe.K_TOPK, moe.K_META, moe.K_DOWN_GEMM, moe.K_COMBINE])
 
+    # Measurement of the design the pages argue against: each chunk's routing
+    # read back by the host before the GEMM launches (same kernels).
+    for lay in layers:
+        lay.set_desc(host_sync_routing=1)
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    h1.record(stream)
+    torch.cuda.synchronize()
+    ms_sync = h0.elapsed_time(h1) / a.steps
+    for lay in layers:
+        lay.set_desc(host_sync_routing=0)
+
     # Dominant kernel: gate/up grouped GEMM, one launch per 2048-token chunk.
     Tc = 2048
     flop_gateup = 2.0 * (Tc * k + Tc) * H * (2 * I)
@@ -218,6 +236,28 @@ def main():
     for lay in layers:
         lay.set_desc(gemv_max_rows=-1)
     dec_us = timed_decode(1)
+
+    # The same decode calls captured in a HIP graph (64 calls over the rotated
+    # layer copies and token rows), then replayed: the host-side launch cost
+    # is gone, the kernels' own boundaries remain.
+    def graph_decode_us(T=1, n=64, reps=20):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                j = (i * 8) % NX
+                xin = xds[j] if T == 1 else xd_all[j:j + T]
+                layers[i % len(layers)].forward_decode(xin, None, yd[:T])
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        return 1000.0 * g0.elapsed_time(g1) / (reps * n)
+
+    dec_graph_us = graph_decode_us(1)
     dkern = breakdown(lambda: decode_run(a.decode_steps), [moe.K_LOGITS, moe.K_META, moe.K_GATEUP_GEMV,
                                                            moe.K_DOWN_GEMV])
     blk = 1152
@@ -289,7 +329,10 @@ def main():
                      "traffic": traffic_from_profile(), "flop_per_launch": flop_gateup, "avg_us": g["avg_us"]},
         "kernels_us": dict(kern, **kern_all),
         "down_gemm_tflops": round(down_tf, 2),
-        "decode": {"us_per_layer": round(dec_us, 3), "T": 1, "kernels_us": dkern, "roofline": dec_roof,
+        "ablation_host_sync_routing": {"ms_per_step": round(ms_sync, 4), "tok_s": round(T / (ms_sync / 1000.0), 1),
+                                       "slowdown_vs_value": round(ms_sync / ms_per_step, 4)},
+        "decode": {"us_per_layer": round(dec_us, 3), "T": 1, "graph_us_per_layer": round(dec_graph_us, 3),
+                   "kernels_us": dkern, "roofline": dec_roof,
                    "sweep_us_per_layer": sweep, "default_gemv_max_rows": moe.moe_default_gemv_max_rows()},
     }
     if not a.no_cpu_baseline:

@@ -57,6 +57,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
   const int bm = d->tile_rows;
   if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128))
     return fail(MOE_ERR_INVALID_ARGUMENT, "tile_rows must be 0, 16, 32, 64 or 128 (got %d)", bm);
+  if (d->host_sync_routing != 0 && d->host_sync_routing != 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "host_sync_routing must be 0 or 1 (got %d)", d->host_sync_routing);
   return MOE_OK;
 }
 
@@ -350,7 +352,17 @@ moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_
   const RouteOut o = ws_route(ws, w);
   TRY(run_route(d, x, Tc, wr, bias, o, s));
   const ChunkArgs C = chunk_args(d, x, Tc, o, ws, w, y);
-  const int mt = (int)max_sched_for(d, Tc);
+  int mt = (int)max_sched_for(d, Tc);
+  if (d->host_sync_routing) {
+    // Measurement of the host round trip: read the schedule's entry count
+    // back, wait for it, and size the GEMM grids from it.
+    int32_t hdr[4] = {0, 0, 0, 0};
+    hipError_t e = hipMemcpyAsync(hdr, o.sched, sizeof(hdr), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "routing read-back: %s", hipGetErrorString(e));
+    if (hdr[0] < 0 || hdr[0] > mt) return fail(MOE_ERR_HIP, "routing read-back: bad entry count %d", hdr[0]);
+    mt = hdr[0];
+  }
   TRY(timed(3, s, "gate/up GEMM", [&](const KTime& kt) { return launch_gateup_gemm(L, C, mt, s, kt); }));
   TRY(timed(4, s, "down GEMM", [&](const KTime& kt) { return launch_down_gemm(L, C, mt, s, kt); }));
   TRY(timed(7, s, "combine", [&](const KTime& kt) { return launch_combine(L, C, s, kt); }));

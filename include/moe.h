@@ -74,6 +74,12 @@ typedef struct {
     int32_t max_chunk;     /* tokens per prefill chunk (1..8192); routing metadata is per chunk */
     int32_t tile_rows;     /* BM: rows per tile of the block map; 0 = library default (128);
                               one of 16, 32, 64, 128 */
+    int32_t host_sync_routing; /* 0 (the normal path): routing never returns to the host.  1: a
+                              measurement of the alternative the pages argue against ("Keep expert
+                              routing on the GPU"): after each chunk's routing, the grouped-GEMM path
+                              copies the schedule's entry count to the host, synchronises the stream
+                              and sizes the GEMM launches from it.  Same kernels and results; the
+                              call then blocks and cannot be captured in a graph. */
 } moe_layer_desc;
 
 /*

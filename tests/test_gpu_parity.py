@@ -309,6 +309,62 @@ def test_repeat_calls_bit_identical(M):
     assert torch.equal(d1, d2)
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_graph_replays_match_eager(M, T):
+    """Decode captured in a HIP graph (the calls enqueue kernels only: no
+    allocation, copy, memset or host synchronisation), replayed several times
+    with other eager work in between; every replay equals the eager call on
+    the same rows bit for bit, and the oracle within tolerance."""
+    case = mi.make_case("decode")
+    lay = get_layer(M, case)
+    H = case["cfg"]["H"]
+    rows = [mi.gen_x(T, H, 9000 + r) for r in range(3)]
+    eager = []
+    for r in rows:
+        eager.append(lay.forward_decode(dev(M, r), None).clone())
+    torch.cuda.synchronize()
+    x_static = dev(M, rows[0]).clone()
+    y_static = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lay.forward_decode(x_static, None, y_static)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lay.forward_decode(x_static, None, y_static)
+    other = dev(M, mi.gen_x(2, H, 9100))
+    for rep in range(2):
+        for i, r in enumerate(rows):
+            x_static.copy_(dev(M, r))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_static, eager[i]), (rep, i)
+            lay.forward_decode(other, None)  # eager work between replays
+            torch.cuda.synchronize()
+    sub = dict(case, x=rows[-1], T=T)
+    check_close(y_static.cpu().numpy(), oracle_rows(sub), f"decode graph replay T={T}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill512"])
+def test_host_sync_routing_same_result(M, name):
+    """The host-synchronised routing measurement (schedule size read back,
+    GEMM grids sized on the host) runs the same kernels: same bits as the
+    normal path."""
+    case = mi.make_case(name)
+    lay = get_layer(M, case)
+    x, b = dev(M, case["x"]), dev(M, case["bias"])
+    y0 = lay.forward_prefill(x, b).clone()
+    lay.set_desc(host_sync_routing=1)
+    try:
+        y1 = lay.forward_prefill(x, b)
+        torch.cuda.synchronize()
+    finally:
+        lay.set_desc(host_sync_routing=0)
+    assert torch.equal(y0, y1)
+
+
 def test_zero_tokens_is_noop(M):
     case = mi.make_case("tiny")
     lay = get_layer(M, case)
