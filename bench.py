@@ -200,6 +200,24 @@ def main():
     for lay in layers:
         lay.set_desc(host_sync_routing=0)
 
+    # Measurement of the other design the pages argue against: the active
+    # experts rebuilt as fp16 in HBM by a pass of their own, then the grouped
+    # GEMMs read fp16 weights (same rounding, same results).
+    for lay in layers:
+        lay.set_desc(dequant_pass=1)
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    h0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    h1.record(stream)
+    torch.cuda.synchronize()
+    ms_dq = h0.elapsed_time(h1) / a.steps
+    kern_dq = breakdown(prefill_pass, [moe.K_DEQUANT, moe.K_GATEUP_GEMM, moe.K_DOWN_GEMM])
+    for lay in layers:
+        lay.set_desc(dequant_pass=0)
+
     # Dominant kernel: gate/up grouped GEMM, one launch per 2048-token chunk.
     Tc = 2048
     flop_gateup = 2.0 * (Tc * k + Tc) * H * (2 * I)
@@ -331,6 +349,8 @@ def main():
         "down_gemm_tflops": round(down_tf, 2),
         "ablation_host_sync_routing": {"ms_per_step": round(ms_sync, 4), "tok_s": round(T / (ms_sync / 1000.0), 1),
                                        "slowdown_vs_value": round(ms_sync / ms_per_step, 4)},
+        "ablation_dequant_pass": {"ms_per_step": round(ms_dq, 4), "tok_s": round(T / (ms_dq / 1000.0), 1),
+                                  "slowdown_vs_value": round(ms_dq / ms_per_step, 4), "kernels_us": kern_dq},
         "decode": {"us_per_layer": round(dec_us, 3), "T": 1, "graph_us_per_layer": round(dec_graph_us, 3),
                    "kernels_us": dkern, "roofline": dec_roof,
                    "sweep_us_per_layer": sweep, "default_gemv_max_rows": moe.moe_default_gemv_max_rows()},

@@ -17,10 +17,11 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED_SH
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP", 5: "MOE_ERR_DEVICE_UNSUPPORTED"}
 
 # Kernel ids of moe_profile_read.
-K_LOGITS, K_TOPK, K_META, K_GATEUP_GEMM, K_DOWN_GEMM, K_GATEUP_GEMV, K_DOWN_GEMV, K_COMBINE = range(8)
+K_LOGITS, K_TOPK, K_META, K_GATEUP_GEMM, K_DOWN_GEMM, K_GATEUP_GEMV, K_DOWN_GEMV, K_COMBINE, K_DEQUANT = range(9)
 KERNEL_NAMES = {K_LOGITS: "k_screen|k_logits_small", K_TOPK: "k_route_exact", K_META: "k_meta|k_topk_meta",
                 K_GATEUP_GEMM: "k_gateup_gemm", K_DOWN_GEMM: "k_down_gemm",
-                K_GATEUP_GEMV: "k_gemv_experts", K_DOWN_GEMV: "k_gemv_reduce", K_COMBINE: "k_combine"}
+                K_GATEUP_GEMV: "k_gemv_experts", K_DOWN_GEMV: "k_gemv_reduce", K_COMBINE: "k_combine",
+                K_DEQUANT: "k_dequant_active"}
 
 
 class MoEError(RuntimeError):
@@ -32,7 +33,7 @@ class MoEError(RuntimeError):
 class LayerDesc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("hidden", "n_experts", "top_k", "inter", "shared_inter",
                                          "group_size", "gemv_max_rows", "max_chunk", "tile_rows",
-                                         "host_sync_routing")]
+                                         "host_sync_routing", "dequant_pass")]
 
 
 class QMatrix(C.Structure):
@@ -98,9 +99,9 @@ def _stream(stream):
 
 
 def make_desc(hidden, n_experts, top_k, inter, shared_inter, gemv_max_rows=-1, max_chunk=2048,
-              tile_rows=0, group_size=64, host_sync_routing=0) -> LayerDesc:
+              tile_rows=0, group_size=64, host_sync_routing=0, dequant_pass=0) -> LayerDesc:
     return LayerDesc(hidden, n_experts, top_k, inter, shared_inter, group_size, gemv_max_rows,
-                     max_chunk, tile_rows, host_sync_routing)
+                     max_chunk, tile_rows, host_sync_routing, dequant_pass)
 
 
 def moe_packed_bytes(desc: LayerDesc) -> int:

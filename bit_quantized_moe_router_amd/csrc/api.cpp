@@ -59,6 +59,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "tile_rows must be 0, 16, 32, 64 or 128 (got %d)", bm);
   if (d->host_sync_routing != 0 && d->host_sync_routing != 1)
     return fail(MOE_ERR_INVALID_ARGUMENT, "host_sync_routing must be 0 or 1 (got %d)", d->host_sync_routing);
+  if (d->dequant_pass != 0 && d->dequant_pass != 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "dequant_pass must be 0 or 1 (got %d)", d->dequant_pass);
   return MOE_OK;
 }
 
@@ -97,7 +99,7 @@ Blob blob_geom(const moe_layer_desc* d) {
 
 struct Ws {
   size_t logits, wnorm, xsum, x16, ids, tw, counts, offsets, sorted, inv, tiles, sched, n_tiles, active, n_active, segs,
-      hbuf, obuf, dpart;
+      hbuf, obuf, dpart, wdq;
   size_t total;
 };
 
@@ -132,6 +134,9 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   w.obuf = o;
   w.dpart = o;
   o += al(Tc * k * H * 2 > dpart_bytes ? Tc * k * H * 2 : dpart_bytes);
+  // Separate-dequant measurement only: an fp16 copy of the blob's blocks.
+  w.wdq = o;
+  if (d->dequant_pass) o += al(blob_geom(d).total / kBlockBytes * kDqBlockBytes);
   w.total = o;
   return w;
 }
@@ -173,7 +178,7 @@ int max_long_tiles(const moe_layer_desc* d) {
 }
 
 // ---- kernel timing (measurement mode) ----------------------------------------
-constexpr int kNumKernels = 8;
+constexpr int kNumKernels = 9;
 struct Pending {
   int kid;
   hipEvent_t a, b;
@@ -249,6 +254,7 @@ LayerArgs layer_args(const moe_layer_desc* d, const void* packed) {
   L.gateup_bytes = b.gateup_bytes;
   L.shared_base = b.shared_base;
   L.shared_gateup_bytes = b.shared_gateup_bytes;
+  L.wdq = nullptr;
   return L;
 }
 
@@ -352,6 +358,11 @@ moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_
   const RouteOut o = ws_route(ws, w);
   TRY(run_route(d, x, Tc, wr, bias, o, s));
   const ChunkArgs C = chunk_args(d, x, Tc, o, ws, w, y);
+  LayerArgs Lc = L;
+  if (d->dequant_pass) {
+    Lc.wdq = at<uint8_t>(ws, w.wdq);
+    TRY(timed(8, s, "separate dequant", [&](const KTime& kt) { return launch_dequant_active(Lc, C, s, kt); }));
+  }
   int mt = (int)max_sched_for(d, Tc);
   if (d->host_sync_routing) {
     // Measurement of the host round trip: read the schedule's entry count
@@ -363,9 +374,9 @@ moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_
     if (hdr[0] < 0 || hdr[0] > mt) return fail(MOE_ERR_HIP, "routing read-back: bad entry count %d", hdr[0]);
     mt = hdr[0];
   }
-  TRY(timed(3, s, "gate/up GEMM", [&](const KTime& kt) { return launch_gateup_gemm(L, C, mt, s, kt); }));
-  TRY(timed(4, s, "down GEMM", [&](const KTime& kt) { return launch_down_gemm(L, C, mt, s, kt); }));
-  TRY(timed(7, s, "combine", [&](const KTime& kt) { return launch_combine(L, C, s, kt); }));
+  TRY(timed(3, s, "gate/up GEMM", [&](const KTime& kt) { return launch_gateup_gemm(Lc, C, mt, s, kt); }));
+  TRY(timed(4, s, "down GEMM", [&](const KTime& kt) { return launch_down_gemm(Lc, C, mt, s, kt); }));
+  TRY(timed(7, s, "combine", [&](const KTime& kt) { return launch_combine(Lc, C, s, kt); }));
   return MOE_OK;
 }
 

@@ -52,7 +52,13 @@ struct LayerArgs {
   int64_t gateup_bytes;         // routed gate/up region
   int64_t shared_base;          // byte offset of the shared expert
   int64_t shared_gateup_bytes;  // shared gate/up region
+  // Separate-dequant measurement only (else null): fp16 weights, each 1152-byte
+  // block of the blob expanded to 4096 bytes at the same block index; in a
+  // block, the 8 weights of lane l for MFMA k-step c sit at c * 1024 + l * 16.
+  uint8_t* wdq;
 };
+
+constexpr int kDqBlockBytes = 4096;
 
 struct ChunkArgs {
   const uint16_t* x;      // [T][H] bf16

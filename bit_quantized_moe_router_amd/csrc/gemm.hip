@@ -50,6 +50,8 @@
 // routing kernel's longest-first order (full tiles before partial ones).
 #include "launch.h"
 
+#include <type_traits>
+
 namespace moe {
 
 constexpr int kTileRows = 128;                 // largest tile the kernel takes
@@ -108,13 +110,19 @@ struct QGroup {
   uint32_t s0, s1;
 };
 
+// Pre-dequantised weights of one K group for the wave's 2 blocks (the
+// separate-dequant measurement): the fp16 B operands of the group's 4 k-steps.
+struct QGroupP {
+  uint4 b0[4], b1[4];
+};
+
 // Per-workgroup tile description.
 struct Tile {
   int e, r0, rows, rowbase, ncols, G, ct;
   bool shared;
 };
 
-template <bool kGateUp, int NF>
+template <bool kGateUp, int NF, bool kPre>
 __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C, const Tile& T, uint8_t* smem) {
   const int H = L.H;
   const int G = T.G;
@@ -144,19 +152,34 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
     qb0 = wbase + (int64_t)n0 * G * kBlockBytes;
     qb1 = wbase + (int64_t)n1 * G * kBlockBytes;
   }
-  auto load_q = [&](int g, QGroup& q) {
-    const int64_t off = (int64_t)(g < G ? g : G - 1) * qstride;
-    q.c0 = *reinterpret_cast<const uint4*>(qb0 + off + lane * 16);
-    q.c1 = *reinterpret_cast<const uint4*>(qb1 + off + lane * 16);
-    q.s0 = *reinterpret_cast<const uint32_t*>(qb0 + off + kCodeBytes + col * 4);
-    q.s1 = *reinterpret_cast<const uint32_t*>(qb1 + off + kCodeBytes + col * 4);
+  // Separate-dequant measurement: the same blocks in the fp16 copy.
+  const uint8_t* pb0 = kPre ? L.wdq + (qb0 - L.blob) / kBlockBytes * kDqBlockBytes : nullptr;
+  const uint8_t* pb1 = kPre ? L.wdq + (qb1 - L.blob) / kBlockBytes * kDqBlockBytes : nullptr;
+  const int64_t pstride = qstride / kBlockBytes * kDqBlockBytes;
+  using QG = typename std::conditional<kPre, QGroupP, QGroup>::type;
+  auto load_q = [&](int g, QG& q) {
+    if constexpr (kPre) {
+      // Groups padded past G read as zero weights.
+      const int64_t off = (int64_t)(g < G ? g : G - 1) * pstride;
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        q.b0[c] = g < G ? *reinterpret_cast<const uint4*>(pb0 + off + c * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
+        q.b1[c] = g < G ? *reinterpret_cast<const uint4*>(pb1 + off + c * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const int64_t off = (int64_t)(g < G ? g : G - 1) * qstride;
+      q.c0 = *reinterpret_cast<const uint4*>(qb0 + off + lane * 16);
+      q.c1 = *reinterpret_cast<const uint4*>(qb1 + off + lane * 16);
+      q.s0 = *reinterpret_cast<const uint32_t*>(qb0 + off + kCodeBytes + col * 4);
+      q.s1 = *reinterpret_cast<const uint32_t*>(qb1 + off + kCodeBytes + col * 4);
+    }
   };
   // ---- token of each row (gate/up gathers activation rows by token) ----
   // The index load goes out before the first weight codes so that waiting
   // for it leaves those in flight.
   int my_tok = 0;
   if (kGateUp && tid < kTileRows && tid < T.rows) my_tok = T.shared ? T.r0 + tid : C.sorted[T.rowbase + tid];
-  QGroup q0, q1, q2, q3;
+  QG q0, q1, q2, q3;
   load_q(0, q0);
   if (kGateUp) {
     if (tid < kTileRows) tok[tid] = T.shared ? my_tok : my_tok / L.k;
@@ -217,14 +240,17 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   // MFMAs of one K group (codes q, A buffer `cur`), software pipelined: the
   // A fragments and weights of k-step c+1 (for c = 3: k-step 0 of the next
   // group, codes qn) are read and rebuilt while the MFMAs of k-step c run.
-  auto compute = [&](int cur, const QGroup& q, const QGroup& qn, bool live, bool live_n) {
+  auto compute = [&](int cur, const QG& q, const QG& qn, bool live, bool live_n) {
     f16x2v_t s20, b20, s21, b21, n20, m20, n21, m21;
-    sbpair(q.s0, live, s20, b20);
-    sbpair(q.s1, live, s21, b21);
-    sbpair(qn.s0, live_n, n20, m20);
-    sbpair(qn.s1, live_n, n21, m21);
-    const uint32_t cw0[4] = {q.c0.x, q.c0.y, q.c0.z, q.c0.w};
-    const uint32_t cw1[4] = {q.c1.x, q.c1.y, q.c1.z, q.c1.w};
+    uint32_t cw0[4], cw1[4];
+    if constexpr (!kPre) {
+      sbpair(q.s0, live, s20, b20);
+      sbpair(q.s1, live, s21, b21);
+      sbpair(qn.s0, live_n, n20, m20);
+      sbpair(qn.s1, live_n, n21, m21);
+      cw0[0] = q.c0.x; cw0[1] = q.c0.y; cw0[2] = q.c0.z; cw0[3] = q.c0.w;
+      cw1[0] = q.c1.x; cw1[1] = q.c1.y; cw1[2] = q.c1.z; cw1[3] = q.c1.w;
+    }
     const uint8_t* abase = at + cur * kABufBytes + aoff0;
     f16x8_t av[NF];
 #pragma unroll
@@ -235,11 +261,21 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
       if (c < 3) {
 #pragma unroll
         for (int f = 0; f < NF; f++) an[f] = *reinterpret_cast<const f16x8_t*>(abase + f * 32 * kARow + (c + 1) * 16);
-        bn0 = dequant8(cw0[c + 1], s20, b20);
-        bn1 = dequant8(cw1[c + 1], s21, b21);
+        if constexpr (kPre) {
+          bn0 = __builtin_bit_cast(f16x8_t, q.b0[c + 1]);
+          bn1 = __builtin_bit_cast(f16x8_t, q.b1[c + 1]);
+        } else {
+          bn0 = dequant8(cw0[c + 1], s20, b20);
+          bn1 = dequant8(cw1[c + 1], s21, b21);
+        }
       } else {
-        bn0 = dequant8(qn.c0.x, n20, m20);
-        bn1 = dequant8(qn.c1.x, n21, m21);
+        if constexpr (kPre) {
+          bn0 = __builtin_bit_cast(f16x8_t, qn.b0[0]);
+          bn1 = __builtin_bit_cast(f16x8_t, qn.b1[0]);
+        } else {
+          bn0 = dequant8(qn.c0.x, n20, m20);
+          bn1 = dequant8(qn.c1.x, n21, m21);
+        }
       }
 #pragma unroll
       for (int f = 0; f < NF; f++) {
@@ -264,7 +300,7 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
     if (wave_cols) compute(CUR, Q, QN, (g) < G, (g) + 1 < G);  \
     MOE_STORE_A((CUR) ^ 1, as);               \
     MOE_LOAD_A((g) + 2, as);                  \
-    load_q((g) + 4, Q);                       \
+    load_q((g) + (kPre ? 2 : 4), Q);          \
     __syncthreads();                          \
   } while (0)
 
@@ -273,16 +309,23 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   // groups 1..3 in flight.
   MOE_LOAD_A(0, as);
   load_q(1, q1);
-  load_q(2, q2);
-  load_q(3, q3);
+  if constexpr (!kPre) {
+    load_q(2, q2);
+    load_q(3, q3);
+  }
   MOE_STORE_A(0, as);
   MOE_LOAD_A(1, as);
   if (wave_cols) {
-    f16x2v_t s20, b20, s21, b21;
-    sbpair(q0.s0, true, s20, b20);
-    sbpair(q0.s1, true, s21, b21);
-    bc0 = dequant8(q0.c0.x, s20, b20);
-    bc1 = dequant8(q0.c1.x, s21, b21);
+    if constexpr (kPre) {
+      bc0 = __builtin_bit_cast(f16x8_t, q0.b0[0]);
+      bc1 = __builtin_bit_cast(f16x8_t, q0.b1[0]);
+    } else {
+      f16x2v_t s20, b20, s21, b21;
+      sbpair(q0.s0, true, s20, b20);
+      sbpair(q0.s1, true, s21, b21);
+      bc0 = dequant8(q0.c0.x, s20, b20);
+      bc1 = dequant8(q0.c1.x, s21, b21);
+    }
   }
   __syncthreads();
 
@@ -291,10 +334,17 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   // across the back edge instead of draining them at the loop header.
   const int Gp = (G + 3) & ~3;
   for (int g = 0; g < Gp; g += 4) {
-    MOE_GEMM_STEP(g, 0, q0, q1, ao);
-    MOE_GEMM_STEP(g + 1, 1, q1, q2, ae);
-    MOE_GEMM_STEP(g + 2, 0, q2, q3, ao);
-    MOE_GEMM_STEP(g + 3, 1, q3, q0, ae);
+    if constexpr (kPre) {  // two register sets: codes of g+2 into the set g used
+      MOE_GEMM_STEP(g, 0, q0, q1, ao);
+      MOE_GEMM_STEP(g + 1, 1, q1, q0, ae);
+      MOE_GEMM_STEP(g + 2, 0, q0, q1, ao);
+      MOE_GEMM_STEP(g + 3, 1, q1, q0, ae);
+    } else {
+      MOE_GEMM_STEP(g, 0, q0, q1, ao);
+      MOE_GEMM_STEP(g + 1, 1, q1, q2, ae);
+      MOE_GEMM_STEP(g + 2, 0, q2, q3, ao);
+      MOE_GEMM_STEP(g + 3, 1, q3, q0, ae);
+    }
   }
 #undef MOE_GEMM_STEP
 #undef MOE_LOAD_A
@@ -354,7 +404,7 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   }
 }
 
-template <bool kGateUp>
+template <bool kGateUp, bool kPre>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_expert_gemm(LayerArgs L, ChunkArgs C, int n_ct) {
   // ---- workgroup -> (tile, column tile), XCD-aware ----
@@ -383,13 +433,13 @@ void k_expert_gemm(LayerArgs L, ChunkArgs C, int n_ct) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int nf = (T.rows + 31) >> 5;
   if (nf <= 1)
-    gemm_tile<kGateUp, 1>(L, C, T, smem);
+    gemm_tile<kGateUp, 1, kPre>(L, C, T, smem);
   else if (nf == 2)
-    gemm_tile<kGateUp, 2>(L, C, T, smem);
+    gemm_tile<kGateUp, 2, kPre>(L, C, T, smem);
   else if (nf == 3)
-    gemm_tile<kGateUp, 3>(L, C, T, smem);
+    gemm_tile<kGateUp, 3, kPre>(L, C, T, smem);
   else
-    gemm_tile<kGateUp, 4>(L, C, T, smem);
+    gemm_tile<kGateUp, 4, kPre>(L, C, T, smem);
 }
 
 // y[t] = (shared expert's output, already in y) + sum_j w_tj * 256 * obuf[pos(t, j)]
@@ -433,28 +483,73 @@ int gateup_col_tiles(int I, int Is) {
   return (Imax + kGateUpColsPerWg - 1) / kGateUpColsPerWg;
 }
 
-template <bool kGateUp>
+template <bool kGateUp, bool kPre>
 static hipError_t launch_expert_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
                                      const KTime& kt) {
   constexpr int smem = kGateUp ? kSmemGateUp : kSmemDown;
   static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_expert_gemm<kGateUp>), smem, lds_set);
+  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_expert_gemm<kGateUp, kPre>), smem, lds_set);
   if (e != hipSuccess) return e;
   const int n_ct = kGateUp ? gateup_col_tiles(L.I, L.Is) : (L.H + kDownColsPerWg - 1) / kDownColsPerWg;
   const int tiles8 = (max_sched + 7) / 8 * 8;
-  MOE_LAUNCH(k_expert_gemm<kGateUp>, dim3((unsigned)(tiles8 * n_ct)), dim3(kWaves * 64), smem, s, kt.start, kt.stop,
-             L, C, n_ct);
+  MOE_LAUNCH((k_expert_gemm<kGateUp, kPre>), dim3((unsigned)(tiles8 * n_ct)), dim3(kWaves * 64), smem, s, kt.start,
+             kt.stop, L, C, n_ct);
   return hipGetLastError();
 }
 
 hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
                               const KTime& kt) {
-  return launch_expert_gemm<true>(L, C, max_sched, s, kt);
+  return L.wdq ? launch_expert_gemm<true, true>(L, C, max_sched, s, kt)
+               : launch_expert_gemm<true, false>(L, C, max_sched, s, kt);
 }
 
 hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
                             const KTime& kt) {
-  return launch_expert_gemm<false>(L, C, max_sched, s, kt);
+  return L.wdq ? launch_expert_gemm<false, true>(L, C, max_sched, s, kt)
+               : launch_expert_gemm<false, false>(L, C, max_sched, s, kt);
+}
+
+// ---------------------------------------------------------------------------
+// Separate-dequant measurement ("Optimizing on-device inference for Apple
+// Silicon", section "Dequantise weights during matrix multiplication": the
+// alternative of rebuilding the weights in a pass of their own): the chunk's
+// active experts and the shared expert rebuilt as fp16 into L.wdq, block by
+// block, with the same rounding as the fused path (dequant8), so the GEMMs
+// that read them give the same bits.  grid = (E + 1 expert slots, kDqSplit).
+// ---------------------------------------------------------------------------
+constexpr int kDqSplit = 16;
+
+__global__ __launch_bounds__(256) void k_dequant_active(LayerArgs L, ChunkArgs C) {
+  const int slot = blockIdx.x;
+  const int nact = *C.n_active;
+  int e;
+  if (slot < nact)
+    e = C.active[slot];
+  else if (slot == nact && L.Is > 0)
+    e = L.E;
+  else
+    return;
+  const int64_t base = e == L.E ? L.shared_base : (int64_t)e * L.expert_bytes;
+  const int64_t bytes = e == L.E ? L.shared_gateup_bytes + (int64_t)(L.H / 32) * (L.Is / 64) * kBlockBytes
+                                 : L.expert_bytes;
+  const int nblk = (int)(bytes / kBlockBytes);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
+  for (int b = blockIdx.y * 4 + wave; b < nblk; b += kDqSplit * 4) {
+    const uint8_t* blk = L.blob + base + (int64_t)b * kBlockBytes;
+    const uint4 q = *reinterpret_cast<const uint4*>(blk + lane * 16);
+    const uint32_t sb = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
+    const _Float16 sh = (_Float16)bf16_bits_to_f32(sb & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(sb >> 16);
+    const f16x2v_t s2 = {sh, sh}, b2 = {bh, bh};
+    uint8_t* dst = L.wdq + (base / kBlockBytes + b) * kDqBlockBytes + lane * 16;
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int c = 0; c < 4; c++) *reinterpret_cast<f16x8_t*>(dst + c * 1024) = dequant8(w[c], s2, b2);
+  }
+}
+
+hipError_t launch_dequant_active(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt) {
+  MOE_LAUNCH(k_dequant_active, dim3((unsigned)(L.E + 1), kDqSplit), dim3(256), 0, s, kt.start, kt.stop, L, C);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt) {

@@ -85,6 +85,9 @@ hipError_t launch_gateup_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sc
                               const KTime& kt = KTime{});
 hipError_t launch_down_gemm(const LayerArgs& L, const ChunkArgs& C, int max_sched, hipStream_t s,
                             const KTime& kt = KTime{});
+// Separate-dequant measurement: the chunk's active experts (and the shared
+// expert) rebuilt as fp16 into L.wdq; the GEMMs then read B from there.
+hipError_t launch_dequant_active(const LayerArgs& L, const ChunkArgs& C, hipStream_t s, const KTime& kt = KTime{});
 // Gate/up column tiles per row tile (the GEMM grid's second dimension).
 int gateup_col_tiles(int I, int Is);
 // Grouped-GEMM workgroups resident per compute unit.

@@ -80,6 +80,12 @@ typedef struct {
                               copies the schedule's entry count to the host, synchronises the stream
                               and sizes the GEMM launches from it.  Same kernels and results; the
                               call then blocks and cannot be captured in a graph. */
+    int32_t dequant_pass;  /* 0 (the normal path): weights are rebuilt inside the grouped GEMMs.  1: a
+                              measurement of the alternative the pages compare against ("Dequantise
+                              weights during matrix multiplication"): each chunk's active experts and
+                              the shared expert are first rebuilt as fp16 into the workspace (a
+                              separate pass), then the grouped GEMMs read fp16 weights.  Same rounding,
+                              same results; the workspace grows by 4096/1152 x the packed size. */
 } moe_layer_desc;
 
 /*
@@ -204,7 +210,7 @@ const char *moe_last_error(void);
  *   the decode GEMV path), 3 = gate/up grouped GEMM, 4 = down grouped GEMM,
  *   5 = top-k + gate/up GEMV + split down GEMV (decode GEMV path), 6 = sum of
  *   the decode path's partial outputs, 7 = per-token combine of the
- *   grouped-GEMM path
+ *   grouped-GEMM path, 8 = separate dequant pass (dequant_pass = 1)
  */
 moe_status moe_profile_enable(int32_t mask);
 moe_status moe_profile_reset(void);

@@ -56,7 +56,7 @@ def test_workspace_and_tile_bounds():
     (dict(group_size=32), 2), (dict(hidden=1028), 2), (dict(inter=772), 2), (dict(shared_inter=100), 2),
     (dict(top_k=9, n_experts=8), 1), (dict(top_k=0), 1), (dict(n_experts=0), 2), (dict(n_experts=1024), 2),
     (dict(tile_rows=48), 1), (dict(tile_rows=256), 1), (dict(max_chunk=0), 1), (dict(gemv_max_rows=9), 1),
-    (dict(host_sync_routing=2), 1),
+    (dict(host_sync_routing=2), 1), (dict(dequant_pass=-1), 1),
 ])
 def test_invalid_desc_rejected(kw, status):
     with pytest.raises(moe.MoEError) as ei:

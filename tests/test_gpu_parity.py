@@ -400,6 +400,31 @@ def test_batch_invariant_gemv_path(M):
             assert torch.equal(y[i], y1[i][0]), (T, i)
 
 
+@pytest.mark.parametrize("name", ["tiny", "prefill512"])
+def test_dequant_pass_same_result(M, name):
+    """The separate-dequant measurement (active experts rebuilt as fp16 into
+    the workspace, GEMMs reading them) rounds every weight as the fused path
+    does: same bits, and the dequant kernel is the one that ran."""
+    from bit_quantized_moe_router_amd import K_DEQUANT, moe_profile_enable, moe_profile_read, moe_profile_reset
+    case = mi.make_case(name)
+    lay = get_layer(M, case)
+    x, b = dev(M, case["x"]), dev(M, case["bias"])
+    y0 = lay.forward_prefill(x, b).clone()
+    lay.set_desc(dequant_pass=1)
+    moe_profile_reset()
+    moe_profile_enable(1 << K_DEQUANT)
+    try:
+        y1 = lay.forward_prefill(x, b)
+        torch.cuda.synchronize()
+        ran = moe_profile_read(K_DEQUANT)[1]
+    finally:
+        moe_profile_enable(0)
+        moe_profile_reset()
+        lay.set_desc(dequant_pass=0)
+    assert ran >= 1
+    assert torch.equal(y0, y1)
+
+
 def test_zero_tokens_is_noop(M):
     case = mi.make_case("tiny")
     lay = get_layer(M, case)
