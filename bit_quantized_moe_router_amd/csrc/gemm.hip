@@ -7,11 +7,12 @@
 //
 // Workgroup = 4 waves (one per SIMD) over a tile of up to 128 rows of one
 // expert; two workgroups share a compute unit, so one's prologue and
-// epilogue run under the other's MFMAs.  Each wave owns 2 weight blocks of 32 columns (gate/up: one block
-// of gate and the same block of up; down: 2 output blocks) and all rows of
-// the tile: up to 4 x 2 accumulators of v_mfma_f32_32x32x16_f16 (fp32).  The
-// kernel is instantiated per number of 32-row fragments the tile needs
-// (1..4), so small tiles issue only the MFMAs of their rows.
+// epilogue run under the other's MFMAs.  Each wave owns 2 weight blocks of 32
+// columns (gate/up: one block of gate and the same block of up; down: 2
+// output blocks) and all rows of the tile: up to 4 x 2 accumulators of
+// v_mfma_f32_32x32x16_f16 (fp32).  The kernel is instantiated per number of
+// 32-row fragments the tile needs (1..4), so small tiles issue only the MFMAs
+// of their rows.
 //
 // Weights stay 4-bit in HBM and never pass through LDS: the packed layout puts
 // each lane's 16 bytes of codes exactly where the MFMA B operand needs them,
@@ -21,11 +22,15 @@
 // before the token indices of the tile are known.
 //
 // Activations (gathered token rows for gate/up, the expert's contiguous rows
-// of the intermediate for down) are shared by the 8 waves through LDS: per K
-// group the workgroup stages 128 rows x 64 columns (double buffered, one
-// barrier per group); each thread moves four 16-byte pieces, loaded one group
-// ahead into one register set.  Rows past the tile's
-// count reuse a valid row and are never stored.
+// of the intermediate for down) are shared by the 4 waves through LDS: per K
+// group the workgroup stages up to 128 rows x 64 columns (double buffered,
+// one barrier per group); each thread moves up to four 16-byte pieces, loaded
+// one group ahead into one register set.  Rows past the tile's count reuse a
+// valid row and are never stored.
+//
+// A second instantiation (kPre) serves the separate-dequant measurement: the
+// same kernel reading fp16 weights rebuilt beforehand by k_dequant_active
+// instead of rebuilding them from the codes.
 //
 // Results leave through LDS: the workgroup's output tile is assembled there
 // and written back as whole rows with 16-byte stores (the shared expert's
