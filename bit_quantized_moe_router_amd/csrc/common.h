@@ -107,6 +107,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// bf16 bits -> fp16 bits of value / 256 (exact whenever the result is normal).
+__device__ __forceinline__ uint16_t f32_to_f16_scaled(uint16_t b) {
+  return __builtin_bit_cast(uint16_t, (_Float16)(bf16_bits_to_f32(b) * 0.00390625f));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);

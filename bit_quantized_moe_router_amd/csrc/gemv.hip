@@ -6,11 +6,14 @@
 // With one to a few rows the layer is bound by weight bytes, so each expert's
 // packed weights are streamed once.  A wave reads one 1152-byte gate or up
 // block (32 output rows x one 64-column group) with a single 16-byte load per
-// lane, so a lane holds 32 codes of one output row; every wave issues the
-// loads of all its blocks before it computes.  Codes expand to bf16 pairs
-// (128 + q) and meet the activation pairs in v_dot2_f32_bf16; the per-group
-// affine fold is
-//   acc += s * dot + (b - 128 s) * sum(x over the group).
+// lane, so a lane holds 32 codes of one output row, in the lane order of the
+// MFMA B operand; every wave issues the loads of all its blocks before it
+// computes.  Gate/up runs on v_mfma_f32_32x32x16_f16 with the rows (up to 8)
+// as the A operand: the expansion of the codes to fp16 is the only per-code
+// vector work, and the per-group scale and bias are applied to the group's
+// dot products (affine fold) instead of to every weight.  The down projection
+// expands codes to bf16 pairs (128 + q) for v_dot2_f32_bf16 with h, folded as
+//   acc += s * dot + (b - 128 s) * sum(h over the group).
 // The down projection is split along the intermediate: the workgroup that
 // produced 32 columns of h applies the matching 32 columns of the down matrix
 // (half of each down block, loaded in the same round as gate/up) and writes a
@@ -22,6 +25,30 @@
 namespace moe {
 
 constexpr int kGemvMaxRows = 8;
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// 8 bf16 activations -> fp16 of value / 256.
+__device__ __forceinline__ uint4 to_f16x8_scaled(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) o[j] = f32_to_f16_scaled(w[j] & 0xFFFFu) | ((uint32_t)f32_to_f16_scaled(w[j] >> 16) << 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b) { return (a & mask) | b; }
+
+// The 8 codes of one dword as fp16 pairs for k-slots 0..7 of an MFMA step
+// (slot 2i holds nibble i, slot 2i+1 nibble i+4): slots {0,1,4,5} get
+// 1024 + q (the nibble in mantissa bits 0-3 of 1024), slots {2,3,6,7} get
+// 64 + q (the nibble in bits 4-7, which weigh 1/16 at the exponent of 64).
+__device__ __forceinline__ void expand_codes_f16(uint32_t d, uint32_t m1024, uint32_t m64, uint32_t out[4]) {
+  const uint32_t d8 = d >> 8;
+  out[0] = and_or(d, 0x000F000Fu, m1024);
+  out[1] = and_or(d, 0x00F000F0u, m64);
+  out[2] = and_or(d8, 0x000F000Fu, m1024);
+  out[3] = and_or(d8, 0x00F000F0u, m64);
+}
 constexpr int kGuPref = 4;     // groups per wave whose gate/up loads are issued together
 constexpr int kMaxGroups = 128;              // H / 64 for H <= 8192
 constexpr int kMaxAssign = kGemvMaxRows * 16; // T * k on the GEMV path
@@ -103,10 +130,13 @@ __global__ __launch_bounds__(kFuThreads) void k_gemv_experts(LayerArgs L, ChunkA
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];  // [T][H] x rows, then [T][2E+16] top-k lists
+  // [T][H] x rows as fp16(x / 256), then [T][2E+16] top-k lists
+  extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
   uint16_t* xl = reinterpret_cast<uint16_t*>(gsm);
   int* lists = reinterpret_cast<int*>(gsm + (size_t)T * H * 2);
-  __shared__ float xs[kGemvMaxRows * kMaxGroups];
+  // [g][row] sums of the fp16 activations over the slots biased by 1024 (xsa) and by 64 (xsb)
+  __shared__ __attribute__((aligned(16))) float xsa[kMaxGroups * kGemvMaxRows];
+  __shared__ __attribute__((aligned(16))) float xsb[kMaxGroups * kGemvMaxRows];
   __shared__ int s_ids[kMaxAssign];
   __shared__ float s_tw[kMaxAssign];
   __shared__ uint32_t s_bm[kMaxE / 32];
@@ -122,10 +152,10 @@ __global__ __launch_bounds__(kFuThreads) void k_gemv_experts(LayerArgs L, ChunkA
   if (tid + kFuThreads < nx) xr1 = reinterpret_cast<const uint4*>(C.x)[tid + kFuThreads];
   // ---- top-k of each row ----
   if (wave < T) topk_small(logits + (int64_t)wave * E, E, k, wave, s_ids, s_tw, lists + wave * (2 * E + 16));
-  if (tid < nx) reinterpret_cast<uint4*>(xl)[tid] = xr0;
-  if (tid + kFuThreads < nx) reinterpret_cast<uint4*>(xl)[tid + kFuThreads] = xr1;
+  if (tid < nx) reinterpret_cast<uint4*>(xl)[tid] = to_f16x8_scaled(xr0);
+  if (tid + kFuThreads < nx) reinterpret_cast<uint4*>(xl)[tid + kFuThreads] = to_f16x8_scaled(xr1);
   for (int i = tid + 2 * kFuThreads; i < nx; i += kFuThreads)
-    reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(C.x)[i];
+    reinterpret_cast<uint4*>(xl)[i] = to_f16x8_scaled(reinterpret_cast<const uint4*>(C.x)[i]);
   if (tid < kMaxE / 32) s_bm[tid] = 0u;
   __syncthreads();
 
@@ -248,78 +278,86 @@ __global__ __launch_bounds__(kFuThreads) void k_gemv_experts(LayerArgs L, ChunkA
   load(wave);
   load_dn(0);
 
-  // Per-group activation sums while the codes are in flight: 8 lanes per
-  // group, 8 columns each, then a 3-step shuffle tree.
-  for (int i0 = 0; i0 < T * G * 8; i0 += kFuThreads) {
-    const int i = i0 + tid, gi = i >> 3, part8 = i & 7;
-    float sm = 0.f;
-    if (gi < T * G) {
-      const int t = gi / G, g = gi - t * G;
-      const uint4 v = *reinterpret_cast<const uint4*>(xl + t * H + g * kGroup + part8 * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; j++) sm += bf16_bits_to_f32(w[j] & 0xFFFFu) + bf16_bits_to_f32(w[j] >> 16);
+  // Per-group activation sums of the workgroup's rows while the codes are in
+  // flight, split by the bias of the slots they meet (columns 8i + {0,1,4,5}
+  // and 8i + {2,3,6,7}): 8 lanes per (row, group), 8 columns each, then a
+  // 3-step shuffle tree.
+  for (int i0 = 0; i0 < rows * G * 8; i0 += kFuThreads) {
+    const int i = i0 + tid, gj = i >> 3, part8 = i & 7;
+    const bool ok = gj < rows * G;
+    const int j = ok ? gj / G : 0, g = gj - j * G;
+    float sa = 0.f, sb = 0.f;
+    if (ok) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xl + tok[j] * H + g * kGroup + part8 * 8);
+      sa = (f16_bits_to_f32(v.x & 0xFFFFu) + f16_bits_to_f32(v.x >> 16)) +
+           (f16_bits_to_f32(v.z & 0xFFFFu) + f16_bits_to_f32(v.z >> 16));
+      sb = (f16_bits_to_f32(v.y & 0xFFFFu) + f16_bits_to_f32(v.y >> 16)) +
+           (f16_bits_to_f32(v.w & 0xFFFFu) + f16_bits_to_f32(v.w >> 16));
     }
-    sm += __shfl_xor(sm, 1);
-    sm += __shfl_xor(sm, 2);
-    sm += __shfl_xor(sm, 4);
-    if (gi < T * G && part8 == 0) xs[gi] = sm;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      sa += __shfl_xor(sa, o);
+      sb += __shfl_xor(sb, o);
+    }
+    if (ok && part8 == 0) {
+      xsa[g * kGemvMaxRows + j] = sa;
+      xsb[g * kGemvMaxRows + j] = sb;
+    }
   }
   __syncthreads();
 
-  // ---- gate/up dot products ----
-  float accg[kGemvMaxRows], accu[kGemvMaxRows];
-#pragma unroll
-  for (int j = 0; j < kGemvMaxRows; j++) accg[j] = accu[j] = 0.f;
+  // ---- gate/up: per group, four v_mfma_f32_32x32x16_f16 steps per matrix ----
+  // A: lane l supplies row m = l % 32 of the workgroup's rows (rows past the
+  // count repeat the last one; their results are never read) with the fp16
+  // activations x' = x / 256 of input columns 32h + 8c .. +7 of the group in
+  // step c, the k-slots the packer gave the lane's codes.  B: the lane's 8
+  // codes of the step as fp16 1024 + q or 64 + q (expand_codes_f16).  Per
+  // group D = sum_k x' (q + o_k), o_k the slot's bias, and with s' = 256 s,
+  // b' = 256 b the affine fold is
+  //   acc += s' D + (b' - 1024 s') Xa + (b' - 64 s') Xb
+  // (Xa, Xb: the row's sums of x' over the slots biased by 1024 and by 64).
+  // The accumulators hold column n = l % 32 and rows 4h + i in register i.
+  uint32_t m1024, m64;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m1024));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(m64));
+  const uint16_t* xrow = xl + tok[(lane & 31) < rows ? (lane & 31) : rows - 1] * H + h * 32;
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   for (int g0 = wave; g0 < G; g0 += kGuPref * kFuWaves) {
     if (g0 != wave) load(g0);
 #pragma unroll
     for (int p = 0; p < kGuPref; p++) {
       const int g = g0 + p * kFuWaves;
       if (g >= G) break;
-      uint32_t qg[16], qu[16];
-      expand_codes(cg[p].x, qg + 0);
-      expand_codes(cg[p].y, qg + 4);
-      expand_codes(cg[p].z, qg + 8);
-      expand_codes(cg[p].w, qg + 12);
-      expand_codes(cu[p].x, qu + 0);
-      expand_codes(cu[p].y, qu + 4);
-      expand_codes(cu[p].z, qu + 8);
-      expand_codes(cu[p].w, qu + 12);
-      const float sg = bf16_bits_to_f32(sbg[p] & 0xFFFFu), bpg = bf16_bits_to_f32(sbg[p] >> 16) - 128.f * sg;
-      const float su = bf16_bits_to_f32(sbu[p] & 0xFFFFu), bpu = bf16_bits_to_f32(sbu[p] >> 16) - 128.f * su;
+      const uint32_t cgw[4] = {cg[p].x, cg[p].y, cg[p].z, cg[p].w};
+      const uint32_t cuw[4] = {cu[p].x, cu[p].y, cu[p].z, cu[p].w};
+      f32x16_t dg = {}, du = {};
 #pragma unroll
-      for (int j = 0; j < kGemvMaxRows; j++) {
-        if (j < rows) {
-          const int t = tok[j];
-          const uint4* xp = reinterpret_cast<const uint4*>(xl + t * H + g * kGroup + h * 32);
-          float dg = 0.f, du = 0.f;
+      for (int c = 0; c < 4; c++) {
+        const f16x8_t a = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(xrow + g * kGroup + 8 * c));
+        uint4 q;
+        expand_codes_f16(cgw[c], m1024, m64, reinterpret_cast<uint32_t*>(&q));
+        dg = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, q), dg, 0, 0, 0);
+        expand_codes_f16(cuw[c], m1024, m64, reinterpret_cast<uint32_t*>(&q));
+        du = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, q), du, 0, 0, 0);
+      }
+      const float sg = 256.f * bf16_bits_to_f32(sbg[p] & 0xFFFFu), bg = 256.f * bf16_bits_to_f32(sbg[p] >> 16);
+      const float su = 256.f * bf16_bits_to_f32(sbu[p] & 0xFFFFu), bu = 256.f * bf16_bits_to_f32(sbu[p] >> 16);
+      const float cga = bg - 1024.f * sg, cgb = bg - 64.f * sg, cua = bu - 1024.f * su, cub = bu - 64.f * su;
+      const float4 xav = *reinterpret_cast<const float4*>(&xsa[g * kGemvMaxRows + 4 * h]);
+      const float4 xbv = *reinterpret_cast<const float4*>(&xsb[g * kGemvMaxRows + 4 * h]);
+      const float xa[4] = {xav.x, xav.y, xav.z, xav.w}, xb[4] = {xbv.x, xbv.y, xbv.z, xbv.w};
 #pragma unroll
-          for (int c = 0; c < 4; c++) {
-            const uint4 xv = xp[c];
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              dg = dot2_bf16(qg[4 * c + i], xw[i], dg);
-              du = dot2_bf16(qu[4 * c + i], xw[i], du);
-            }
-          }
-          const float xsv = h == 0 ? xs[t * G + g] : 0.f;
-          accg[j] = fmaf(sg, dg, fmaf(bpg, xsv, accg[j]));
-          accu[j] = fmaf(su, du, fmaf(bpu, xsv, accu[j]));
-        }
+      for (int i = 0; i < 4; i++) {
+        accg[i] = fmaf(sg, dg[i], fmaf(cga, xa[i], fmaf(cgb, xb[i], accg[i])));
+        accu[i] = fmaf(su, du[i], fmaf(cua, xa[i], fmaf(cub, xb[i], accu[i])));
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < kGemvMaxRows; j++) {
-    if (j < rows) {
-      accg[j] += __shfl_xor(accg[j], 32);
-      accu[j] += __shfl_xor(accu[j], 32);
-      if (h == 0) {
-        red[wave][j][0][col] = accg[j];
-        red[wave][j][1][col] = accu[j];
-      }
+  for (int i = 0; i < 4; i++) {
+    if (4 * h + i < rows) {
+      red[wave][4 * h + i][0][col] = accg[i];
+      red[wave][4 * h + i][1][col] = accu[i];
     }
   }
   __syncthreads();

@@ -23,11 +23,6 @@ namespace moe {
 
 constexpr int kMaxTileRows = 128;
 
-// bf16 bits -> fp16 bits of value / 256 (exact whenever the result is normal).
-__device__ __forceinline__ uint16_t f32_to_f16_scaled(uint16_t b) {
-  return __builtin_bit_cast(uint16_t, (_Float16)(bf16_bits_to_f32(b) * 0.00390625f));
-}
-
 // ---------------------------------------------------------------------------
 // Few tokens: all T x E logits in float64.  One single-wave workgroup per
 // expert (the router rows spread over every compute unit), lanes split h in
