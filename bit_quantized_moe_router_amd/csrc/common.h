@@ -121,7 +121,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u with the reciprocal instruction (about 1 ulp) in place of an
+// IEEE division; g -> -inf gives -0 (1 + e^-g = inf, rcp = 0), as the division does.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // Expert weight base pointer and widths.
 __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e) {
