@@ -51,15 +51,24 @@ def parse():
     return p.parse_args()
 
 
+def gemm_source_digest():
+    """First 16 hex digits of the SHA-256 of the grouped GEMM's sources (the
+    kernel file, then the header of shared device helpers)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "bit_quantized_moe_router_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def traffic_from_profile():
     """HBM bytes per gate/up GEMM launch from the committed counter summary, if
     it was taken on the current GEMM source (else None)."""
     import hashlib
     prof = os.path.join(ROOT, "profiles", "k_expert_gemm_traffic_prefill4096.md")
-    src = os.path.join(ROOT, "bit_quantized_moe_router_amd", "csrc", "gemm.hip")
     try:
         fields = dict(l.split(":", 1) for l in open(prof).read().splitlines() if l.count(":") == 1 and " " not in l.split(":")[0])
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        digest = gemm_source_digest()
         if fields.get("gemm_source_sha256_16", "").strip() != digest:
             return None
         return int(fields["gateup_traffic_bytes_per_launch"])
