@@ -191,14 +191,14 @@ __global__ __launch_bounds__(kFuThreads) void k_gemv_experts(LayerArgs L, ChunkA
     const uint32_t word = lane < nw ? s_bm[lane] : 0u;
     const int cnt = __popc(word);
     const int incl = wave_incl_scan(cnt);
-    const int nact = __shfl(incl, 63);
+    const int nact = lane_value(incl, 63);
     int e = -1;
     if (slot < nact) {
       const bool here = incl > slot && incl - cnt <= slot;
       const uint64_t hm = __ballot(here);
       const int wl = __ffsll((unsigned long long)hm) - 1;
-      const uint32_t wv = __shfl(word, wl);
-      int r = slot - (__shfl(incl, wl) - __shfl(cnt, wl));
+      const uint32_t wv = (uint32_t)lane_value((int)word, wl);
+      int r = slot - (lane_value(incl, wl) - lane_value(cnt, wl));
       uint32_t v = wv;
       for (; r > 0; r--) v &= v - 1;
       e = wl * 32 + (__ffs(v) - 1);

@@ -387,7 +387,7 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
   }
   __builtin_amdgcn_wave_barrier();
   const float myv = lane < k ? sel_v[lane] : 0.f;
-  const float vmax = __shfl(myv, 0);
+  const float vmax = lane_value(myv, 0);
   const float ex = lane < k ? __expf(myv - vmax) : 0.f;
   float sum = ex;
 #pragma unroll
@@ -497,7 +497,7 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     if (half) {
       const int la = ra > half ? ca : 0, lb = rb > half ? cb : 0;
       const int ia = wave_incl_scan(la), ib = wave_incl_scan(lb);
-      const int ta = __shfl(ia, 63);
+      const int ta = lane_value(ia, 63);
       const int ka = ra > half ? min(ca, max(max_long - (ia - la), 0)) : 0;
       const int kb = rb > half ? min(cb, max(max_long - (ta + ib - lb), 0)) : 0;
       if (ra > half) {
@@ -520,7 +520,7 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     }
     // First entry of each bin: 1 + the entries of all larger bins.
     const int ia = wave_incl_scan(fa), ib = wave_incl_scan(fb);
-    const int ta = __shfl(ia, 63), tb = __shfl(ib, 63);
+    const int ta = lane_value(ia, 63), tb = lane_value(ib, 63);
     if (ra >= 1) s_pbin[ra] = 1 + ia - fa;
     if (rb >= 1) s_pbin[rb] = 1 + ta + ib - fb;
     if (lane == 0 && sched) reinterpret_cast<int4*>(sched)[0] = make_int4(ta + tb, 0, 0, 0);

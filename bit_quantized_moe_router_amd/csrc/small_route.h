@@ -17,14 +17,25 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// Inclusive prefix sum over the wave's 64 lanes, in ALU cross-lane moves
+// (DPP) rather than LDS permutes: shifts by 1, 2, 4 and 8 within each row of
+// 16 lanes (lanes shifted in from outside the row read 0), then the total of
+// row 0 (lane 15) into row 1 and of row 2 into row 3, then the total of the
+// lower half (lane 31) into rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
   return v;
+}
+
+// Value of lane l (wave-uniform l) in every lane.
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
 // k-th largest of the 64 lanes' values m (k <= 64; -inf for lanes without
@@ -210,7 +221,7 @@ __device__ __forceinline__ void topk_small(const float* __restrict__ l, int E, i
   }
   __builtin_amdgcn_wave_barrier();
   const float myv = lane < k ? sel_v[lane] : 0.f;
-  const float vmax = __shfl(myv, 0);
+  const float vmax = lane_value(myv, 0);
   const float ex = lane < k ? __expf(myv - vmax) : 0.f;
   float sum = ex;
 #pragma unroll
@@ -259,7 +270,7 @@ __device__ __forceinline__ void meta_small(const int32_t* __restrict__ ids, int 
   for (int q = 0; q < 5; q++) {
     const int inc = wave_incl_scan(sum[q]);
     excl[q] = inc - sum[q];
-    total[q] = __shfl(inc, 63);
+    total[q] = lane_value(inc, 63);
   }
   const int routed_tiles = total[1], full_total = total[3];
   const int sfull = with_shared ? T / BM : 0;
