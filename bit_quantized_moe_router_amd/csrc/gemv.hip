@@ -294,11 +294,13 @@ __global__ __launch_bounds__(kFuThreads) void k_gemv_experts(LayerArgs L, ChunkA
       sb = (f16_bits_to_f32(v.y & 0xFFFFu) + f16_bits_to_f32(v.y >> 16)) +
            (f16_bits_to_f32(v.w & 0xFFFFu) + f16_bits_to_f32(v.w >> 16));
     }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      sa += __shfl_xor(sa, o);
-      sb += __shfl_xor(sb, o);
-    }
+    // 8-lane sums: pairs, quads, then the next quad into lanes 0-3 of the group (row_shl:4).
+    sa += dpp_f32<0xB1>(sa);
+    sb += dpp_f32<0xB1>(sb);
+    sa += dpp_f32<0x4E>(sa);
+    sb += dpp_f32<0x4E>(sb);
+    sa += dpp_f32<0x104>(sa);
+    sb += dpp_f32<0x104>(sb);
     if (ok && part8 == 0) {
       xsa[g * kGemvMaxRows + j] = sa;
       xsb[g * kGemvMaxRows + j] = sb;
@@ -376,8 +378,10 @@ __global__ __launch_bounds__(kFuThreads) void k_gemv_experts(LayerArgs L, ChunkA
     }
     const uint16_t hb = f32_to_bf16_rne(silu_mul(gs, us));
     float hs = ok ? bf16_bits_to_f32(hb) : 0.f;
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) hs += __shfl_xor(hs, off);
+    // 32-lane sum (two rows of lanes): row sums, then lanes 0 and 32 add rows 1 and 3.
+    hs = row_sum16(hs);
+    const float r1 = lane_value(hs, 16), r3 = lane_value(hs, 48);
+    hs += lane < 32 ? r1 : r3;
     if (ok) {
       reinterpret_cast<uint16_t*>(s_h[j])[n] = hb;
       if (n == 0) s_hs[j] = hs;

@@ -186,9 +186,7 @@ __global__ __launch_bounds__(256) void k_screen(const uint16_t* __restrict__ x, 
     const double sv[4] = {ss0, ss1, ss2, ss3};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      double v = sv[i];
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+      const double v = row_sum16(sv[i]);  // the 16 threads of a weight row are one row of lanes
       const int ee = e0 + wr0 + 16 * i;
       if (wp == 0 && ee < E) wsq[gs * E + ee] = v;
     }
@@ -282,12 +280,9 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
       *reinterpret_cast<uint4*>(x16 + (int64_t)t * H + h) = make_uint4(c[0], c[1], c[2], c[3]);
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    xx += __shfl_xor(xx, off);
-    amax = fmaxf(amax, __shfl_xor(amax, off));
-    w2max = fmax(w2max, __shfl_xor(w2max, off));
-  }
+  xx = wave_sum_f64(xx);
+  amax = wave_max_f32(amax);
+  w2max = wave_max_f64(w2max);
   if (lane == 0) {
     red[3 * wave + 0] = xx;
     red[3 * wave + 1] = (double)amax;
@@ -349,8 +344,12 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
       acc = fma((double)bf16_bits_to_f32(xq.y & 0xFFFFu), (double)w4.z, acc);
       acc = fma((double)bf16_bits_to_f32(xq.y >> 16), (double)w4.w, acc);
     }
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) acc += __shfl_xor(acc, off);
+    // Half-wave sum: the two rows of lanes of this half, (row sum) + (row sum).
+    // Rows belong to one half whole, so the other half may be inactive here.
+    acc = row_sum16(acc);
+    const double r0 = lane_value_f64(acc, 0), r1 = lane_value_f64(acc, 16);
+    const double r2 = lane_value_f64(acc, 32), r3 = lane_value_f64(acc, 48);
+    acc = lane < 32 ? r0 + r1 : r2 + r3;
     float lg = (float)acc;
     if (bias) lg = lg + bias[e];
     if (l32 == 0) cand_v[c] = lg;
@@ -389,9 +388,7 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
   const float myv = lane < k ? sel_v[lane] : 0.f;
   const float vmax = lane_value(myv, 0);
   const float ex = lane < k ? __expf(myv - vmax) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  const float sum = wave_sum_f32(ex);  // the sum topk_small takes, so both give the same weights
   if (lane < k) tw[(int64_t)t * k + lane] = ex / sum;
 }
 
@@ -510,9 +507,7 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
         fb = kb;
         if (cb > kb) atomicAdd(&s_extra[rb - half], cb - kb);
       }
-      int cut = (ra > half ? ca - ka : 0) + (rb > half ? cb - kb : 0);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) cut += __shfl_xor(cut, off);
+      const int cut = wave_sum_i32((ra > half ? ca - ka : 0) + (rb > half ? cb - kb : 0));
       if (lane == 0) atomicAdd(&s_extra[half], cut);
       __builtin_amdgcn_wave_barrier();
       fa += ra >= 1 && ra <= half ? s_extra[ra] : 0;

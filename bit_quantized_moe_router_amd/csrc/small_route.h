@@ -11,10 +11,56 @@ constexpr int kMaxEPerLane = 8;  // E <= 512
 constexpr int kSmallT = 8;
 constexpr int kMaxE = 512;
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+// ---- cross-lane sums by DPP (ALU moves within rows of 16 lanes) and
+// v_readlane (across rows), instead of LDS permutes.  Fixed order: the same
+// inputs give the same bits. ----
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int v) { return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false); }
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_i32<kCtrl>(__builtin_bit_cast(int, v)));
+}
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)dpp_i32<kCtrl>((int)(uint32_t)u), hi = (uint32_t)dpp_i32<kCtrl>((int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double lane_value_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over each row of 16 lanes, in every lane of the row: pairs (lane xor
+// 1), quads (xor 2), then the row rotated by 4 and by 8.
+template <class V>
+__device__ __forceinline__ V row_sum16(V v) {
+  if constexpr (sizeof(V) == 8) {
+    v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f64<0x124>(v);  // row_ror:4
+    v += dpp_f64<0x128>(v);  // row_ror:8
+  } else if constexpr (__is_same(V, float)) {
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x124>(v);
+    v += dpp_f32<0x128>(v);
+  } else {
+    v += dpp_i32<0xB1>(v);
+    v += dpp_i32<0x4E>(v);
+    v += dpp_i32<0x124>(v);
+    v += dpp_i32<0x128>(v);
+  }
   return v;
+}
+
+// Sum over the wave's 64 lanes: the row sums of lanes 0, 16, 32 and 48 added
+// as (r0 + r1) + (r2 + r3); every lane gets that value.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = row_sum16(v);
+  return (lane_value_f64(v, 0) + lane_value_f64(v, 16)) + (lane_value_f64(v, 32) + lane_value_f64(v, 48));
 }
 
 // Inclusive prefix sum over the wave's 64 lanes, in ALU cross-lane moves
@@ -36,6 +82,31 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 __device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ float lane_value(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = row_sum16(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v = row_sum16(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// Maximum over the wave's 64 lanes (exact whatever the order).
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x124>(v));
+  v = fmaxf(v, dpp_f32<0x128>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = fmax(v, dpp_f64<0xB1>(v));
+  v = fmax(v, dpp_f64<0x4E>(v));
+  v = fmax(v, dpp_f64<0x124>(v));
+  v = fmax(v, dpp_f64<0x128>(v));
+  return fmax(fmax(lane_value_f64(v, 0), lane_value_f64(v, 16)), fmax(lane_value_f64(v, 32), lane_value_f64(v, 48)));
 }
 
 // k-th largest of the 64 lanes' values m (k <= 64; -inf for lanes without
@@ -223,9 +294,7 @@ __device__ __forceinline__ void topk_small(const float* __restrict__ l, int E, i
   const float myv = lane < k ? sel_v[lane] : 0.f;
   const float vmax = lane_value(myv, 0);
   const float ex = lane < k ? __expf(myv - vmax) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  const float sum = wave_sum_f32(ex);
   if (lane < k) tw[(int64_t)t * k + lane] = ex / sum;
 }
 
