@@ -49,7 +49,7 @@ __device__ __forceinline__ void expand_codes_f16(uint32_t d, uint32_t m1024, uin
   out[2] = and_or(d8, 0x000F000Fu, m1024);
   out[3] = and_or(d8, 0x00F000F0u, m64);
 }
-constexpr int kGuPref = 4;     // groups per wave whose gate/up loads are issued together
+constexpr int kGuPref = 2;     // groups per wave whose gate/up loads are issued together
 constexpr int kMaxGroups = 128;              // H / 64 for H <= 8192
 constexpr int kMaxAssign = kGemvMaxRows * 16; // T * k on the GEMV path
 constexpr int kGuSmemMax = 64 * 1024 + kGemvMaxRows * (2 * 512 + 16) * 4;  // x rows + top-k lists
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kFuThreads) void k_gemv_reduce(LayerArgs L, ChunkAr
   }
 }
 
-__global__ __launch_bounds__(kFuThreads) void k_gemv_experts(LayerArgs L, ChunkArgs C, const float* logits,
+__global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_gemv_experts(LayerArgs L, ChunkArgs C, const float* logits,
                                                             float* __restrict__ part, int nbs) {
   const int slot = (int)blockIdx.x / nbs, nb = (int)blockIdx.x - slot * nbs;
   const int T = C.T, H = L.H, G = H / kGroup, E = L.E, k = L.k, N = T * k;
