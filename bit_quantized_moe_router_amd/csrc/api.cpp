@@ -33,7 +33,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 }
 
 constexpr int kDefaultTileRows = 128;
-constexpr int kDefaultGemvMaxRows = 6;  // measured crossover: GEMV faster for T <= 6, grouped GEMM from T = 7
+constexpr int kDefaultGemvMaxRows = 8;  // measured: the GEMV path is faster at every T <= 8 (the decode maximum)
 constexpr int kMaxRowsDecode = 8;
 
 moe_status validate_desc(const moe_layer_desc* d) {
