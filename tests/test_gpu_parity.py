@@ -202,6 +202,8 @@ EDGE_DECODE = [  # T, H, E, k, I, Is, seed, zipf
     (8, 192, 1, 1, 128, 0, 31, None),     # one expert, no shared expert
     (7, 128, 8, 3, 64, 128, 21, 22),      # Is != I, zipf bias
     (8, 320, 16, 8, 192, 64, 71, None),   # k == 8 of 16, odd group counts
+    (8, 4096, 64, 8, 256, 256, 91, None), # T * H at the GEMV's LDS limit, 64 groups per row
+    (4, 8192, 32, 4, 128, 64, 93, None),  # widest hidden the GEMV takes, 128 groups per row
 ]
 
 
@@ -223,6 +225,26 @@ def test_decode_gemv_edge_shapes(M, T, H, E, k, I, Is, seed, zipf):
         moe_profile_reset()
     assert ran == (1, 0), ran
     check_close(y.cpu().numpy(), oracle_rows(case), f"edge {case['name']} GEMV decode")
+
+
+@pytest.mark.parametrize("gemv,scale", [(8, 1.0 / 32), (8, 256.0), (0, 1.0 / 32), (0, 16.0)])
+def test_decode_activation_scale(M, gemv, scale):
+    """Both decode paths keep activations as fp16(x / 256) for their MFMAs:
+    small activations (many of them fp16 subnormals after the scaling) and
+    large ones stay within tolerance of the oracle.  The grouped-GEMM path
+    also keeps h as fp16(h / 256), so |h| must stay below about 1.7e7; h
+    grows with the square of the activations' scale, and x * 16 (|x| up to
+    about 70) is well inside it.  The GEMV path keeps h in bf16 and takes
+    x * 256 (|x| up to about 1000)."""
+    case = mi.small_layer(3, 1024, 32, 4, 256, 128, 97, None)
+    x = mi.bf16_bits_to_f32(case["x"]) * np.float32(scale)
+    case["x"] = mi.f32_to_bf16_bits(x)
+    lay = M.MoELayer(case["w"], case["k"], max_tokens=8, gemv_max_rows=gemv)
+    y = lay.forward_decode(dev(M, case["x"]), None)
+    torch.cuda.synchronize()
+    yn = y.cpu().numpy()
+    assert np.all(np.isfinite(yn))
+    check_close(yn, oracle_rows(case), f"decode x*{scale} gemv_max_rows={gemv}")
 
 
 def _sample_tokens(case, n, seed):
