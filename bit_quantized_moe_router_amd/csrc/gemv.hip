@@ -67,8 +67,10 @@ constexpr int kGuSmemMax = 64 * 1024 + kGemvMaxRows * (2 * 512 + 16) * 4;  // x 
 // ---------------------------------------------------------------------------
 constexpr int kFuWaves = 8;
 constexpr int kFuThreads = kFuWaves * 64;
-constexpr int kRedCols = 64;                 // output columns per reduce workgroup
-constexpr int kRedGroups = kFuThreads / 16;  // term groups of a reduce workgroup (16 float4 columns each)
+constexpr int kRedThreads = 512;                 // threads of a reduce workgroup
+constexpr int kRedCols = 64;                     // output columns per reduce workgroup
+constexpr int kRedC4 = kRedCols / 4;             // float4 columns of a reduce workgroup
+constexpr int kRedGroups = kRedThreads / kRedC4; // term groups of a reduce workgroup
 constexpr int kFuDn = 4;                     // down outputs per thread per load round
 constexpr int kFuBatch = 8;                  // partials a reduce thread loads together
 
@@ -76,14 +78,14 @@ constexpr int kFuBatch = 8;                  // partials a reduce thread loads t
 // assignments j = 0..k-1 with blocks nb ascending, then the shared expert's
 // blocks), so y does not depend on the order in which workgroups ran.
 // grid = T x H/64.
-__global__ __launch_bounds__(kFuThreads) void k_gemv_reduce(LayerArgs L, ChunkArgs C, const float* __restrict__ part,
+__global__ __launch_bounds__(kRedThreads) void k_gemv_reduce(LayerArgs L, ChunkArgs C, const float* __restrict__ part,
                                                            int nbs) {
-  __shared__ float4 red4[kRedGroups][16];
+  __shared__ float4 red4[kRedGroups][kRedC4];
   const int tid = threadIdx.x;
   const int H = L.H, k = L.k, Tk = C.Tk;
   const int nslice = H / kRedCols;
   const int t = (int)blockIdx.x / nslice, sl = (int)blockIdx.x - t * nslice;
-  const int c4 = tid & 15, tg = tid >> 4;
+  const int c4 = tid % kRedC4, tg = tid / kRedC4;
   const int col = sl * kRedCols + c4 * 4;
   const int nI = L.I / 32, nS = L.Is / 32;
   const int nrt = k * nI, nterm = nrt + nS;
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kFuThreads) void k_gemv_reduce(LayerArgs L, ChunkAr
   }
   red4[tg][c4] = acc;
   __syncthreads();
-  if (tid < 16) {
+  if (tid < kRedC4) {
     float4 sm = red4[0][tid];
     for (int g = 1; g < kRedGroups; g++) {
       const float4 v = red4[g][tid];
@@ -433,7 +435,7 @@ hipError_t launch_gemv_reduce(const LayerArgs& L, const ChunkArgs& C, const floa
                               const KTime& kt) {
   const int Imax = L.I > L.Is ? L.I : L.Is;
   if (L.H % kRedCols != 0) return hipErrorInvalidValue;
-  MOE_LAUNCH(k_gemv_reduce, dim3((unsigned)(C.T * (L.H / kRedCols))), dim3(kFuThreads), 0, s, kt.start, kt.stop, L,
+  MOE_LAUNCH(k_gemv_reduce, dim3((unsigned)(C.T * (L.H / kRedCols))), dim3(kRedThreads), 0, s, kt.start, kt.stop, L,
              C, part, Imax / 32);
   return hipGetLastError();
 }
