@@ -153,7 +153,8 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
   if (tid < nx) xr0 = reinterpret_cast<const uint4*>(C.x)[tid];
   if (tid + kFuThreads < nx) xr1 = reinterpret_cast<const uint4*>(C.x)[tid + kFuThreads];
   // ---- top-k of each row ----
-  if (wave < T) topk_small(logits + (int64_t)wave * E, E, k, wave, s_ids, s_tw, lists + wave * (2 * E + 16));
+  // The GEMV needs each row's selected experts and weights, not their order.
+  if (wave < T) topk_small(logits + (int64_t)wave * E, E, k, wave, s_ids, s_tw, lists + wave * (2 * E + 16), false);
   if (tid < nx) reinterpret_cast<uint4*>(xl)[tid] = to_f16x8_scaled(xr0);
   if (tid + kFuThreads < nx) reinterpret_cast<uint4*>(xl)[tid + kFuThreads] = to_f16x8_scaled(xr1);
   for (int i = tid + 2 * kFuThreads; i < nx; i += kFuThreads)

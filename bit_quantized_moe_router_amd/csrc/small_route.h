@@ -232,8 +232,14 @@ __device__ __forceinline__ void group_sums(const uint16_t* __restrict__ x, int T
 // comparison, a superset of the key comparison) are listed and ranked exactly
 // (larger first, equal logits towards the lower expert), then the softmax
 // over the k selected.  lds: 2 E + 16 ints.
+//
+// ordered = false (a caller that needs the selected set and its weights, not
+// their order): when exactly k logits pass the threshold they are all
+// selected, and they are written in increasing expert order without the
+// ranking (the softmax then sums in that order).
 __device__ __forceinline__ void topk_small(const float* __restrict__ l, int E, int k, int t,
-                                           int32_t* __restrict__ ids, float* __restrict__ tw, int* lds) {
+                                           int32_t* __restrict__ ids, float* __restrict__ tw, int* lds,
+                                           bool ordered = true) {
   const int lane = threadIdx.x & 63;
   int* cand_e = lds;
   float* cand_v = reinterpret_cast<float*>(cand_e + E);
@@ -261,6 +267,17 @@ __device__ __forceinline__ void topk_small(const float* __restrict__ l, int E, i
     C += __popcll(mk);
   }
   __builtin_amdgcn_wave_barrier();
+  if (!ordered && C == k) {  // wave-uniform
+    const float vc = lane < k ? cand_v[lane] : -INFINITY;
+    const float vmax = wave_max_f32(vc);
+    const float ex = lane < k ? __expf(vc - vmax) : 0.f;
+    const float sum = wave_sum_f32(ex);
+    if (lane < k) {
+      ids[(int64_t)t * k + lane] = cand_e[lane];
+      tw[(int64_t)t * k + lane] = ex / sum;
+    }
+    return;
+  }
   if (C <= 64) {
     // Candidates in lanes; the others are broadcast with v_readlane.
     const float vc = lane < C ? cand_v[lane] : 0.f;
