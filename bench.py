@@ -102,7 +102,7 @@ def cpu_baseline(case, budget_s):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+        print(f"bench.py runs on one GPU only: the layer has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     import torch
