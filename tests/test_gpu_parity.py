@@ -407,6 +407,25 @@ def test_batch_invariant_gemm_path(M):
             assert torch.equal(y[i], y_big[pos[i]]), (T, i)
 
 
+def test_batch_invariant_gemm_path_large_tiles(M):
+    """The same invariance across tile sizes for routed experts: in one
+    skewed 2048-token chunk (Zipf logit bias) the popular experts fill
+    128-row tiles, long ones cut into pieces, while the same rows decoded a
+    few at a time sit in one-fragment tiles; the bits must agree."""
+    case = mi.make_case("prefill4096")
+    lay = get_layer(M, case, gemv_max_rows=0, max_tokens=2048)
+    x = case["x"][:2048]
+    bias = dev(M, case["bias"])
+    y_big = lay.forward_prefill(dev(M, x), bias)
+    torch.cuda.synchronize()
+    pos = [0, 1, 511, 1024, 1500, 2047]
+    for T in (1, 3, 6):
+        y = lay.forward_decode(dev(M, x[pos[:T]]), bias)
+        torch.cuda.synchronize()
+        for i in range(T):
+            assert torch.equal(y[i], y_big[pos[i]]), (T, i)
+
+
 def test_batch_invariant_gemv_path(M):
     """Within the GEMV path a row's output does not depend on the other rows
     either (per-row dot products, fixed-order partial sums)."""
