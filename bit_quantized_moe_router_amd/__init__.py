@@ -17,11 +17,12 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED_SH
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP", 5: "MOE_ERR_DEVICE_UNSUPPORTED"}
 
 # Kernel ids of moe_profile_read.
-K_LOGITS, K_TOPK, K_META, K_GATEUP_GEMM, K_DOWN_GEMM, K_GATEUP_GEMV, K_DOWN_GEMV, K_COMBINE, K_DEQUANT = range(9)
+(K_LOGITS, K_TOPK, K_META, K_GATEUP_GEMM, K_DOWN_GEMM, K_GATEUP_GEMV, K_DOWN_GEMV, K_COMBINE, K_DEQUANT,
+ K_PROBE_READ, K_PROBE_MFMA) = range(11)
 KERNEL_NAMES = {K_LOGITS: "k_screen|k_logits_small", K_TOPK: "k_route_exact", K_META: "k_meta|k_topk_meta",
                 K_GATEUP_GEMM: "k_gateup_gemm", K_DOWN_GEMM: "k_down_gemm",
                 K_GATEUP_GEMV: "k_gemv_experts", K_DOWN_GEMV: "k_gemv_reduce", K_COMBINE: "k_combine",
-                K_DEQUANT: "k_dequant_active"}
+                K_DEQUANT: "k_dequant_active", K_PROBE_READ: "k_stream_read", K_PROBE_MFMA: "k_mfma_rate"}
 
 
 class MoEError(RuntimeError):
@@ -55,6 +56,11 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python bit_quantized_moe_router_amd/build.py`")
+        # torch carries its own HIP runtime (same soname as ROCm's).  Loading it
+        # first makes libmoe.so bind to that one; loaded the other way round the
+        # process would hold two HIP runtimes, and the second to open the GPU
+        # finds no device.
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         P, vp, i32, sz = C.POINTER, C.c_void_p, C.c_int32, C.c_size_t
         D = P(LayerDesc)
@@ -71,11 +77,14 @@ def lib():
         L.moe_status_str.restype = C.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = C.c_char_p
+        L.moe_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
+        L.moe_probe_mfma_rate.argtypes = [i32, i32, vp, vp, vp]
         L.moe_profile_enable.argtypes = [i32]
         L.moe_profile_reset.argtypes = []
         L.moe_profile_read.argtypes = [i32, P(C.c_double), P(i32)]
         for name in ("moe_packed_bytes", "moe_workspace_bytes", "moe_max_tiles", "moe_pack_weights",
-                     "moe_route", "moe_forward_prefill", "moe_forward_decode", "moe_profile_enable",
+                     "moe_route", "moe_forward_prefill", "moe_forward_decode",
+                     "moe_probe_stream_read", "moe_probe_mfma_rate", "moe_profile_enable",
                      "moe_profile_reset", "moe_profile_read"):
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -157,6 +166,16 @@ def moe_forward_decode(desc, packed, router_w, logit_bias, x, T, y, ws, stream=N
     _check(lib().moe_forward_decode(C.byref(desc), _ptr(packed), _ptr(router_w), _ptr(logit_bias),
                                     _ptr(x), T, _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)))
+
+
+def moe_probe_stream_read(src, nbytes, sink, max_workgroups, stream=None):
+    """Streaming read of nbytes of src (16-byte pieces per lane); sink holds max_workgroups words."""
+    _check(lib().moe_probe_stream_read(_ptr(src), nbytes, _ptr(sink), max_workgroups, _stream(stream)))
+
+
+def moe_probe_mfma_rate(iters, workgroups, clocks, sink, stream=None):
+    """MFMA-only kernel: workgroups x 4 waves x iters x 8 MFMAs of 32x32x16 (32768 flop each)."""
+    _check(lib().moe_probe_mfma_rate(iters, workgroups, _ptr(clocks), _ptr(sink), _stream(stream)))
 
 
 def moe_profile_enable(mask: int):

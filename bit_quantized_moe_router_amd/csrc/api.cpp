@@ -178,7 +178,7 @@ int max_long_tiles(const moe_layer_desc* d) {
 }
 
 // ---- kernel timing (measurement mode) ----------------------------------------
-constexpr int kNumKernels = 9;
+constexpr int kNumKernels = 11;
 struct Pending {
   int kid;
   hipEvent_t a, b;
@@ -501,8 +501,8 @@ moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, co
                               size_t ws_bytes, void* stream) {
   TRY(forward_checks(desc, packed, router_w, x, T, y, ws, ws_bytes));
   if (T == 0) return MOE_OK;
-  if (T > kMaxRowsDecode) return fail(MOE_ERR_INVALID_ARGUMENT, "decode takes 1..8 rows (got %d)", T);
   TRY(check_device());
+  // T > R* (and always T > 8, the GEMV's largest row count) takes the grouped-GEMM path.
   const int R = desc->gemv_max_rows < 0 ? kDefaultGemvMaxRows : desc->gemv_max_rows;
   const bool gemv = T <= R && T <= desc->max_chunk && (int64_t)T * desc->hidden <= 32768;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -539,6 +539,24 @@ const char* moe_status_str(moe_status s) {
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t max_workgroups,
+                                 void* stream) {
+  if (!src || !sink || max_workgroups < 1 || (reinterpret_cast<uintptr_t>(src) & 15) || (bytes & 15))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "probe: null pointer, max_workgroups < 1, or src/bytes not 16-byte aligned");
+  TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(9, s, "stream-read probe",
+               [&](const KTime& kt) { return launch_stream_read(src, bytes, sink, max_workgroups, s, kt); });
+}
+
+moe_status moe_probe_mfma_rate(int32_t iters, int32_t workgroups, uint64_t* clocks, uint32_t* sink, void* stream) {
+  if (iters < 1 || workgroups < 1 || !sink) return fail(MOE_ERR_INVALID_ARGUMENT, "probe: iters, workgroups or sink");
+  TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(10, s, "MFMA-rate probe",
+               [&](const KTime& kt) { return launch_mfma_rate(iters, workgroups, clocks, sink, s, kt); });
+}
 
 moe_status moe_profile_enable(int32_t mask) {
   g_prof_mask = (uint32_t)mask;

@@ -12,8 +12,10 @@
 // as the A operand: the expansion of the codes to fp16 is the only per-code
 // vector work, and the per-group scale and bias are applied to the group's
 // dot products (affine fold) instead of to every weight.  The down projection
-// expands codes to bf16 pairs (128 + q) for v_dot2_f32_bf16 with h, folded as
-//   acc += s * dot + (b - 128 s) * sum(h over the group).
+// expands codes to bf16 pairs (128 + q) for v_dot2_f32_bf16 with h, carried as
+// two bf16 parts hi = bf16(h) and lo = bf16(h - hi) (about 16 significant
+// bits), folded as
+//   acc += s * (dot(hi) + dot(lo)) + (b - 128 s) * sum(hi + lo over the group).
 // The down projection is split along the intermediate: the workgroup that
 // produced 32 columns of h applies the matching 32 columns of the down matrix
 // (half of each down block, loaded in the same round as gate/up) and writes a
@@ -144,7 +146,9 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
   __shared__ uint32_t s_bm[kMaxE / 32];
   __shared__ int tok[kGemvMaxRows], arow[kGemvMaxRows], s_info[2];
   __shared__ float wgt[kGemvMaxRows], s_hs[kGemvMaxRows];
-  __shared__ __attribute__((aligned(16))) uint32_t s_h[kGemvMaxRows][16];  // bf16 h of the 32 columns, as pairs
+  // h of the 32 columns as two bf16 parts (hi = bf16(h), lo = bf16(h - hi)), as pairs
+  __shared__ __attribute__((aligned(16))) uint32_t s_h[kGemvMaxRows][16];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hl[kGemvMaxRows][16];
   __shared__ float red[kFuWaves][kGemvMaxRows][2][32];
 
   // ---- activation rows into registers (their latency overlaps the top-k) ----
@@ -366,8 +370,8 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
     }
   }
   __syncthreads();
-  // ---- SwiGLU: thread 32*j + n finishes row j, column n; h is rounded to
-  // bf16 and its 32-column sum taken for the down fold ----
+  // ---- SwiGLU: thread 32*j + n finishes row j, column n; h is split into
+  // bf16 hi and lo parts and their 32-column sum taken for the down fold ----
   if (tid < kGemvMaxRows * 32) {
     const int j = tid >> 5, n = tid & 31;
     const bool ok = j < rows;
@@ -379,14 +383,17 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
         us += red[w][j][1][n];
       }
     }
-    const uint16_t hb = f32_to_bf16_rne(silu_mul(gs, us));
-    float hs = ok ? bf16_bits_to_f32(hb) : 0.f;
+    const float hv = silu_mul(gs, us);
+    const uint16_t hb = f32_to_bf16_rne(hv);
+    const uint16_t hl = f32_to_bf16_rne(hv - bf16_bits_to_f32(hb));  // hv - hi is exact in fp32
+    float hs = ok ? bf16_bits_to_f32(hb) + bf16_bits_to_f32(hl) : 0.f;
     // 32-lane sum (two rows of lanes): row sums, then lanes 0 and 32 add rows 1 and 3.
     hs = row_sum16(hs);
     const float r1 = lane_value(hs, 16), r3 = lane_value(hs, 48);
     hs += lane < 32 ? r1 : r3;
     if (ok) {
       reinterpret_cast<uint16_t*>(s_h[j])[n] = hb;
+      reinterpret_cast<uint16_t*>(s_hl[j])[n] = hl;
       if (n == 0) s_hs[j] = hs;
     }
   }
@@ -410,6 +417,8 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
         float d = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; i++) d = dot2_bf16(q[i], s_h[j][i], d);
+#pragma unroll
+        for (int i = 0; i < 16; i++) d = dot2_bf16(q[i], s_hl[j][i], d);
         part[((int64_t)arow[j] * nbs + nb) * H + n] = wgt[j] * fmaf(s, d, bp * s_hs[j]);
       }
     }

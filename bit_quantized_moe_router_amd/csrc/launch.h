@@ -101,4 +101,13 @@ hipError_t launch_gemv_experts(const LayerArgs& L, const ChunkArgs& C, const flo
 hipError_t launch_gemv_reduce(const LayerArgs& L, const ChunkArgs& C, const float* part, hipStream_t s,
                               const KTime& kt = KTime{});
 
+// Measurement probes (csrc/probe.hip): a 16-byte-per-lane streaming read of
+// `bytes` with at most max_wgs workgroups (sink: max_wgs words), and the
+// MFMA-only rate kernel over `wgs` workgroups (clocks: 2 * wgs words or null;
+// sink: wgs words).
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int max_wgs, hipStream_t s,
+                              const KTime& kt = KTime{});
+hipError_t launch_mfma_rate(int iters, int wgs, uint64_t* clocks, uint32_t* sink, hipStream_t s,
+                            const KTime& kt = KTime{});
+
 }  // namespace moe

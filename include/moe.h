@@ -55,6 +55,17 @@ typedef enum {
 } moe_status;
 
 /*
+ * Supported activation range.  The grouped-GEMM path feeds its MFMAs fp16(x /
+ * 256) and fp16(h / 256) (h = silu(gate) * up) and stores each routed expert
+ * output as fp16(o / 256): exact scalings, in range while |x|, |h| and |o|
+ * stay below 65504 * 256 (about 1.7e7).  h grows with the square of the
+ * activations' scale; for this layer's weights that is activations up to a
+ * few hundred times N(0, 1).  Beyond that the path gives inf or NaN in y
+ * (with MOE_OK); the decode GEMV path keeps h in bf16 hi/lo parts and reaches
+ * further.  Inputs must be finite.
+ */
+
+/*
  * Layer description.  Limits: hidden and inter multiples of 64 (the group
  * size; the pages' format cannot quantise a width that is not a multiple of
  * the group, cf. the Laya page's quantisation section), hidden <= 8192,
@@ -126,18 +137,37 @@ typedef struct {
     int32_t *n_tiles;
 } moe_routing;
 
-/* Size in bytes of the packed weight blob for `desc` (host output). */
+/*
+ * Size in bytes of the packed weight blob for `desc` (host output): the
+ * canonical 4-bit codes plus one bf16 scale and one bf16 bias per 64 weights,
+ * 0.5625 bytes per parameter (the Laya page's quantisation section gives this
+ * storage cost of the group-64 4-bit format).  Host-only; no device access.
+ */
 moe_status moe_packed_bytes(const moe_layer_desc *desc, size_t *bytes);
 
-/* Workspace bytes needed by moe_route / moe_forward_* for up to max_tokens per call (host output). */
+/*
+ * Workspace bytes needed by moe_route / moe_forward_* for up to max_tokens per
+ * call (host output).  The workspace holds one chunk's routing metadata and
+ * intermediates; prefill reuses it chunk after chunk, so its size is bounded
+ * by max_chunk whatever T is ("Optimizing on-device inference for Apple
+ * Silicon", section "Bound temporary memory with prompt chunking").
+ * Host-only; no device access.
+ */
 moe_status moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens, size_t *bytes);
 
-/* Number of tile_map entries moe_route may write for a chunk of T tokens (host output). */
+/*
+ * Upper bound of the tile_map entries moe_route writes for a chunk of T tokens
+ * (host output): the block map of fixed-size tiles per expert (section "Keep
+ * expert routing on the GPU" of the same page).  Host-only.
+ */
 moe_status moe_max_tiles(const moe_layer_desc *desc, int32_t T, int32_t *n);
 
 /*
  * Repack canonical quantised weights into the library's blob (device, size
- * moe_packed_bytes).  The blob is opaque and valid only for the desc that
+ * moe_packed_bytes).  The format is the page's: 4-bit codes, every 64 weights
+ * along the input dimension sharing one bf16 scale and one bf16 bias, w = s*q
+ * + b ("Optimizing on-device inference for Apple Silicon", section
+ * "Dequantise weights during matrix multiplication").  The blob is opaque and valid only for the desc that
  * made it.  It stores exactly the canonical codes, scales and biases (0.5625
  * bytes per parameter), rearranged so that one 64-lane wave reads a 32-row x
  * 64-column group with one 16-byte load per lane.  sh_* are ignored when
@@ -148,7 +178,11 @@ moe_status moe_pack_weights(const moe_layer_desc *desc, moe_qmatrix gate, moe_qm
                             moe_qmatrix sh_down, void *packed, size_t packed_bytes, void *stream);
 
 /*
- * Route one chunk of T <= max_chunk tokens: router logits
+ * Route one chunk of T <= max_chunk tokens on the GPU, with no return to the
+ * host ("Optimizing on-device inference for Apple Silicon", section "Keep
+ * expert routing on the GPU": top-k, histogram, prefix scan, scatter, block
+ * map; section "Qwen creates three different workload shapes": top-8 of 256
+ * routed experts plus one shared expert): router logits
  * fp32(sum_h x[t,h]*Wr[e,h] accumulated in float64) + logit_bias[e], top-k,
  * softmax weights, then histogram, prefix scan, stable scatter and block map,
  * all on the GPU.
@@ -163,7 +197,10 @@ moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
 
 /*
  * Full layer over T tokens with the grouped dequantising GEMM path, chunk by
- * chunk (max_chunk tokens each):
+ * chunk (max_chunk tokens each; "Optimizing on-device inference for Apple
+ * Silicon", sections "Dequantise weights during matrix multiplication", "Match
+ * tile size to expert load", "Reduce intermediate and state traffic" and
+ * "Bound temporary memory with prompt chunking"):
  *   y[t] = sum_j topk_weights[t,j] * FFN_{topk_ids[t,j]}(x[t]) + FFN_shared(x[t])
  * with FFN(x) = Wd (silu(Wg x) * (Wu x)).
  *   packed  blob from moe_pack_weights
@@ -176,8 +213,13 @@ moe_status moe_forward_prefill(const moe_layer_desc *desc, const void *packed,
                                void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Same layer for a few rows (1 <= T <= 8): the row-parallel GEMV path when
- * T <= gemv_max_rows, otherwise the grouped GEMM path of moe_forward_prefill.
+ * Same layer for a few rows: the row-parallel GEMV path when T <=
+ * gemv_max_rows (at most 8), otherwise the grouped GEMM path of
+ * moe_forward_prefill (any T, chunked the same way).  The pages' one-row
+ * weight path ("Optimizing on-device inference for Apple Silicon", section
+ * "Optimise the one-row weight path") and the choice of kernel by row count
+ * (the dothoosh page on Candle's Metal kernels, its kernel-selection and
+ * crossover sections).
  * The GEMV path is three launches: exact router logits; top-k, gate/up +
  * SwiGLU and the down projection of each workgroup's 32 intermediate columns
  * (partial output rows in the workspace); the sum of each token's partials in

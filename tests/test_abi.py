@@ -93,9 +93,9 @@ def test_errors_before_any_device_work():
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_forward_prefill(d, None, t, None, t, 16, t, _FakeTensor(1 << 30), stream=0)
     assert ei.value.status == 1
-    # Decode takes at most 8 rows.
+    # The GEMV path takes at most 8 rows: a row threshold above 8 is refused.
     with pytest.raises(moe.MoEError) as ei:
-        moe.moe_forward_decode(d, t, t, None, t, 9, t, _FakeTensor(1 << 30), stream=0)
+        moe.moe_forward_decode(_desc(gemv_max_rows=9), t, t, None, t, 9, t, _FakeTensor(1 << 30), stream=0)
     assert ei.value.status == 1
     # Route: T above max_chunk.
     with pytest.raises(moe.MoEError) as ei:

@@ -8,6 +8,7 @@ max-abs <= 2e-2 * RMS(reference) of the float64 oracle.
 import numpy as np
 import pytest
 
+import conftest
 import moe_inputs as mi
 from oracle import oracle as orc
 
@@ -53,6 +54,7 @@ def check_close(y, ref, label):
     rms = np.sqrt(np.mean(ref ** 2))
     maxabs = np.abs(err).max()
     print(f"[parity] {label}: rel_l2={rel:.3e} max_abs/rms={maxabs / rms:.3e}", flush=True)
+    conftest.PARITY_LOG.append((label, float(rel), float(maxabs / rms)))
     assert np.all(np.isfinite(y)), label
     assert rel <= REL_L2, (label, rel)
     assert maxabs <= MAXABS_RMS * rms, (label, maxabs / rms)
@@ -125,7 +127,8 @@ def test_pack_roundtrip(M, name):
 
 # ---- routing ------------------------------------------------------------------
 
-ROUTE_CASES = ["tiny", "decode", "smallrow2", "smallrow5", "smallrow8", "prefill512", "prefill4096"]
+ROUTE_CASES = ["tiny", "decode", "smallrow2", "smallrow3", "smallrow4", "smallrow5", "smallrow8", "prefill512",
+               "prefill4096"]
 
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
@@ -177,6 +180,28 @@ def test_tiny_decode_both_paths(M, T, gemv):
     torch.cuda.synchronize()
     sub = dict(case, x=x, T=T)
     check_close(y.cpu().numpy(), oracle_rows(sub), f"tiny decode T={T} gemv_max_rows={gemv}")
+
+
+@pytest.mark.parametrize("T", [9, 20])
+def test_decode_above_gemv_rows_takes_gemm_path(M, T):
+    """moe_forward_decode with more rows than the GEMV takes runs the grouped-GEMM
+    path (checked by which kernels ran) and matches the oracle."""
+    from bit_quantized_moe_router_amd import (K_DOWN_GEMM, K_GATEUP_GEMV, moe_profile_enable, moe_profile_read,
+                                              moe_profile_reset)
+    case = mi.make_case("decode")
+    lay = get_layer(M, case)
+    x = mi.gen_x(T, case["cfg"]["H"], 6100 + T)
+    moe_profile_reset()
+    moe_profile_enable((1 << K_GATEUP_GEMV) | (1 << K_DOWN_GEMM))
+    try:
+        y = lay.forward_decode(dev(M, x), None)
+        torch.cuda.synchronize()
+        ran = (moe_profile_read(K_GATEUP_GEMV)[1], moe_profile_read(K_DOWN_GEMM)[1])
+    finally:
+        moe_profile_enable(0)
+        moe_profile_reset()
+    assert ran == (0, 1), ran
+    check_close(y.cpu().numpy(), oracle_rows(dict(case, x=x, T=T)), f"decode T={T} (grouped GEMM)")
 
 
 def test_decode_T1(M):
@@ -248,7 +273,7 @@ def test_decode_activation_scale(M, gemv, scale):
 
 
 def _sample_tokens(case, n, seed):
-    """Seeded sample that also holds tokens routed to the most loaded expert of each chunk."""
+    """Seeded random sample of the tokens, plus the first and the last token."""
     rng = np.random.default_rng(seed)
     T = case["T"]
     toks = set(rng.choice(T, size=min(n, T), replace=False).tolist())
@@ -385,6 +410,8 @@ def test_host_sync_routing_same_result(M, name):
     finally:
         lay.set_desc(host_sync_routing=0)
     assert torch.equal(y0, y1)
+    toks = _sample_tokens(case, 24, seed=11)
+    check_close(y1.cpu().numpy()[toks], oracle_rows(case, toks), f"{name} host-synchronised routing")
 
 
 def test_batch_invariant_gemm_path(M):
@@ -464,6 +491,8 @@ def test_dequant_pass_same_result(M, name):
         lay.set_desc(dequant_pass=0)
     assert ran >= 1
     assert torch.equal(y0, y1)
+    toks = _sample_tokens(case, 24, seed=12)
+    check_close(y1.cpu().numpy()[toks], oracle_rows(case, toks), f"{name} separate dequant pass")
 
 
 def test_zero_tokens_is_noop(M):
