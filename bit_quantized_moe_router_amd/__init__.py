@@ -71,6 +71,7 @@ def lib():
         L.moe_route.argtypes = [D, vp, i32, vp, vp, P(Routing), vp, sz, vp]
         L.moe_forward_prefill.argtypes = [D, vp, vp, vp, vp, i32, vp, vp, sz, vp]
         L.moe_forward_decode.argtypes = [D, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+        L.moe_forward_decode_static.argtypes = [D, vp, vp, vp, vp, i32, vp, vp]
         L.moe_default_gemv_max_rows.argtypes = []
         L.moe_default_gemv_max_rows.restype = i32
         L.moe_status_str.argtypes = [C.c_int]
@@ -83,7 +84,7 @@ def lib():
         L.moe_profile_reset.argtypes = []
         L.moe_profile_read.argtypes = [i32, P(C.c_double), P(i32)]
         for name in ("moe_packed_bytes", "moe_workspace_bytes", "moe_max_tiles", "moe_pack_weights",
-                     "moe_route", "moe_forward_prefill", "moe_forward_decode",
+                     "moe_route", "moe_forward_prefill", "moe_forward_decode", "moe_forward_decode_static",
                      "moe_probe_stream_read", "moe_probe_mfma_rate", "moe_profile_enable",
                      "moe_profile_reset", "moe_profile_read"):
             getattr(L, name).restype = C.c_int
@@ -166,6 +167,12 @@ def moe_forward_decode(desc, packed, router_w, logit_bias, x, T, y, ws, stream=N
     _check(lib().moe_forward_decode(C.byref(desc), _ptr(packed), _ptr(router_w), _ptr(logit_bias),
                                     _ptr(x), T, _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)))
+
+
+def moe_forward_decode_static(desc, packed, router_w, logit_bias, x, T, y, stream=None):
+    """moe_forward_decode on the library's fixed device scratch (no workspace argument)."""
+    _check(lib().moe_forward_decode_static(C.byref(desc), _ptr(packed), _ptr(router_w), _ptr(logit_bias),
+                                           _ptr(x), T, _ptr(y), _stream(stream)))
 
 
 def moe_probe_stream_read(src, nbytes, sink, max_workgroups, stream=None):

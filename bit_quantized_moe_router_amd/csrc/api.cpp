@@ -380,6 +380,36 @@ moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_
   return MOE_OK;
 }
 
+// ---- decode without allocation (moe_forward_decode_static) -------------------
+// The workspace of moe_forward_decode_static: a fixed device array that each
+// GPU the library runs on holds until the process ends.  Host code never uses
+// the array's name as an address (it is the host-side stand-in); the device
+// address is taken once per device with hipGetSymbolAddress, with that device
+// current, and kept in g_scratch_ptr.  Every call on one GPU shares the array,
+// so calls that overlap on one GPU race.  No decode kernel reads a workspace
+// byte it has not written in the same call, so nothing needs clearing.
+constexpr size_t kStaticScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+moe_status static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 // The grouped GEMM path over T tokens, max_chunk tokens at a time; the
 // workspace is carved for one chunk and reused (launches are stream-ordered).
 moe_status prefill_loop(const moe_layer_desc* d, const void* packed, const float* wr, const float* bias,
@@ -524,6 +554,25 @@ moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, co
   }));
   TRY(timed(6, s, "partial-output sum", [&](const KTime& kt) { return launch_gemv_reduce(L, C, part, s, kt); }));
   return MOE_OK;
+}
+
+moe_status moe_forward_decode_static(const moe_layer_desc* desc, const void* packed, const float* router_w,
+                                     const float* logit_bias, const uint16_t* x, int32_t T, float* y,
+                                     void* stream) {
+  TRY(validate_desc(desc));
+  if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %d)", T);
+  if (T == 0) return MOE_OK;
+  if (desc->host_sync_routing || desc->dequant_pass)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "the static-scratch decode takes neither host_sync_routing nor dequant_pass");
+  if (!packed || !router_w || !x || !y) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+  const size_t need = ws_layout(desc, T < desc->max_chunk ? T : desc->max_chunk).total;
+  if (need > kStaticScratchBytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "this layer needs %zu bytes of scratch at T=%d; the static scratch holds %zu",
+                need, T, kStaticScratchBytes);
+  TRY(check_device());
+  void* ws = nullptr;
+  TRY(static_scratch(&ws));
+  return moe_forward_decode(desc, packed, router_w, logit_bias, x, T, y, ws, kStaticScratchBytes, stream);
 }
 
 const char* moe_status_str(moe_status s) {

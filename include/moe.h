@@ -231,6 +231,28 @@ moe_status moe_forward_decode(const moe_layer_desc *desc, const void *packed,
                               const uint16_t *x, int32_t T, float *y,
                               void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * moe_forward_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * moe_forward_decode, whose workspace is here a fixed device array of
+ * MOE_STATIC_SCRATCH_BYTES inside the library; each GPU the library runs on
+ * holds its own copy until the process ends.  The call allocates and frees
+ * nothing (its first call on a device looks the array's address up once).
+ * Limits and errors:
+ *   - MOE_ERR_WORKSPACE_TOO_SMALL when the layer's decode workspace at this T
+ *     exceeds MOE_STATIC_SCRATCH_BYTES (moe_workspace_bytes(desc, T) tells);
+ *     16 MiB hold T <= 8 at H=2048, E=256, k=8, I=Is=512 (9.2 MiB);
+ *   - MOE_ERR_INVALID_ARGUMENT for host_sync_routing or dequant_pass set.
+ * Every call on one GPU uses the same array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and give undefined results;
+ * serialise them.  Stream-ordered calls on one stream are safe.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+moe_status moe_forward_decode_static(const moe_layer_desc *desc, const void *packed,
+                                     const float *router_w, const float *logit_bias,
+                                     const uint16_t *x, int32_t T, float *y, void *stream);
+
 /* Default R* of the library (host output). */
 int32_t moe_default_gemv_max_rows(void);
 
