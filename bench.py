@@ -63,8 +63,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--counter-pass", action="store_true",
-                   help="short run for rocprofv3 --pmc passes: 8 prefill steps, then copies of known size "
-                        "that calibrate FETCH_SIZE/WRITE_SIZE; prints no JSON line")
+                   help="short run for rocprofv3 --pmc passes: 4 prefill T=4096 steps, 8 prefill T=512 calls, "
+                        "16 cold decode calls, then copies of known size that calibrate FETCH_SIZE/WRITE_SIZE; "
+                        "prints no JSON line")
     return p.parse_args()
 
 
@@ -192,8 +193,17 @@ def main():
             lay.set_desc(**kw)
 
     if a.counter_pass:
-        for i in range(8):
+        # 4 prefill T=4096 steps (8 chunks), 8 prefill T=512 calls, 16 cold
+        # decode T=1 calls, then copies of known size.
+        for i in range(4):
             step(i)
+        x512 = to_dev(mi.make_case("prefill512")["x"], dev)
+        for i in range(8):
+            layers[i % len(layers)].forward_prefill(x512, None, ys[0][:512])
+        dl = list(layers) + [clone_layer(layers[0], 8) for _ in range(16 - len(layers))]
+        xd = to_dev(mi.gen_x(16, H, 4242), dev)
+        for i in range(16):
+            dl[i].forward_decode(xd[i:i + 1], None, ys[0][:1])
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)  # 256 MiB
         dst = torch.empty_like(src)
         for _ in range(3):
