@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# MOE_ORACLE_LIB selects another build of the same source (the sanitizer
+# build that tests/test_oracle_sanitized.py loads in a child process).
+LIB_PATH = os.environ.get("MOE_ORACLE_LIB", os.path.join(HERE, "liboracle.so"))
 
 _lib = None
 
@@ -33,6 +35,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
+            if "MOE_ORACLE_LIB" in os.environ:
+                raise ImportError(f"MOE_ORACLE_LIB={LIB_PATH} does not exist")
             from . import build as _b
             _b.build()
         L = C.CDLL(LIB_PATH)
