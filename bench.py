@@ -23,7 +23,8 @@ Run order (one process):
  6. decode: cold (24 layer copies rotated, about 420 MB read between two
     calls on the same copy, so every call reads its weights from HBM) and warm
     (one copy, one token row, every byte cached) per-call latency; graph
-    replay; the T = 1..8 sweep of both paths behind the row threshold; the
+    replay; the T = 1..8 sweep of both paths behind the row threshold and of
+    the GEMV with the grouped GEMM's arithmetic (batch_invariant = 1); the
     decode `roofline` against 8 TB/s and against the streaming-read probe at
     the same byte count;
  7. probes: sustained 16-byte-per-lane streaming read over 4 GiB, and the
@@ -435,17 +436,18 @@ def main():
                                    "frac_of_probe": round(ex_bytes / (gemv_ex["avg_us"] * 1e-6) / 1e9 /
                                                           pr_ex["kernel_GBs"], 4) if gemv_ex else None}}
 
-    # Row-count sweep of both paths (GEMV forced, grouped GEMM forced), cold.
+    # Row-count sweep, cold: the GEMV forced, the grouped GEMM forced, and the
+    # GEMV with the grouped GEMM's arithmetic (batch_invariant = 1) forced.
     sweep = {}
     for T_ in (1, 2, 3, 4, 5, 6, 7, 8):
         row = {}
-        for name, r in (("gemv", 8), ("gemm", 0)):
+        for name, r, bi in (("gemv", 8, 0), ("gemm", 0, 0), ("gemv_batch_invariant", 8, 1)):
             for lay in dlayers:
-                lay.set_desc(gemv_max_rows=r)
+                lay.set_desc(gemv_max_rows=r, batch_invariant=bi)
             row[name] = round(decode_b2b(T_, True, 100), 2)
         sweep[str(T_)] = row
     for lay in dlayers:
-        lay.set_desc(gemv_max_rows=-1)
+        lay.set_desc(gemv_max_rows=-1, batch_invariant=0)
     del dlayers[len(layers):]
 
     # ---- 7. probes: sustained streaming read, MFMA-only rate and clock ----
@@ -510,7 +512,8 @@ def main():
                    "warm_us_per_layer": round(dec_warm_b2b, 3), "warm_per_call_us": dec_warm,
                    "graph_us_per_layer": round(dec_graph_us, 3), "kernels_us": dkern, "roofline": dec_roof,
                    "layer_copies_rotated": NC, "token_rows_rotated": NX,
-                   "sweep_us_per_layer_cold": sweep, "default_gemv_max_rows": moe.moe_default_gemv_max_rows()},
+                   "sweep_us_per_layer_cold": sweep,
+                   "batch_invariant_us_per_layer": sweep["1"]["gemv_batch_invariant"], "default_gemv_max_rows": moe.moe_default_gemv_max_rows()},
         "probes": {"stream_read_4GiB": pr_big, "mfma": mfma_probe},
         "env": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": cus, "rocm": rocm,
                 "torch": torch.__version__, "hip_runtime": torch.version.hip,

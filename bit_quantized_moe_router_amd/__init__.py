@@ -34,7 +34,7 @@ class MoEError(RuntimeError):
 class LayerDesc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("hidden", "n_experts", "top_k", "inter", "shared_inter",
                                          "group_size", "gemv_max_rows", "max_chunk", "tile_rows",
-                                         "host_sync_routing", "dequant_pass")]
+                                         "host_sync_routing", "dequant_pass", "batch_invariant")]
 
 
 class QMatrix(C.Structure):
@@ -109,9 +109,9 @@ def _stream(stream):
 
 
 def make_desc(hidden, n_experts, top_k, inter, shared_inter, gemv_max_rows=-1, max_chunk=2048,
-              tile_rows=0, group_size=64, host_sync_routing=0, dequant_pass=0) -> LayerDesc:
+              tile_rows=0, group_size=64, host_sync_routing=0, dequant_pass=0, batch_invariant=0) -> LayerDesc:
     return LayerDesc(hidden, n_experts, top_k, inter, shared_inter, group_size, gemv_max_rows,
-                     max_chunk, tile_rows, host_sync_routing, dequant_pass)
+                     max_chunk, tile_rows, host_sync_routing, dequant_pass, batch_invariant)
 
 
 def moe_packed_bytes(desc: LayerDesc) -> int:

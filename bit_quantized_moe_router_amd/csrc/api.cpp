@@ -34,6 +34,10 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 
 constexpr int kDefaultTileRows = 128;
 constexpr int kDefaultGemvMaxRows = 8;  // measured: the GEMV path is faster at every T <= 8 (the decode maximum)
+// With batch_invariant = 1 both paths give the same bits, so the threshold only
+// picks the faster: measured, the GEMV path with the grouped GEMM's arithmetic
+// is faster up to 4 rows (26 us at T = 1 against 47 us) and slower from 5.
+constexpr int kDefaultGemvMaxRowsBi = 4;
 constexpr int kMaxRowsDecode = 8;
 
 moe_status validate_desc(const moe_layer_desc* d) {
@@ -61,6 +65,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "host_sync_routing must be 0 or 1 (got %d)", d->host_sync_routing);
   if (d->dequant_pass != 0 && d->dequant_pass != 1)
     return fail(MOE_ERR_INVALID_ARGUMENT, "dequant_pass must be 0 or 1 (got %d)", d->dequant_pass);
+  if (d->batch_invariant != 0 && d->batch_invariant != 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "batch_invariant must be 0 or 1 (got %d)", d->batch_invariant);
   return MOE_OK;
 }
 
@@ -533,7 +539,8 @@ moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, co
   if (T == 0) return MOE_OK;
   TRY(check_device());
   // T > R* (and always T > 8, the GEMV's largest row count) takes the grouped-GEMM path.
-  const int R = desc->gemv_max_rows < 0 ? kDefaultGemvMaxRows : desc->gemv_max_rows;
+  const int R = desc->gemv_max_rows >= 0 ? desc->gemv_max_rows
+                : desc->batch_invariant ? kDefaultGemvMaxRowsBi : kDefaultGemvMaxRows;
   const bool gemv = T <= R && T <= desc->max_chunk && (int64_t)T * desc->hidden <= 32768;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!gemv) return prefill_loop(desc, packed, router_w, logit_bias, x, T, y, ws, s);
@@ -549,6 +556,16 @@ moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, co
                                o.wsq, o.ids, o.tw, nullptr, nullptr, nullptr, s, &two, kt);
   }));
   const ChunkArgs C = chunk_args(desc, x, T, o, ws, w, y);
+  if (desc->batch_invariant) {
+    // The grouped-GEMM path's arithmetic: gate/up into fp16 h rows, then down + combine.
+    TRY(timed(5, s, "top-k + gate/up GEMV (grouped-GEMM arithmetic)", [&](const KTime& kt) {
+      return launch_gemv_gateup_bi(L, C, o.logits, C.hbuf, o.ids, o.tw, s, kt);
+    }));
+    TRY(timed(6, s, "down GEMV + combine (grouped-GEMM arithmetic)", [&](const KTime& kt) {
+      return launch_gemv_down_bi(L, C, C.hbuf, o.ids, o.tw, s, kt);
+    }));
+    return MOE_OK;
+  }
   TRY(timed(5, s, "top-k + gate/up + split down GEMV", [&](const KTime& kt) {
     return launch_gemv_experts(L, C, o.logits, part, s, kt);
   }));

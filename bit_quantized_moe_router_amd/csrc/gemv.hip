@@ -127,41 +127,31 @@ __global__ __launch_bounds__(kRedThreads) void k_gemv_reduce(LayerArgs L, ChunkA
   }
 }
 
-__global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_gemv_experts(LayerArgs L, ChunkArgs C, const float* logits,
-                                                            float* __restrict__ part, int nbs) {
-  const int slot = (int)blockIdx.x / nbs, nb = (int)blockIdx.x - slot * nbs;
-  const int T = C.T, H = L.H, G = H / kGroup, E = L.E, k = L.k, N = T * k;
-  const int tid = threadIdx.x;
+// ---------------------------------------------------------------------------
+// Prologue of a decode workgroup (any multiple of 64 threads): the activation rows
+// into LDS as fp16(x / 256) (xl, [T][H]), the top-k of each row (wave t for
+// row t; `ordered` = false lists a row's experts in expert order when exactly k
+// logits pass the threshold, which is all the split-down GEMV needs, while
+// true ranks them as the routing outputs do), then this workgroup's expert
+// and its rows in flat assignment order: s_info = (expert, rows), tok/arow/wgt
+// per row.  Slot: the slot-th smallest selected expert, or the shared expert
+// at slot = number of selected experts.  Ends with a barrier.
+__device__ __forceinline__ void decode_prologue(const LayerArgs& L, const ChunkArgs& C, const float* logits, int slot,
+                                                bool ordered, uint16_t* xl, int* lists, int* s_ids, float* s_tw,
+                                                uint32_t* s_bm, int* tok, int* arow, float* wgt, int* s_info) {
+  const int T = C.T, H = L.H, E = L.E, k = L.k, N = T * k;
+  const int tid = threadIdx.x, nthr = blockDim.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int h = lane >> 5, col = lane & 31;
-  // [T][H] x rows as fp16(x / 256), then [T][2E+16] top-k lists
-  extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
-  uint16_t* xl = reinterpret_cast<uint16_t*>(gsm);
-  int* lists = reinterpret_cast<int*>(gsm + (size_t)T * H * 2);
-  // [g][row] sums of the fp16 activations over the slots biased by 1024 (xsa) and by 64 (xsb)
-  __shared__ __attribute__((aligned(16))) float xsa[kMaxGroups * kGemvMaxRows];
-  __shared__ __attribute__((aligned(16))) float xsb[kMaxGroups * kGemvMaxRows];
-  __shared__ int s_ids[kMaxAssign];
-  __shared__ float s_tw[kMaxAssign];
-  __shared__ uint32_t s_bm[kMaxE / 32];
-  __shared__ int tok[kGemvMaxRows], arow[kGemvMaxRows], s_info[2];
-  __shared__ float wgt[kGemvMaxRows], s_hs[kGemvMaxRows];
-  // h of the 32 columns as two bf16 parts (hi = bf16(h), lo = bf16(h - hi)), as pairs
-  __shared__ __attribute__((aligned(16))) uint32_t s_h[kGemvMaxRows][16];
-  __shared__ __attribute__((aligned(16))) uint32_t s_hl[kGemvMaxRows][16];
-  __shared__ float red[kFuWaves][kGemvMaxRows][2][32];
-
   // ---- activation rows into registers (their latency overlaps the top-k) ----
   const int H8 = H / 8, nx = T * H8;
   uint4 xr0 = make_uint4(0u, 0u, 0u, 0u), xr1 = xr0;
   if (tid < nx) xr0 = reinterpret_cast<const uint4*>(C.x)[tid];
-  if (tid + kFuThreads < nx) xr1 = reinterpret_cast<const uint4*>(C.x)[tid + kFuThreads];
+  if (tid + nthr < nx) xr1 = reinterpret_cast<const uint4*>(C.x)[tid + nthr];
   // ---- top-k of each row ----
-  // The GEMV needs each row's selected experts and weights, not their order.
-  if (wave < T) topk_small(logits + (int64_t)wave * E, E, k, wave, s_ids, s_tw, lists + wave * (2 * E + 16), false);
+  if (wave < T) topk_small(logits + (int64_t)wave * E, E, k, wave, s_ids, s_tw, lists + wave * (2 * E + 16), ordered);
   if (tid < nx) reinterpret_cast<uint4*>(xl)[tid] = to_f16x8_scaled(xr0);
-  if (tid + kFuThreads < nx) reinterpret_cast<uint4*>(xl)[tid + kFuThreads] = to_f16x8_scaled(xr1);
-  for (int i = tid + 2 * kFuThreads; i < nx; i += kFuThreads)
+  if (tid + nthr < nx) reinterpret_cast<uint4*>(xl)[tid + nthr] = to_f16x8_scaled(xr1);
+  for (int i = tid + 2 * nthr; i < nx; i += nthr)
     reinterpret_cast<uint4*>(xl)[i] = to_f16x8_scaled(reinterpret_cast<const uint4*>(C.x)[i]);
   if (tid < kMaxE / 32) s_bm[tid] = 0u;
   __syncthreads();
@@ -242,6 +232,33 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
     }
   }
   __syncthreads();
+}
+
+__global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_gemv_experts(LayerArgs L, ChunkArgs C, const float* logits,
+                                                            float* __restrict__ part, int nbs) {
+  const int slot = (int)blockIdx.x / nbs, nb = (int)blockIdx.x - slot * nbs;
+  const int T = C.T, H = L.H, G = H / kGroup;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, col = lane & 31;
+  // [T][H] x rows as fp16(x / 256), then [T][2E+16] top-k lists
+  extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
+  uint16_t* xl = reinterpret_cast<uint16_t*>(gsm);
+  int* lists = reinterpret_cast<int*>(gsm + (size_t)T * H * 2);
+  // [g][row] sums of the fp16 activations over the slots biased by 1024 (xsa) and by 64 (xsb)
+  __shared__ __attribute__((aligned(16))) float xsa[kMaxGroups * kGemvMaxRows];
+  __shared__ __attribute__((aligned(16))) float xsb[kMaxGroups * kGemvMaxRows];
+  __shared__ int s_ids[kMaxAssign];
+  __shared__ float s_tw[kMaxAssign];
+  __shared__ uint32_t s_bm[kMaxE / 32];
+  __shared__ int tok[kGemvMaxRows], arow[kGemvMaxRows], s_info[2];
+  __shared__ float wgt[kGemvMaxRows], s_hs[kGemvMaxRows];
+  // h of the 32 columns as two bf16 parts (hi = bf16(h), lo = bf16(h - hi)), as pairs
+  __shared__ __attribute__((aligned(16))) uint32_t s_h[kGemvMaxRows][16];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hl[kGemvMaxRows][16];
+  __shared__ float red[kFuWaves][kGemvMaxRows][2][32];
+
+  decode_prologue(L, C, logits, slot, false, xl, lists, s_ids, s_tw, s_bm, tok, arow, wgt, s_info);
   const int e = s_info[0], rows = s_info[1];
   const bool shared = e == L.E;
   const int Iw = shared ? L.Is : L.I;
@@ -426,6 +443,242 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
 }
 
 // ---------------------------------------------------------------------------
+// Decode with the grouped-GEMM path's arithmetic (batch-invariant decode,
+// desc.batch_invariant = 1).  The GEMV path above folds scale and bias per
+// group and splits the down projection, so its bits differ from the grouped
+// GEMM's; these two kernels compute each output element with exactly the
+// operations of the grouped-GEMM path, so a row's output is the same at any
+// row count and on either side of the row threshold (the dothoosh page on
+// Candle's Metal kernels, the section on outputs that change with the kernel
+// chosen by row count):
+//  * gate/up: the same fp16(x / 256) activations and fp16 weights rebuilt
+//    with one rounding of s*q + b (dequant_f16, the grouped GEMM's rebuild),
+//    the same v_mfma_f32_32x32x16_f16 steps in the same order over K into one
+//    fp32 accumulator per element, starting from zero, with the grouped GEMM's
+//    padding of the group count to a multiple of 4 (zero weights, valid A);
+//    then silu(256 g) * 256 u rounded to fp16(h / 256);
+//  * down: the same chain over the intermediate's groups; routed outputs
+//    rounded to fp16(o / 256), the shared expert's output 256 * acc in fp32;
+//  * combine: y = shared + sum over j in top-k rank order of
+//    fma(256 w_tj, o_tj, y), the routing weights from the ranked top-k.
+// An MFMA output element depends only on its row of A and its column of B, so
+// which other rows share the A operand does not change it.
+//
+// Gate/up (k_gemv_gateup_bi): one workgroup per (slot, 32 intermediate
+// columns), like the GEMV.  The chain over K is sequential, so it is handed
+// from wave to wave: each wave loads and rebuilds the weights of four groups
+// of one matrix in parallel with the others, then, in step order, continues
+// its matrix's accumulators (passed through LDS) over its groups.  Gate and up
+// are two chains on different SIMDs; only the MFMAs of each chain are serial,
+// the loads and the rebuild are not.
+// Down + combine (k_gemv_down_bi): one workgroup per (32 output columns,
+// token); each wave runs the chain of one of the token's rows (routed rows in
+// rank order, then the shared row), then the workgroup combines them in rank
+// order and writes y once.
+// ---------------------------------------------------------------------------
+constexpr int kBiGroupsPerWave = 4;
+constexpr int kBiDnWaves = 16;
+
+__device__ __forceinline__ uint16_t to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+typedef _Float16 f16x2b_t __attribute__((ext_vector_type(2)));
+
+// fp16 weights of one packed dword (8 codes) rebuilt as fp16(s*q + b), the
+// k-slot order of the MFMA B operand: the grouped GEMM's rebuild (the
+// exponent of 1024 gives nibbles 0-3 unit steps, that of 64 nibbles 4-7;
+// the offsets are removed exactly and one fp16 FMA per pair rounds s*q + b).
+__device__ __forceinline__ f16x8_t dequant_f16(uint32_t d, f16x2b_t s2, f16x2b_t b2) {
+  const f16x2b_t off_lo = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const f16x2b_t off_hi = {(_Float16)-64.0f, (_Float16)-64.0f};
+  const uint32_t d8 = d >> 8;
+  const f16x2b_t q0 = __builtin_bit_cast(f16x2b_t, and_or(d, 0x000F000Fu, 0x64006400u)) + off_lo;
+  const f16x2b_t q1 = __builtin_bit_cast(f16x2b_t, and_or(d, 0x00F000F0u, 0x54005400u)) + off_hi;
+  const f16x2b_t q2 = __builtin_bit_cast(f16x2b_t, and_or(d8, 0x000F000Fu, 0x64006400u)) + off_lo;
+  const f16x2b_t q3 = __builtin_bit_cast(f16x2b_t, and_or(d8, 0x00F000F0u, 0x54005400u)) + off_hi;
+  return __builtin_bit_cast(
+      f16x8_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q0, s2, b2)),
+                          __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q1, s2, b2)),
+                          __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q2, s2, b2)),
+                          __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q3, s2, b2))));
+}
+
+// Scale and bias of a block row as fp16 pairs; zero for padded groups (live = false).
+__device__ __forceinline__ void sb_f16(uint32_t sb, bool live, f16x2b_t& s2, f16x2b_t& b2) {
+  const uint32_t v = live ? sb : 0u;
+  const _Float16 sh = (_Float16)bf16_bits_to_f32(v & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(v >> 16);
+  s2 = f16x2b_t{sh, sh};
+  b2 = f16x2b_t{bh, bh};
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int c) { return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w; }
+
+constexpr int kBiUpWaves = 16;  // waves 0-7 carry the gate chain, waves 8-15 the up chain
+
+__global__ __launch_bounds__(kBiUpWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void k_gemv_gateup_bi(LayerArgs L, ChunkArgs C, const float* logits, uint16_t* __restrict__ h16,
+                      int32_t* __restrict__ ids_out, float* __restrict__ tw_out, int nbs) {
+  const int slot = (int)blockIdx.x / nbs, nb = (int)blockIdx.x - slot * nbs;
+  const int T = C.T, H = L.H, G = H / kGroup, k = L.k;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, col = lane & 31;
+  extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
+  uint16_t* xl = reinterpret_cast<uint16_t*>(gsm);
+  int* lists = reinterpret_cast<int*>(gsm + (size_t)T * H * 2);
+  __shared__ int s_ids[kMaxAssign];
+  __shared__ float s_tw[kMaxAssign];
+  __shared__ uint32_t s_bm[kMaxE / 32];
+  __shared__ int tok[kGemvMaxRows], arow[kGemvMaxRows], s_info[2];
+  __shared__ float wgt[kGemvMaxRows];
+  __shared__ f32x16_t hand[2][64];  // the gate and up accumulators handed from wave to wave
+
+  decode_prologue(L, C, logits, slot, true, xl, lists, s_ids, s_tw, s_bm, tok, arow, wgt, s_info);
+  // The ranked routing of every row, for the down + combine kernel.
+  if (blockIdx.x == 0 && tid < T * k) {
+    ids_out[tid] = s_ids[tid];
+    tw_out[tid] = s_tw[tid];
+  }
+  const int e = s_info[0], rows = s_info[1];
+  const bool shared = e == L.E;
+  const int Iw = shared ? L.Is : L.I;
+  if (rows == 0 || nb * 32 >= Iw) return;  // workgroup-uniform
+  // Chain m (0: gate, 1: up).  Step s of a pass is run by wave s of the gate
+  // chain and by wave 8 + (s + 2) % 8 of the up chain, so the two waves of a
+  // step sit on different SIMDs (wave w on SIMD w % 4) and their MFMAs overlap.
+  const int m = wave >> 3, j = wave & 7;
+  const int step = m == 0 ? j : (j + 6) % 8;
+  const uint8_t* wbase = expert_base(L, e) + (int64_t)nb * G * 2 * kBlockBytes + m * kBlockBytes;
+  // The lane's A row: row col of the workgroup's rows (rows past the count
+  // repeat the last one; never stored), input columns 32h + 8c of a group.
+  const uint16_t* xrow = xl + tok[col < rows ? col : rows - 1] * H + h * 32;
+  const int Gp = (G + 3) & ~3;
+  f32x16_t acc = {};
+  constexpr int kPass = kFuWaves * kBiGroupsPerWave;
+  for (int p0 = 0; p0 < Gp; p0 += kPass) {
+    const int g0 = p0 + kBiGroupsPerWave * step;  // this wave's first group in this pass
+    f16x8_t bq[kBiGroupsPerWave][4];
+    if (g0 < Gp) {
+      uint4 cq[kBiGroupsPerWave];
+      uint32_t sq[kBiGroupsPerWave];
+#pragma unroll
+      for (int q = 0; q < kBiGroupsPerWave; q++) {
+        const int g = g0 + q, gg = g < G ? g : G - 1;  // padded groups read a valid block, rebuilt as zero
+        const uint8_t* blk = wbase + (int64_t)gg * 2 * kBlockBytes;
+        cq[q] = *reinterpret_cast<const uint4*>(blk + lane * 16);
+        sq[q] = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
+      }
+#pragma unroll
+      for (int q = 0; q < kBiGroupsPerWave; q++) {
+        f16x2b_t s2, b2;
+        sb_f16(sq[q], g0 + q < G, s2, b2);
+#pragma unroll
+        for (int c = 0; c < 4; c++) bq[q][c] = dequant_f16(dword_of(cq[q], c), s2, b2);
+      }
+    }
+    // The chains, in step order: the wave of step s continues its chain's accumulators over its groups.
+    for (int st = 0; st < kFuWaves; st++) {
+      if (step == st && g0 < Gp) {  // wave-uniform
+        if (p0 != 0 || st != 0) acc = hand[m][lane];
+#pragma unroll
+        for (int q = 0; q < kBiGroupsPerWave; q++) {
+          const int g = g0 + q;
+          if (g < Gp) {
+            const int gg = g < G ? g : G - 1;
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+              const f16x8_t a = *reinterpret_cast<const f16x8_t*>(xrow + gg * kGroup + 8 * c);
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq[q][c], acc, 0, 0, 0);
+            }
+          }
+        }
+        hand[m][lane] = acc;
+      }
+      __syncthreads();
+    }
+  }
+  // SwiGLU of the grouped GEMM's epilogue, fp16(h / 256) into h16[assignment row].
+  if (wave == 0) {
+    const f32x16_t accg = hand[0][lane], accu = hand[1][lane];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+      if (r < rows) {
+        const float hv = silu_mul(256.f * accg[i], 256.f * accu[i]);
+        h16[(int64_t)arow[r] * C.Imax + nb * 32 + col] = to_f16_bits(hv * (1.f / 256.f));
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBiDnWaves * 64) void k_gemv_down_bi(LayerArgs L, ChunkArgs C, const uint16_t* __restrict__ h16,
+                                                                  const int32_t* __restrict__ ids,
+                                                                  const float* __restrict__ tw) {
+  const int ob = blockIdx.x, t = blockIdx.y;  // 32 output columns of token t
+  const int H = L.H, k = L.k, Tk = C.T * k;
+  const int nrow = k + (L.Is > 0 ? 1 : 0);  // the token's routed rows in rank order, then its shared row
+  const int tid = threadIdx.x, nwave = blockDim.x >> 6;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, col = lane & 31;
+  __shared__ uint16_t o16[16][32];  // routed outputs, fp16(o / 256)
+  __shared__ float ysh[32];         // shared expert's output, fp32
+  for (int j = wave; j < nrow; j += nwave) {  // wave-uniform
+    const bool shared = j == k;
+    const int a = shared ? Tk + t : t * k + j;  // the row of h
+    const int e = shared ? L.E : ids[a];
+    const int Iw = shared ? L.Is : L.I, Gd = Iw / kGroup, Gdp = (Gd + 3) & ~3;
+    const uint8_t* dbase = expert_base(L, e) + (shared ? L.shared_gateup_bytes : L.gateup_bytes) + (int64_t)ob * Gd * kBlockBytes;
+    // Every lane's A row is this assignment's row of h (the one result row read is row 0).
+    const uint16_t* hrow = h16 + (int64_t)a * C.Imax + h * 32;
+    f32x16_t acc = {};
+    // Weight codes of eight groups go out in one round (the cold reads); the
+    // rows of h, just written and in L2, four groups at a time.
+    for (int g0 = 0; g0 < Gdp; g0 += 8) {
+      uint4 cq[8];
+      uint32_t sq[8];
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int g = g0 + q, gg = g < Gd ? g : Gd - 1;
+        const uint8_t* blk = dbase + (int64_t)gg * kBlockBytes;
+        cq[q] = *reinterpret_cast<const uint4*>(blk + lane * 16);
+        sq[q] = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
+      }
+#pragma unroll
+      for (int q0 = 0; q0 < 8; q0 += 4) {
+        if (g0 + q0 >= Gdp) break;  // wave-uniform: Gdp is a multiple of 4
+        uint4 av[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int g = g0 + q0 + q, gg = g < Gd ? g : Gd - 1;
+#pragma unroll
+          for (int c = 0; c < 4; c++) av[q][c] = *reinterpret_cast<const uint4*>(hrow + gg * kGroup + 8 * c);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          f16x2b_t s2, b2;
+          sb_f16(sq[q0 + q], g0 + q0 + q < Gd, s2, b2);
+#pragma unroll
+          for (int c = 0; c < 4; c++)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, av[q][c]),
+                                                        dequant_f16(dword_of(cq[q0 + q], c), s2, b2), acc, 0, 0, 0);
+        }
+      }
+    }
+    // Row 0 of the result: register 0 of lanes 0..31 (column = lane).
+    if (lane < 32) {
+      if (shared) ysh[lane] = 256.f * acc[0];
+      else o16[j][lane] = to_f16_bits(acc[0]);
+    }
+  }
+  __syncthreads();
+  // The grouped GEMM's combine: the shared output, then the routed rows in rank order.
+  if (tid < 32) {
+    float yv = L.Is > 0 ? ysh[tid] : 0.f;
+    for (int j = 0; j < k; j++) yv = fmaf(256.f * tw[t * k + j], f16_bits_to_f32(o16[j][tid]), yv);
+    C.y[(int64_t)t * H + ob * 32 + tid] = yv;
+  }
+}
+
+// ---------------------------------------------------------------------------
 hipError_t launch_gemv_experts(const LayerArgs& L, const ChunkArgs& C, const float* logits, float* part,
                                hipStream_t s, const KTime& kt) {
   const int Imax = L.I > L.Is ? L.I : L.Is;
@@ -438,6 +691,30 @@ hipError_t launch_gemv_experts(const LayerArgs& L, const ChunkArgs& C, const flo
   if (smem > (size_t)kGuSmemMax || C.T > kGemvMaxRows || C.Tk > kMaxAssign) return hipErrorInvalidValue;
   MOE_LAUNCH(k_gemv_experts, dim3((unsigned)(n_slots * nbs)), dim3(kFuThreads), smem, s, kt.start, kt.stop, L, C,
              logits, part, nbs);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_gateup_bi(const LayerArgs& L, const ChunkArgs& C, const float* logits, uint16_t* h16,
+                                 int32_t* ids, float* tw, hipStream_t s, const KTime& kt) {
+  const int Imax = L.I > L.Is ? L.I : L.Is;
+  const int n_slots = (L.E < C.Tk ? L.E : C.Tk) + 1;
+  const int nbs = Imax / 32;
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_gemv_gateup_bi), kGuSmemMax, lds_set);
+  if (e != hipSuccess) return e;
+  const size_t smem = (size_t)C.T * L.H * 2 + (size_t)C.T * (2 * L.E + 16) * 4;
+  if (smem > (size_t)kGuSmemMax || C.T > kGemvMaxRows || C.Tk > kMaxAssign) return hipErrorInvalidValue;
+  MOE_LAUNCH(k_gemv_gateup_bi, dim3((unsigned)(n_slots * nbs)), dim3(kBiUpWaves * 64), smem, s, kt.start, kt.stop, L,
+             C, logits, h16, ids, tw, nbs);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_down_bi(const LayerArgs& L, const ChunkArgs& C, const uint16_t* h16, const int32_t* ids,
+                               const float* tw, hipStream_t s, const KTime& kt) {
+  if (L.H % 32 != 0 || C.T > kGemvMaxRows || C.Tk > kMaxAssign || L.k > 16) return hipErrorInvalidValue;
+  const int nrow = L.k + (L.Is > 0 ? 1 : 0), nwave = nrow < kBiDnWaves ? nrow : kBiDnWaves;
+  MOE_LAUNCH(k_gemv_down_bi, dim3((unsigned)(L.H / 32), (unsigned)C.T), dim3(nwave * 64), 0, s, kt.start, kt.stop, L,
+             C, h16, ids, tw);
   return hipGetLastError();
 }
 

@@ -100,6 +100,13 @@ hipError_t launch_gemv_experts(const LayerArgs& L, const ChunkArgs& C, const flo
                                hipStream_t s, const KTime& kt = KTime{});
 hipError_t launch_gemv_reduce(const LayerArgs& L, const ChunkArgs& C, const float* part, hipStream_t s,
                               const KTime& kt = KTime{});
+// Decode with the grouped-GEMM path's arithmetic: top-k (ranked routing into
+// ids/tw), gate/up + SwiGLU into h16 ([T*k + T][Imax] fp16(h / 256)); then the
+// down projection of every assignment and the per-token combine into y.
+hipError_t launch_gemv_gateup_bi(const LayerArgs& L, const ChunkArgs& C, const float* logits, uint16_t* h16,
+                                 int32_t* ids, float* tw, hipStream_t s, const KTime& kt = KTime{});
+hipError_t launch_gemv_down_bi(const LayerArgs& L, const ChunkArgs& C, const uint16_t* h16, const int32_t* ids,
+                               const float* tw, hipStream_t s, const KTime& kt = KTime{});
 
 // Measurement probes (csrc/probe.hip): a 16-byte-per-lane streaming read of
 // `bytes` with at most max_wgs workgroups (sink: max_wgs words), and the

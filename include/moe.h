@@ -80,8 +80,8 @@ typedef struct {
     int32_t shared_inter;  /* Is: shared expert intermediate width, 0 = no shared expert */
     int32_t group_size;    /* must be 64 */
     int32_t gemv_max_rows; /* R*: moe_forward_decode uses the row-parallel GEMV path for
-                              T <= R* and the grouped GEMM path above; -1 = library default;
-                              0 = always GEMM; at most 8 */
+                              T <= R* and the grouped GEMM path above; -1 = library default
+                              (8, or 4 with batch_invariant = 1); 0 = always GEMM; at most 8 */
     int32_t max_chunk;     /* tokens per prefill chunk (1..8192); routing metadata is per chunk */
     int32_t tile_rows;     /* BM: rows per tile of the block map; 0 = library default (128);
                               one of 16, 32, 64, 128 */
@@ -97,6 +97,17 @@ typedef struct {
                               the shared expert are first rebuilt as fp16 into the workspace (a
                               separate pass), then the grouped GEMMs read fp16 weights.  Same rounding,
                               same results; the workspace grows by 4096/1152 x the packed size. */
+    int32_t batch_invariant; /* 0: the decode GEMV path folds scale and bias per group and splits the
+                              down projection (its own rounding).  1: the GEMV path computes every
+                              output element with the grouped-GEMM path's operations in the same order
+                              (fp16 weights rebuilt as s*q + b, fp16(x / 256), one MFMA chain over K,
+                              fp16(h / 256) and fp16(o / 256) intermediates, ranked routing weights,
+                              combine in rank order), so a row's output does not depend on the row
+                              threshold or on the other rows of the call (the dothoosh page on Candle,
+                              its section on outputs that change with the kernel chosen by row count).
+                              Costs time: the chain over K runs in order, so one row takes about 26 us
+                              instead of 20; the default R* is then 4, above which the grouped GEMM
+                              path (same bits) is faster. */
 } moe_layer_desc;
 
 /*
@@ -224,7 +235,10 @@ moe_status moe_forward_prefill(const moe_layer_desc *desc, const void *packed,
  * SwiGLU and the down projection of each workgroup's 32 intermediate columns
  * (partial output rows in the workspace); the sum of each token's partials in
  * a fixed order.  y is written once per element, with no atomics, so repeated
- * calls give identical bits.
+ * calls give identical bits.  With batch_invariant = 1 the GEMV path is
+ * instead: exact router logits; top-k, gate/up + SwiGLU into fp16 rows of h;
+ * down projection and combine, with the grouped GEMM path's operations, so
+ * its output equals that path's bit for bit at every T.
  */
 moe_status moe_forward_decode(const moe_layer_desc *desc, const void *packed,
                               const float *router_w, const float *logit_bias,
@@ -253,7 +267,8 @@ moe_status moe_forward_decode_static(const moe_layer_desc *desc, const void *pac
                                      const float *router_w, const float *logit_bias,
                                      const uint16_t *x, int32_t T, float *y, void *stream);
 
-/* Default R* of the library (host output). */
+/* Default R* of the library with batch_invariant = 0 (host output); with
+ * batch_invariant = 1 the default is 4. */
 int32_t moe_default_gemv_max_rows(void);
 
 const char *moe_status_str(moe_status s);

@@ -39,7 +39,9 @@ def get_layer(M, case, **kw):
     key = (case["cfg"]["H"], case["cfg"]["E"], case["cfg"]["I"], case["cfg"]["Is"], case["cfg"]["wseed"],
            case["k"], tuple(sorted(kw.items())))
     if key not in _LAYERS:
+        bi = kw.pop("batch_invariant", 0)
         _LAYERS[key] = M.MoELayer(case["w"], case["k"], max_tokens=kw.pop("max_tokens", 2048), **kw)
+        _LAYERS[key].set_desc(batch_invariant=bi)
     return _LAYERS[key]
 
 
@@ -545,3 +547,73 @@ def test_route_zero_router_with_bias(M, T):
     ref = orc.route(case["x"], w["router_w"], bias, 5, 16, with_shared=False)
     check_route(r, ref, f"zero router T={T}")
     assert np.array_equal(ref["topk_ids"], np.tile(np.arange(5, dtype=np.int32), (T, 1)))
+
+
+# ---- decode with the grouped-GEMM path's arithmetic (batch_invariant = 1) ----------
+
+def test_batch_invariant_decode_equals_gemm_path(M):
+    """With batch_invariant = 1 the GEMV path computes every output element with
+    the grouped-GEMM path's operations in the same order: decoding T = 1..8 rows
+    through the GEMV path (row threshold 8) and through the grouped-GEMM path
+    (row threshold 0) gives the same bits, and the same rows inside a 300-row
+    prefill too, so the row threshold cannot change a row's output.  The
+    library's default threshold in this mode (4) gives the same bits again."""
+    case = mi.make_case("decode")
+    H = case["cfg"]["H"]
+    gv = get_layer(M, case, gemv_max_rows=8, batch_invariant=1, max_tokens=512)
+    gm = get_layer(M, case, gemv_max_rows=0, batch_invariant=1, max_tokens=512)
+    gd = get_layer(M, case, gemv_max_rows=-1, batch_invariant=1, max_tokens=512)
+    big = mi.gen_x(300, H, 7702)
+    pos = [3, 40, 64, 128, 129, 200, 257, 299]
+    y_big = gm.forward_prefill(dev(M, big), None)
+    torch.cuda.synchronize()
+    for T in range(1, 9):
+        x = dev(M, big[pos[:T]])
+        y1 = gv.forward_decode(x, None).clone()
+        y0 = gm.forward_decode(x, None).clone()
+        yd = gd.forward_decode(x, None)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y0), T
+        assert torch.equal(yd, y0), T
+        for i in range(T):
+            assert torch.equal(y1[i], y_big[pos[i]]), (T, i)
+    check_close(y1.cpu().numpy(), oracle_rows(dict(case, x=big[pos], T=8)), "batch-invariant decode T=8")
+
+
+def test_batch_invariant_decode_zipf_large_tiles(M):
+    """The same against rows of a skewed 2048-token chunk (Zipf logit bias),
+    where the grouped GEMM serves the popular experts in 128-row and cut tiles."""
+    case = mi.make_case("prefill4096")
+    gm = get_layer(M, case, gemv_max_rows=0, max_tokens=2048)
+    gv = get_layer(M, case, gemv_max_rows=8, batch_invariant=1, max_tokens=2048)
+    x = case["x"][:2048]
+    bias = dev(M, case["bias"])
+    y_big = gm.forward_prefill(dev(M, x), bias)
+    torch.cuda.synchronize()
+    pos = [0, 1, 511, 1024, 1500, 1777, 2000, 2047]
+    for T in (1, 2, 5, 8):
+        y = gv.forward_decode(dev(M, x[pos[:T]]), bias)
+        torch.cuda.synchronize()
+        for i in range(T):
+            assert torch.equal(y[i], y_big[pos[i]]), (T, i)
+
+
+@pytest.mark.parametrize("T,H,E,k,I,Is,seed,zipf", [
+    (5, 64, 4, 4, 64, 64, 61, None),       # k == E, one group along H
+    (8, 192, 1, 1, 128, 0, 31, None),      # one expert, no shared expert, 3 groups (padded to 4)
+    (7, 128, 8, 3, 64, 128, 21, 22),       # Is != I, zipf bias
+    (8, 320, 16, 8, 192, 64, 71, None),    # odd group counts along H and I
+    (4, 8192, 32, 4, 128, 64, 93, None),   # 128 groups: four passes of the wave chain
+    (2, 128, 32, 16, 64, 64, 97, None),    # k = 16: 17 rows per token, more than the 16 down waves
+])
+def test_batch_invariant_decode_edge_shapes(M, T, H, E, k, I, Is, seed, zipf):
+    case = mi.small_layer(T, H, E, k, I, Is, seed, zipf)
+    gv = M.MoELayer(case["w"], k, max_tokens=T, gemv_max_rows=8)
+    gv.set_desc(batch_invariant=1)
+    gm = M.MoELayer(case["w"], k, max_tokens=T, gemv_max_rows=0)
+    x, b = dev(M, case["x"]), dev(M, case["bias"])
+    y1 = gv.forward_decode(x, b).clone()
+    y0 = gm.forward_decode(x, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y0)
+    check_close(y1.cpu().numpy(), oracle_rows(case), f"edge {case['name']} batch-invariant decode")
