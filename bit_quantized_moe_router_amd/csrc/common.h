@@ -12,7 +12,12 @@
 //          [32*(l/32), 32*(l/32)+32) of the group as 4 dwords; dword c covers
 //          columns 8c..8c+7 of that range with the even columns' codes in
 //          nibbles 0..3 and the odd columns' codes in nibbles 4..7.
-//   scale/bias: 32 dwords, dword r = scale bits | bias bits << 16 for row r.
+//   scale/bias: 32 dwords, dword r = fp16(scale) | fp16(bias) << 16 for row
+//          r: the bf16 values rounded to fp16 (to nearest even) by the packer.
+//          The conversion is exact for magnitudes in [2^-14, 65504]; smaller
+//          ones become fp16 subnormals, larger ones infinity.  The kernels
+//          rebuild weights in fp16 and so use these values directly: an fp16
+//          pair (s, b) feeds a packed FMA with each half broadcast.
 //
 // A dword d of codes expands to four bf16 pairs with one AND-OR each:
 //   ((d >> 4i) & 0x000F000F) | 0x43004300 = (bf16(128 + q[2i]), bf16(128 + q[2i+1]))

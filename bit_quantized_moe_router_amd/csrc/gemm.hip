@@ -231,13 +231,13 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   }
 
   const int aoff0 = col * kARow + h * 64;  // lane's A bytes: row 32 f + col, columns 32 h + 8 c
-  // Scale and bias of one block as fp16 pairs; zero (weights rebuild to 0)
-  // for groups padded past G.
+  // Scale and bias of one block (the blob's fp16 pair) broadcast to both
+  // halves, which the packed FMA takes by operand selection; zero (weights
+  // rebuild to 0) for groups padded past G.
   auto sbpair = [&](uint32_t sb, bool live, f16x2v_t& s2, f16x2v_t& b2) {
-    const uint32_t v = live ? sb : 0u;
-    const _Float16 sh = (_Float16)bf16_bits_to_f32(v & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(v >> 16);
-    s2 = f16x2v_t{sh, sh};
-    b2 = f16x2v_t{bh, bh};
+    const f16x2v_t v = __builtin_bit_cast(f16x2v_t, live ? sb : 0u);
+    s2 = __builtin_shufflevector(v, v, 0, 0);
+    b2 = __builtin_shufflevector(v, v, 1, 1);
   };
   // B operands of k-step 0 of the current group, rebuilt during the last
   // k-step of the previous group.
@@ -542,9 +542,8 @@ __global__ __launch_bounds__(256) void k_dequant_active(LayerArgs L, ChunkArgs C
   for (int b = blockIdx.y * 4 + wave; b < nblk; b += kDqSplit * 4) {
     const uint8_t* blk = L.blob + base + (int64_t)b * kBlockBytes;
     const uint4 q = *reinterpret_cast<const uint4*>(blk + lane * 16);
-    const uint32_t sb = *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4);
-    const _Float16 sh = (_Float16)bf16_bits_to_f32(sb & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(sb >> 16);
-    const f16x2v_t s2 = {sh, sh}, b2 = {bh, bh};
+    const f16x2v_t v = __builtin_bit_cast(f16x2v_t, *reinterpret_cast<const uint32_t*>(blk + kCodeBytes + col * 4));
+    const f16x2v_t s2 = __builtin_shufflevector(v, v, 0, 0), b2 = __builtin_shufflevector(v, v, 1, 1);
     uint8_t* dst = L.wdq + (base / kBlockBytes + b) * kDqBlockBytes + lane * 16;
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll

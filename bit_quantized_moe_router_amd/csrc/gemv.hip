@@ -377,8 +377,8 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
         expand_codes_f16(cuw[c], m1024, m64, reinterpret_cast<uint32_t*>(&q));
         du = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, q), du, 0, 0, 0);
       }
-      const float sg = 256.f * bf16_bits_to_f32(sbg[p] & 0xFFFFu), bg = 256.f * bf16_bits_to_f32(sbg[p] >> 16);
-      const float su = 256.f * bf16_bits_to_f32(sbu[p] & 0xFFFFu), bu = 256.f * bf16_bits_to_f32(sbu[p] >> 16);
+      const float sg = 256.f * f16_bits_to_f32(sbg[p] & 0xFFFFu), bg = 256.f * f16_bits_to_f32(sbg[p] >> 16);
+      const float su = 256.f * f16_bits_to_f32(sbu[p] & 0xFFFFu), bu = 256.f * f16_bits_to_f32(sbu[p] >> 16);
       const float cga = bg - 1024.f * sg, cgb = bg - 64.f * sg, cua = bu - 1024.f * su, cub = bu - 64.f * su;
       const float4 xav = *reinterpret_cast<const float4*>(&xsa[g * kGemvMaxRows + 4 * h]);
       const float4 xbv = *reinterpret_cast<const float4*>(&xsb[g * kGemvMaxRows + 4 * h]);
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
       expand_codes(dq[p].y, q + 4);
       expand_codes(dq[p].z, q + 8);
       expand_codes(dq[p].w, q + 12);
-      const float s = bf16_bits_to_f32(dsb[p] & 0xFFFFu), bp = bf16_bits_to_f32(dsb[p] >> 16) - 128.f * s;
+      const float s = f16_bits_to_f32(dsb[p] & 0xFFFFu), bp = f16_bits_to_f32(dsb[p] >> 16) - 128.f * s;
       for (int j = 0; j < rows; j++) {
         float d = 0.f;
 #pragma unroll
@@ -513,12 +513,12 @@ __device__ __forceinline__ f16x8_t dequant_f16(uint32_t d, f16x2b_t s2, f16x2b_t
                           __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q3, s2, b2))));
 }
 
-// Scale and bias of a block row as fp16 pairs; zero for padded groups (live = false).
+// Scale and bias of a block row (the blob's fp16 pair) broadcast to both
+// halves, as the grouped GEMM takes them; zero for padded groups (live = false).
 __device__ __forceinline__ void sb_f16(uint32_t sb, bool live, f16x2b_t& s2, f16x2b_t& b2) {
-  const uint32_t v = live ? sb : 0u;
-  const _Float16 sh = (_Float16)bf16_bits_to_f32(v & 0xFFFFu), bh = (_Float16)bf16_bits_to_f32(v >> 16);
-  s2 = f16x2b_t{sh, sh};
-  b2 = f16x2b_t{bh, bh};
+  const f16x2b_t v = __builtin_bit_cast(f16x2b_t, live ? sb : 0u);
+  s2 = __builtin_shufflevector(v, v, 0, 0);
+  b2 = __builtin_shufflevector(v, v, 1, 1);
 }
 
 __device__ __forceinline__ uint32_t dword_of(const uint4& v, int c) { return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w; }

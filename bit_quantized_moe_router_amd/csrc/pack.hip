@@ -1,8 +1,10 @@
 // Weight packer: canonical 4-bit codes + bf16 scale/bias -> the blob layout
 // described in common.h.  One workgroup of 256 threads writes one 1152-byte
 // block: thread j writes code dword j (lane j/4, dword j%4) and, for j < 32,
-// the scale/bias dword of row j.  Reads of the canonical rows are 4-byte
-// aligned because K is a multiple of 64.
+// the scale/bias dword of row j, both converted from bf16 to fp16 (round to
+// nearest even, the conversion every kernel would otherwise make on every
+// load).  Reads of the canonical rows are 4-byte aligned because K is a
+// multiple of 64.
 #include "launch.h"
 
 namespace moe {
@@ -40,7 +42,8 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs P) {
 
   if (j < kBlockRows) {
     const int64_t gi = ((int64_t)m * P.N + nb * kBlockRows + j) * G + g;
-    uint32_t sb = (uint32_t)P.scales[gi] | ((uint32_t)P.biases[gi] << 16);
+    const uint32_t sb = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(P.scales[gi])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(P.biases[gi])) << 16);
     reinterpret_cast<uint32_t*>(out + kCodeBytes)[j] = sb;
   }
 }

@@ -179,9 +179,13 @@ moe_status moe_max_tiles(const moe_layer_desc *desc, int32_t T, int32_t *n);
  * along the input dimension sharing one bf16 scale and one bf16 bias, w = s*q
  * + b ("Optimizing on-device inference for Apple Silicon", section
  * "Dequantise weights during matrix multiplication").  The blob is opaque and valid only for the desc that
- * made it.  It stores exactly the canonical codes, scales and biases (0.5625
- * bytes per parameter), rearranged so that one 64-lane wave reads a 32-row x
- * 64-column group with one 16-byte load per lane.  sh_* are ignored when
+ * made it.  It stores exactly the canonical codes (0.5625 bytes per parameter
+ * with the scales and biases), rearranged so that one 64-lane wave reads a
+ * 32-row x 64-column group with one 16-byte load per lane; the scales and
+ * biases are stored converted to fp16 (round to nearest even), the type the
+ * kernels rebuild weights in.  The conversion is exact for magnitudes in
+ * [2^-14, 65504]; smaller values lose bits as fp16 subnormals and larger
+ * ones become infinity, so the supported scale and bias range is fp16's.  sh_* are ignored when
  * shared_inter == 0.  One-time preparation; not part of the forward path.
  */
 moe_status moe_pack_weights(const moe_layer_desc *desc, moe_qmatrix gate, moe_qmatrix up,

@@ -94,6 +94,12 @@ def unpack_matrix(blob, base, N, K, stride_nb, stride_g, stride_blk=1152):
     return q, (sb & 0xFFFF).astype(np.uint16), (sb >> 16).astype(np.uint16)
 
 
+def bf16_as_f16_bits(a):
+    """The packer's conversion of bf16 scale/bias bits to fp16 bits (round to nearest even)."""
+    f = (np.asarray(a, np.uint32) << 16).view(np.float32)
+    return f.astype(np.float16).view(np.uint16)
+
+
 def canon_q(codes):
     q = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), np.uint8)
     q[..., 0::2] = codes & 15
@@ -116,15 +122,27 @@ def test_pack_roundtrip(M, name):
         for which, m in ((0, "gate"), (1, "up")):
             q, s, b = unpack_matrix(blob, e * ex + which * 1152, I, H, (H // 64) * 2 * 1152, 2 * 1152)
             assert np.array_equal(q, canon_q(w[m]["codes"][e])), (e, m)
-            assert np.array_equal(s, w[m]["scales"][e]) and np.array_equal(b, w[m]["biases"][e])
+            assert np.array_equal(s, bf16_as_f16_bits(w[m]["scales"][e]))
+            assert np.array_equal(b, bf16_as_f16_bits(w[m]["biases"][e]))
         q, s, b = unpack_matrix(blob, e * ex + gu, H, I, (I // 64) * 1152, 1152)
         assert np.array_equal(q, canon_q(w["down"]["codes"][e]))
-        assert np.array_equal(s, w["down"]["scales"][e]) and np.array_equal(b, w["down"]["biases"][e])
+        assert np.array_equal(s, bf16_as_f16_bits(w["down"]["scales"][e]))
+        assert np.array_equal(b, bf16_as_f16_bits(w["down"]["biases"][e]))
     sgu = (Is // 32) * (H // 64) * 2 * 1152
     q, s, b = unpack_matrix(blob, E * ex + 1152, Is, H, (H // 64) * 2 * 1152, 2 * 1152)
     assert np.array_equal(q, canon_q(w["sh_up"]["codes"][0]))
     q, s, b = unpack_matrix(blob, E * ex + sgu, H, Is, (Is // 64) * 1152, 1152)
-    assert np.array_equal(q, canon_q(w["sh_down"]["codes"][0])) and np.array_equal(b, w["sh_down"]["biases"][0])
+    assert np.array_equal(q, canon_q(w["sh_down"]["codes"][0]))
+    assert np.array_equal(b, bf16_as_f16_bits(w["sh_down"]["biases"][0]))
+    # In fp16's normal range the conversion is exact; below it (small biases)
+    # it is off by less than half the fp16 subnormal step, 2^-25.
+    for m in ("gate", "up", "down"):
+        for a in (w[m]["scales"], w[m]["biases"]):
+            f = (np.asarray(a, np.uint32) << 16).view(np.float32)
+            g = f.astype(np.float16).astype(np.float32)
+            normal = np.abs(f) >= 2.0 ** -14
+            assert np.array_equal(g[normal], f[normal])
+            assert np.all(np.abs(g - f) <= 2.0 ** -25)
 
 
 # ---- routing ------------------------------------------------------------------
