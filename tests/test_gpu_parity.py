@@ -376,14 +376,15 @@ def test_repeat_calls_bit_identical(M):
     assert torch.equal(d1, d2)
 
 
-@pytest.mark.parametrize("T", [1, 3])
-def test_decode_graph_replays_match_eager(M, T):
+@pytest.mark.parametrize("T,bi", [(1, 0), (3, 0), (2, 1)])
+def test_decode_graph_replays_match_eager(M, T, bi):
     """Decode captured in a HIP graph (the calls enqueue kernels only: no
     allocation, copy, memset or host synchronisation), replayed several times
     with other eager work in between; every replay equals the eager call on
-    the same rows bit for bit, and the oracle within tolerance."""
+    the same rows bit for bit, and the oracle within tolerance.  bi = 1: the
+    GEMV with the grouped GEMM's arithmetic."""
     case = mi.make_case("decode")
-    lay = get_layer(M, case)
+    lay = get_layer(M, case, batch_invariant=bi)
     H = case["cfg"]["H"]
     rows = [mi.gen_x(T, H, 9000 + r) for r in range(3)]
     eager = []
@@ -411,7 +412,7 @@ def test_decode_graph_replays_match_eager(M, T):
             lay.forward_decode(other, None)  # eager work between replays
             torch.cuda.synchronize()
     sub = dict(case, x=rows[-1], T=T)
-    check_close(y_static.cpu().numpy(), oracle_rows(sub), f"decode graph replay T={T}")
+    check_close(y_static.cpu().numpy(), oracle_rows(sub), f"decode graph replay T={T}" + (" batch-invariant" if bi else ""))
 
 
 @pytest.mark.parametrize("name", ["tiny", "prefill512"])

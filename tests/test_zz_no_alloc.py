@@ -37,8 +37,8 @@ def moe_static_limit():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("gemv", [8, 0])
-def test_static_decode_matches_workspace_decode(gemv):
+@pytest.mark.parametrize("gemv,bi", [(8, 0), (0, 0), (8, 1)])
+def test_static_decode_matches_workspace_decode(gemv, bi):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -47,6 +47,7 @@ def test_static_decode_matches_workspace_decode(gemv):
     case = mi.make_case("decode")
     H = case["cfg"]["H"]
     lay = MoELayer(case["w"], case["k"], device="cuda", max_tokens=8, gemv_max_rows=gemv)
+    lay.set_desc(batch_invariant=bi)  # 1: the GEMV with the grouped GEMM's arithmetic
     assert moe.moe_workspace_bytes(lay.desc, 8) <= moe_static_limit()
     rows = mi.gen_x(8, H, 5150 + gemv)
     xs = {8: to_dev(rows, "cuda"), 3: to_dev(rows[5:8], "cuda")}
@@ -59,11 +60,12 @@ def test_static_decode_matches_workspace_decode(gemv):
     for T in (8, 3):
         ref = lay.forward_decode(xs[T], None)
         torch.cuda.synchronize()
-        assert torch.equal(ys[T], ref), (gemv, T)
+        assert torch.equal(ys[T], ref), (gemv, bi, T)
     # And the oracle, within the layer tolerance, for the second (smaller) call.
     want, _ = orc.forward(case["w"], case["k"], rows[5:8], None, 2048, 64)
     got = ys[3].cpu().numpy().astype(np.float64)
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)
     mx = np.abs(got - want).max() / np.sqrt(np.mean(want ** 2))
-    print(f"[parity] static decode T=3 gemv_max_rows={gemv}: rel_l2={rel:.3e} max_abs/rms={mx:.3e}", flush=True)
+    print(f"[parity] static decode T=3 gemv_max_rows={gemv} batch_invariant={bi}: rel_l2={rel:.3e} "
+          f"max_abs/rms={mx:.3e}", flush=True)
     assert rel <= 5e-3 and mx <= 2e-2
