@@ -10,8 +10,9 @@ consecutive layers of a model would.  `--warmup` steps, then exactly
 `--steps` timed steps with nothing else enqueued and no kernel timing inside.
 
 Run order (one process):
- 1. the pages' two ablations against the headline in alternating blocks of
-    steps, each step stamped by events, so the legs share clock and thermal
+ 1. the pages' two ablations (host-synchronised routing, a separate dequant
+    pass) and their tile-height ablation (fixed tiles of 16, 32 or 64 rows)
+    against the headline in alternating blocks of steps, each step stamped by events, so the legs share clock and thermal
     state; kept as raw samples, reported as p50 / p95 / mean per leg.  This
     also brings the device to the clocks it holds under this load;
  2. the headline: W warm-up steps, then K timed steps (the contract);
@@ -213,12 +214,19 @@ def main():
         print("counter pass done", flush=True)
         return
 
-    # The separate-dequant leg needs a larger workspace: sized once here.
+    # The separate-dequant and fixed-tile legs need larger workspaces: sized once here.
     set_all(dequant_pass=1)
     set_all(dequant_pass=0)
+    set_all(tile_rows=16)
+    set_all(tile_rows=0)
 
     # ---- 1. ablations in alternating blocks, per-step samples ----
-    legs = [("headline", {}), ("host_sync_routing", {"host_sync_routing": 1}), ("dequant_pass", {"dequant_pass": 1})]
+    # Fixed tiles of 16, 32 or 64 rows against the default (128-row tiles whose
+    # row fragments follow each expert's load, long ones cut): the pages' tile
+    # height ablation.  All legs give the same bits.
+    legs = [("headline", {}), ("host_sync_routing", {"host_sync_routing": 1}), ("dequant_pass", {"dequant_pass": 1}),
+            ("fixed_tiles_16", {"tile_rows": 16}), ("fixed_tiles_32", {"tile_rows": 32}),
+            ("fixed_tiles_64", {"tile_rows": 64})]
     samples = {name: [] for name, _ in legs}
     B = a.ablation_block
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(B + 1)]
@@ -237,7 +245,7 @@ def main():
                 evs[j + 1].record(stream)
             torch.cuda.synchronize()
             samples[name] += [1000.0 * evs[j].elapsed_time(evs[j + 1]) for j in range(B)]
-            set_all(host_sync_routing=0, dequant_pass=0)
+            set_all(host_sync_routing=0, dequant_pass=0, tile_rows=0)
     leg_stats = {name: stats(v) for name, v in samples.items()}
     base50 = leg_stats["headline"]["p50"]
 
@@ -505,8 +513,11 @@ def main():
         "ablation_dequant_pass": dict(leg_stats["dequant_pass"],
                                       slowdown_p50=round(leg_stats["dequant_pass"]["p50"] / base50, 4),
                                       kernels_us=kern_dq),
-        "ablation_protocol": f"{a.ablation_rounds} rounds x 3 legs x {B} event-stamped steps, legs alternating, "
-                             "2 untimed steps after each switch; us per step",
+        "ablation_fixed_tiles": {str(bm): dict(leg_stats[f"fixed_tiles_{bm}"],
+                                               slowdown_p50=round(leg_stats[f"fixed_tiles_{bm}"]["p50"] / base50, 4))
+                                 for bm in (16, 32, 64)},
+        "ablation_protocol": f"{a.ablation_rounds} rounds x {len(legs)} legs x {B} event-stamped steps, legs "
+                             "alternating, 2 untimed steps after each switch; us per step",
         "prefill512": prefill512,
         "decode": {"us_per_layer": round(dec_us, 3), "T": 1, "cold_per_call_us": dec_cold,
                    "warm_us_per_layer": round(dec_warm_b2b, 3), "warm_per_call_us": dec_warm,

@@ -474,6 +474,20 @@ def test_batch_invariant_gemm_path_large_tiles(M):
             assert torch.equal(y[i], y_big[pos[i]]), (T, i)
 
 
+def test_fixed_tile_heights_same_bits(M):
+    """The tile-height ablation's legs compute the same layer: one skewed
+    2048-token chunk with the metadata's tiles fixed at 16, 32 or 64 rows gives
+    the bits of the default (128-row tiles with row fragments following each
+    expert's load, long tiles cut)."""
+    case = mi.make_case("prefill4096")
+    x, bias = dev(M, case["x"][:2048]), dev(M, case["bias"])
+    y0 = get_layer(M, case, max_tokens=2048).forward_prefill(x, bias).clone()
+    for bm in (16, 32, 64):
+        y = get_layer(M, case, max_tokens=2048, tile_rows=bm).forward_prefill(x, bias)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0), bm
+
+
 def test_batch_invariant_gemv_path(M):
     """Within the GEMV path a row's output does not depend on the other rows
     either (per-row dot products, fixed-order partial sums)."""
