@@ -165,6 +165,32 @@ def test_route_bitexact(M, name):
         check_route(r, ref, f"{name}[{c0}:]")
 
 
+@pytest.mark.parametrize("spread", [1e-7, 3e-3])
+def test_route_near_ties(M, spread):
+    """Router rows that all differ from one shared row by a relative `spread`:
+    every logit of a token lies within a few times the screen's error bound
+    of the others, so the exact step recomputes most or all experts (up to
+    256 candidates, ranked through LDS past 64) and must still give the
+    oracle's top-k exactly."""
+    case = mi.make_case("prefill512")
+    rng = np.random.default_rng(4711)
+    H, E = case["cfg"]["H"], case["cfg"]["E"]
+    base = rng.standard_normal(H).astype(np.float32) * np.float32(0.02)
+    wr = (base[None, :] * (1 + spread * rng.standard_normal((E, H)))).astype(np.float32)
+    w = dict(case["w"], router_w=wr)
+    lay = M.MoELayer(w, case["k"], max_tokens=256)
+    x = case["x"][:256]
+    r = lay.route(dev(M, x), None)
+    torch.cuda.synchronize()
+    ref = orc.route(x, wr, None, case["k"], lay.desc.tile_rows or 128)
+    logits = ref["logits"].astype(np.float64)
+    kth = -np.sort(-logits, axis=1)[:, case["k"] - 1]
+    close = (logits >= kth[:, None] - 1e-3).sum(axis=1)  # experts within 1e-3 of the k-th logit
+    print(f"[route] near ties spread={spread}: median experts within 1e-3 of the k-th: {int(np.median(close))}",
+          flush=True)
+    check_route(r, ref, f"near ties spread={spread}")
+
+
 @pytest.mark.parametrize("bm", [16, 32, 128])
 def test_route_tile_rows(M, bm):
     case = mi.make_case("prefill512")
