@@ -40,8 +40,9 @@
 // fp16 (11 significant bits instead of 8), which cuts the rounding error of
 // the rebuilt weights eightfold.  Activations enter as fp16(x / 256) (written
 // by the routing kernels) and the intermediate as fp16(h / 256); the power-of-
-// two scale is exact and keeps any bf16-sized value inside the fp16 range, and
-// the epilogues multiply it back.
+// two scale is exact, keeps magnitudes up to 65504 * 256 (about 1.7e7) inside
+// the fp16 range (larger ones become infinity; include/moe.h states this as
+// the supported activation range), and the epilogues multiply it back.
 //
 // MFMA 32x32x16 operand layout (wave64): lane l supplies row (A) / column (B)
 // l % 32 and eight consecutive k-slots 8*(l/32)..+7; the result holds column
