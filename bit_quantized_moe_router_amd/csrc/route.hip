@@ -672,13 +672,15 @@ __global__ __launch_bounds__(1024) void k_meta(const int32_t* __restrict__ ids, 
 // workgroups.  The flat assignment range is cut into segments of kSegAssign
 // ids, one 1024-thread workgroup each (16 waves x one chunk of 64).  The
 // per-(segment, expert) counts segcnt[seg][E] are already there (taken by the
-// exact top-k).  Every workgroup
+// exact top-k).  Every segment workgroup
 //  * sums the counts per expert and takes the expert offsets (the scans of
-//    meta_scan_tiles; workgroup 0 also writes counts, offsets, the active
-//    list, the tile map and the schedule);
+//    meta_scan_tiles);
 //  * bases its segment's experts at offset[e] + counts of e in earlier
 //    segments, then per wave from the wave counts;
 //  * scatters its segment stably with the leader atomics of meta_body.
+// One more workgroup (blockIdx.x == nseg) sums the counts and writes counts,
+// offsets, the active list, the tile map and the schedule, in parallel with
+// the scatter.
 // ---------------------------------------------------------------------------
 constexpr int kSegWaves = kSegAssign / 64;  // one chunk of 64 per wave
 
@@ -695,11 +697,12 @@ __global__ __launch_bounds__(1024) void k_meta_segments(const int32_t* __restric
   __shared__ int wc[kSegWaves][kMaxE];  // per-wave counts, then per-wave bases
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int seg = blockIdx.x, N = T * k;
+  const bool tiles_wg = seg == nseg;  // workgroup-uniform
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   // The segment's ids go out first.
   const int a = seg * kSegAssign + tid;
-  const int ev = a < N ? ids[a] : -1;
+  const int ev = !tiles_wg && a < N ? ids[a] : -1;
   int tot = 0, pre = 0;
   if (tid < E) {
     for (int g0 = 0; g0 < nseg; g0 += kScanBatch) {
@@ -713,9 +716,14 @@ __global__ __launch_bounds__(1024) void k_meta_segments(const int32_t* __restric
       }
     }
   }
+  if (tiles_wg) {
+    meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, true, counts, offsets, tiles, n_tiles, active, n_active,
+                    sched);
+    return;
+  }
   for (int i = tid; i < kSegWaves * E; i += blockDim.x) wc[i / E][i % E] = 0;
-  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, seg == 0, counts, offsets, tiles,
-                                    n_tiles, active, n_active, sched);
+  const int off_e = meta_scan_tiles(tot, T, k, E, BM, with_shared, max_long, false, counts, offsets, tiles, n_tiles,
+                                    active, n_active, sched);
   // (meta_scan_tiles ends with a barrier: wc is cleared.)
   __syncthreads();
   if (ev >= 0) atomicAdd(&wc[wave][ev], 1);
@@ -807,7 +815,7 @@ hipError_t launch_meta(const int32_t* ids, int T, int k, int E, int BM, int with
                counts, offsets, sorted, tiles, n_tiles, active, n_active, inv, sched);
     return hipGetLastError();
   }
-  MOE_LAUNCH(k_meta_segments, dim3(nseg), dim3(kSegAssign), 0, s, kt.start, kt.stop, ids, T, k, E, BM, with_shared,
+  MOE_LAUNCH(k_meta_segments, dim3(nseg + 1), dim3(kSegAssign), 0, s, kt.start, kt.stop, ids, T, k, E, BM, with_shared,
              max_long, nseg, segcnt, counts, offsets, sorted, inv, tiles, n_tiles, active, n_active, sched);
   return hipGetLastError();
 }
