@@ -61,9 +61,9 @@ constexpr int kScrRow = 144;                   // LDS bytes per row of one group
 constexpr int kScrBuf = 64 * kScrRow;          // one 64-row tile of one group
 constexpr int kScrSmem = 2 * 3 * kScrBuf;      // x, hi, lo; double buffered
 
-// LDS bytes of one k_route_exact workgroup: reduction slots, x row (bf16),
+// LDS bytes of one k_route_exact workgroup: reduction slots, x row (float64),
 // screened logits, candidate experts and logits (E each), selected logits (16).
-__host__ __device__ constexpr int route_exact_smem_bytes(int H, int E) { return 256 + H * 2 + E * 12 + 64; }
+__host__ __device__ constexpr int route_exact_smem_bytes(int H, int E) { return 256 + H * 8 + E * 12 + 64; }
 
 
 __global__ __launch_bounds__(256) void k_screen(const uint16_t* __restrict__ x, int T, int H,
@@ -228,8 +228,8 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
   const int t = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   double* red = reinterpret_cast<double*>(rsm);                 // [4 waves][3]
-  uint16_t* xl = reinterpret_cast<uint16_t*>(rsm + 256);
-  float* av = reinterpret_cast<float*>(rsm + 256 + H * 2);
+  double* xl = reinterpret_cast<double*>(rsm + 256);             // x row, widened once for every candidate
+  float* av = reinterpret_cast<float*>(rsm + 256 + H * 8);
   int* cand_e = reinterpret_cast<int*>(av + E);
   float* cand_v = reinterpret_cast<float*>(cand_e + E);
   float* sel_v = cand_v + E;
@@ -267,15 +267,15 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
     const int h = 8 * tid + 2048 * i;
     if (h < H) {  // H is a multiple of 64: a group of 8 threads is all in or all out
       const uint4 v = xv[i];
-      *reinterpret_cast<uint4*>(xl + h) = v;
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       uint32_t c[4];
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         c[j] = f32_to_f16_scaled(w[j] & 0xFFFFu) | ((uint32_t)f32_to_f16_scaled(w[j] >> 16) << 16);
-        const float f0 = bf16_bits_to_f32(w[j] & 0xFFFFu), f1 = bf16_bits_to_f32(w[j] >> 16);
-        xx = fma((double)f0, (double)f0, xx);
-        xx = fma((double)f1, (double)f1, xx);
+        const double f0 = (double)bf16_bits_to_f32(w[j] & 0xFFFFu), f1 = (double)bf16_bits_to_f32(w[j] >> 16);
+        *reinterpret_cast<double2*>(xl + h + 2 * j) = make_double2(f0, f1);
+        xx = fma(f0, f0, xx);
+        xx = fma(f1, f1, xx);
       }
       *reinterpret_cast<uint4*>(x16 + (int64_t)t * H + h) = make_uint4(c[0], c[1], c[2], c[3]);
     }
@@ -338,11 +338,12 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* __restrict_
 #pragma unroll 16
     for (int h = 4 * l32; h < H; h += 128) {
       const float4 w4 = *reinterpret_cast<const float4*>(wrow + h);
-      const uint2 xq = *reinterpret_cast<const uint2*>(xl + h);
-      acc = fma((double)bf16_bits_to_f32(xq.x & 0xFFFFu), (double)w4.x, acc);
-      acc = fma((double)bf16_bits_to_f32(xq.x >> 16), (double)w4.y, acc);
-      acc = fma((double)bf16_bits_to_f32(xq.y & 0xFFFFu), (double)w4.z, acc);
-      acc = fma((double)bf16_bits_to_f32(xq.y >> 16), (double)w4.w, acc);
+      const double2 x01 = *reinterpret_cast<const double2*>(xl + h);
+      const double2 x23 = *reinterpret_cast<const double2*>(xl + h + 2);
+      acc = fma(x01.x, (double)w4.x, acc);
+      acc = fma(x01.y, (double)w4.y, acc);
+      acc = fma(x23.x, (double)w4.z, acc);
+      acc = fma(x23.y, (double)w4.w, acc);
     }
     // Half-wave sum: the two rows of lanes of this half, (row sum) + (row sum).
     // Rows belong to one half whole, so the other half may be inactive here.
