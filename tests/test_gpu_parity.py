@@ -347,6 +347,7 @@ EDGE = [
     (9, 192, 1, 1, 128, 0, 31, None, 64, 32),   # one expert, no shared expert
     (50, 256, 32, 8, 192, 64, 51, 52, 2048, 64),  # k=8 of 32, I not a multiple of 128
     (5, 64, 4, 4, 64, 64, 61, None, 2, 16),     # k == E, tiny chunks
+    (300, 256, 32, 8, 64, 64, 91, 92, 2048, 128),  # 2400 assignments: three metadata segments, the last partial
 ]
 
 
