@@ -340,6 +340,19 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   // across the back edge instead of draining them at the loop header.
   const int Gp = (G + 3) & ~3;
   for (int g = 0; g < Gp; g += 4) {
+    if constexpr (kGateUp) {
+      // Issue priority by the work left, in quarters of the K loop.  Of two
+      // workgroups on a compute unit the older one otherwise wins every tie
+      // and the pair finishes far apart (full tiles: 52 and 67 us per
+      // 2048-token chunk); this way the one behind outranks the other, the
+      // pair ends closer together and the small tiles that follow start
+      // together.  (The down GEMM's loop, 8 groups, is too short for it.)
+      const int q = ((Gp - g) * 4 - 1) / Gp;  // 3 .. 0
+      if (q >= 3) __builtin_amdgcn_s_setprio(3);
+      else if (q == 2) __builtin_amdgcn_s_setprio(2);
+      else if (q == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     if constexpr (kPre) {  // two register sets: codes of g+2 into the set g used
       MOE_GEMM_STEP(g, 0, q0, q1, ao);
       MOE_GEMM_STEP(g + 1, 1, q1, q0, ae);
