@@ -139,7 +139,7 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   const int64_t dpart_bytes = (Td * k + Td) * (Im / 32) * H * 4;
   w.obuf = o;
   w.dpart = o;
-  o += al(Tc * k * H * 2 > dpart_bytes ? Tc * k * H * 2 : dpart_bytes);
+  o += al((Tc * k + Tc) * H * 2 > dpart_bytes ? (Tc * k + Tc) * H * 2 : dpart_bytes);
   // Separate-dequant measurement only: an fp16 copy of the blob's blocks.
   w.wdq = o;
   if (d->dequant_pass) o += al(blob_geom(d).total / kBlockBytes * kDqBlockBytes);

@@ -85,7 +85,7 @@ struct ChunkArgs {
   const int32_t* active;  // [E] experts with rows, increasing
   const int32_t* n_active;// [1]
   uint16_t* hbuf;         // [T*k + T][Imax]: fp16(h / 256), grouped-GEMM path
-  uint16_t* obuf;         // [T*k][H] GEMM path: fp16(routed expert output / 256) per sorted position
+  uint16_t* obuf;         // [T*k + T][H] GEMM path: fp16(expert output / 256), routed rows per sorted position, then the shared rows
   float* y;               // [T][H]
   int Imax;               // row stride of hbuf
 };

@@ -33,8 +33,8 @@
 // instead of rebuilding them from the codes.
 //
 // Results leave through LDS: the workgroup's output tile is assembled there
-// and written back as whole rows with 16-byte stores (the shared expert's
-// down rows, fp32, go straight to y).
+// and written back as whole rows with 16-byte stores (the down GEMM writes the
+// shared expert's rows into the same fp16 buffer, after the routed rows).
 //
 // Operand precision: the pages rebuild weights in bf16; here the operands are
 // fp16 (11 significant bits instead of 8), which cuts the rounding error of
@@ -370,27 +370,10 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
 #undef MOE_STORE_A
 
   // ---- epilogue (the last step ended with a barrier: LDS is free) ----
-  if (!kGateUp && T.shared) {
-    // Shared expert: y = 256 * acc in fp32, straight to memory.
-    if (!wave_cols) return;
-#pragma unroll
-    for (int f = 0; f < NF; f++) {
-#pragma unroll
-      for (int b = 0; b < 2; b++) {
-        if (b >= nvb) continue;
-        const int ocol = (nb0 + b) * 32 + col;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int r = f * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (r < T.rows) C.y[(int64_t)(T.r0 + r) * H + ocol] = 256.f * acc[f][b][i];
-        }
-      }
-    }
-    return;
-  }
-  // gate/up: fp16(silu(256 g) * 256 u / 256) into hbuf; down (routed rows):
-  // fp16(out / 256) into obuf, combined per token later (k_combine).  The
-  // tile is assembled in LDS, then stored row by row in 16-byte pieces.
+  // gate/up: fp16(silu(256 g) * 256 u / 256) into hbuf; down: fp16(out / 256)
+  // into obuf, routed and shared rows alike (the shared expert's rows after the
+  // routed ones), combined per token later (k_combine).  The tile is
+  // assembled in LDS, then stored row by row in 16-byte pieces.
   constexpr int kRowB = kGateUp ? kEpiRowGateUp : kEpiRowDown;
   if (wave_cols) {
 #pragma unroll
@@ -461,7 +444,7 @@ void k_expert_gemm(LayerArgs L, ChunkArgs C, int n_ct) {
     gemm_tile<kGateUp, 4, kPre>(L, C, T, smem);
 }
 
-// y[t] = (shared expert's output, already in y) + sum_j w_tj * 256 * obuf[pos(t, j)]
+// y[t] = 256 * obuf[T k + t] (the shared expert's row) + sum_j w_tj * 256 * obuf[pos(t, j)]
 // in top-k order.  One workgroup per token, 8 columns per thread.
 __global__ __launch_bounds__(256) void k_combine(LayerArgs L, ChunkArgs C) {
   const int t = blockIdx.x;
@@ -469,10 +452,14 @@ __global__ __launch_bounds__(256) void k_combine(LayerArgs L, ChunkArgs C) {
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
     float acc[8];
     if (L.Is > 0) {
-      const float4 a = *reinterpret_cast<const float4*>(C.y + (int64_t)t * H + c);
-      const float4 b = *reinterpret_cast<const float4*>(C.y + (int64_t)t * H + c + 4);
-      acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
-      acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
+      const uint4 o = *reinterpret_cast<const uint4*>(C.obuf + ((int64_t)C.Tk + t) * H + c);
+      const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const f16x2v_t p = __builtin_bit_cast(f16x2v_t, ow[i]);
+        acc[2 * i] = 256.f * (float)p.x;
+        acc[2 * i + 1] = 256.f * (float)p.y;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 8; i++) acc[i] = 0.f;

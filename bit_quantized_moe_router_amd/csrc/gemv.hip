@@ -469,8 +469,8 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4, 4
 //    padding of the group count to a multiple of 4 (zero weights, valid A);
 //    then silu(256 g) * 256 u rounded to fp16(h / 256);
 //  * down: the same chain over the intermediate's groups; routed outputs
-//    rounded to fp16(o / 256), the shared expert's output 256 * acc in fp32;
-//  * combine: y = shared + sum over j in top-k rank order of
+//    and the shared expert's output alike rounded to fp16(o / 256);
+//  * combine: y = 256 * shared + sum over j in top-k rank order of
 //    fma(256 w_tj, o_tj, y), the routing weights from the ranked top-k.
 // An MFMA output element depends only on its row of A and its column of B, so
 // which other rows share the A operand does not change it.
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kBiDnWaves * 64) void k_gemv_down_bi(LayerArgs L, C
   const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
   __shared__ uint16_t o16[16][32];  // routed outputs, fp16(o / 256)
-  __shared__ float ysh[32];         // shared expert's output, fp32
+  __shared__ float ysh[32];         // shared expert's output, 256 * fp16(o / 256)
   for (int j = wave; j < nrow; j += nwave) {  // wave-uniform
     const bool shared = j == k;
     const int a = shared ? Tk + t : t * k + j;  // the row of h
@@ -677,7 +677,7 @@ __global__ __launch_bounds__(kBiDnWaves * 64) void k_gemv_down_bi(LayerArgs L, C
     }
     // Row 0 of the result: register 0 of lanes 0..31 (column = lane).
     if (lane < 32) {
-      if (shared) ysh[lane] = 256.f * acc[0];
+      if (shared) ysh[lane] = 256.f * f16_bits_to_f32(to_f16_bits(acc[0]));
       else o16[j][lane] = to_f16_bits(acc[0]);
     }
   }
