@@ -6,19 +6,24 @@ chunks of 2048; H=2048, 256 experts top-8 + shared, I=512, 4-bit group-64
 weights, Zipf(1.1) logit bias).  Inputs are resident in HBM before the timed
 region.  Weight copies rotate every step (4 packed blobs, 1.8 GB, more than
 the 256 MB Infinity Cache) so each step reads its weights from HBM, as
-consecutive layers of a model would.  `--warmup` steps, then exactly
-`--steps` timed steps with nothing else enqueued and no kernel timing inside.
+consecutive layers of a model would.  Each layer's workspace holds two chunk
+areas, so the library runs the two chunks on two streams, both in flight.
+`--warmup` steps, then exactly `--steps` timed steps with nothing else
+enqueued and no kernel timing inside.
 
 Run order (one process):
- 1. the pages' two ablations (host-synchronised routing, a separate dequant
-    pass) and their tile-height ablation (fixed tiles of 16, 32 or 64 rows)
-    against the headline in alternating blocks of steps, each step stamped by events, so the legs share clock and thermal
-    state; kept as raw samples, reported as p50 / p95 / mean per leg.  This
-    also brings the device to the clocks it holds under this load;
+ 1. one chunk at a time (the same layers over one chunk area), the pages' two
+    ablations (host-synchronised routing, a separate dequant pass; both run
+    one chunk at a time) and their tile-height ablation (fixed tiles of 16, 32
+    or 64 rows) against the headline in alternating blocks of steps, each step
+    stamped by events, so the legs share clock and thermal state; kept as raw
+    samples, reported as p50 / p95 / mean per leg.  This also brings the
+    device to the clocks it holds under this load;
  2. the headline: W warm-up steps, then K timed steps (the contract);
  3. the gate/up grouped GEMM event-stamped by its own dispatch over K more
-    steps: its average duration for `roofline`;
- 4. per-kernel averages, one extra pass per kernel;
+    steps run one chunk at a time, so that no other kernel shares the device
+    during a launch: its average duration for `roofline`;
+ 4. per-kernel averages, one extra pass per kernel, one chunk at a time;
  5. prefill of 512 tokens (near-uniform routing, every expert touched):
     tok/s and the share of 8 TB/s its algorithmic bytes reach;
  6. decode: cold (24 layer copies rotated, about 420 MB read between two
@@ -180,8 +185,10 @@ def main():
         lay.ws = torch.empty(moe.moe_workspace_bytes(lay.desc, max_tokens), dtype=torch.uint8, device=dev)
         return lay
 
-    layers = [MoELayer(w, k, device=dev, max_tokens=2048)]
-    layers += [clone_layer(layers[0], 2048) for _ in range(a.copies - 1)]
+    # Workspaces sized for the whole 4096-token call: two chunk areas, so the
+    # library keeps both 2048-token chunks in flight (one per stream).
+    layers = [MoELayer(w, k, device=dev, max_tokens=T)]
+    layers += [clone_layer(layers[0], T) for _ in range(a.copies - 1)]
     x = to_dev(case["x"], dev)
     bias = to_dev(case["bias"], dev)
     ys = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in layers]
@@ -189,6 +196,25 @@ def main():
     def step(i):
         lay = layers[i % len(layers)]
         lay.forward_prefill(x, bias, ys[i % len(layers)])
+
+    def one_chunk_views():
+        # The same layers over the first chunk area of their workspace only: the
+        # library then runs the chunks one after the other on the caller's
+        # stream (per-kernel timing of each kernel alone on the device).
+        out = []
+        for lay in layers:
+            v = MoELayer.__new__(MoELayer)
+            v.__dict__.update(lay.__dict__)
+            v.desc = moe.make_desc(lay.H, lay.E, lay.k, lay.I, lay.Is)
+            v.max_tokens = 2048
+            v.ws = lay.ws[:moe.moe_workspace_bytes(v.desc, 2048)]
+            out.append(v)
+        return out
+
+    serial = one_chunk_views()
+
+    def step_serial(i):
+        serial[i % len(serial)].forward_prefill(x, bias, ys[i % len(serial)])
 
     def set_all(**kw):
         for lay in layers:
@@ -198,7 +224,7 @@ def main():
         # 4 prefill T=4096 steps (8 chunks), 8 prefill T=512 calls, 16 cold
         # decode T=1 calls, then copies of known size.
         for i in range(4):
-            step(i)
+            step_serial(i)
         x512 = to_dev(mi.make_case("prefill512")["x"], dev)
         for i in range(8):
             layers[i % len(layers)].forward_prefill(x512, None, ys[0][:512])
@@ -219,28 +245,33 @@ def main():
     set_all(dequant_pass=0)
     set_all(tile_rows=16)
     set_all(tile_rows=0)
+    serial = one_chunk_views()
 
     # ---- 1. ablations in alternating blocks, per-step samples ----
-    # Fixed tiles of 16, 32 or 64 rows against the default (128-row tiles whose
+    # One chunk at a time (the workspace's first chunk area only) against two
+    # in flight; host-synchronised routing and the separate dequant pass (both
+    # one chunk at a time by construction, so also compared with that leg);
+    # fixed tiles of 16, 32 or 64 rows against the default (128-row tiles whose
     # row fragments follow each expert's load, long ones cut): the pages' tile
     # height ablation.  All legs give the same bits.
-    legs = [("headline", {}), ("host_sync_routing", {"host_sync_routing": 1}), ("dequant_pass", {"dequant_pass": 1}),
-            ("fixed_tiles_16", {"tile_rows": 16}), ("fixed_tiles_32", {"tile_rows": 32}),
-            ("fixed_tiles_64", {"tile_rows": 64})]
-    samples = {name: [] for name, _ in legs}
+    legs = [("headline", {}, step), ("serial_chunks", {}, step_serial),
+            ("host_sync_routing", {"host_sync_routing": 1}, step), ("dequant_pass", {"dequant_pass": 1}, step),
+            ("fixed_tiles_16", {"tile_rows": 16}, step), ("fixed_tiles_32", {"tile_rows": 32}, step),
+            ("fixed_tiles_64", {"tile_rows": 64}, step)]
+    samples = {name: [] for name, _, _ in legs}
     B = a.ablation_block
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(B + 1)]
     it = 0
     for rnd in range(a.ablation_rounds):
-        for name, kw in legs:
+        for name, kw, fn in legs:
             set_all(**kw)
             for _ in range(2):  # untimed: the first step after a switch
-                step(it)
+                fn(it)
                 it += 1
             torch.cuda.synchronize()
             evs[0].record(stream)
             for j in range(B):
-                step(it)
+                fn(it)
                 it += 1
                 evs[j + 1].record(stream)
             torch.cuda.synchronize()
@@ -248,6 +279,7 @@ def main():
             set_all(host_sync_routing=0, dequant_pass=0, tile_rows=0)
     leg_stats = {name: stats(v) for name, v in samples.items()}
     base50 = leg_stats["headline"]["p50"]
+    serial50 = leg_stats["serial_chunks"]["p50"]
 
     # ---- 2. the headline: W warm-up steps, then exactly K timed steps ----
     for i in range(a.warmup):
@@ -264,11 +296,12 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms_per_step = e0.elapsed_time(e1) / a.steps
 
-    # ---- 3. the gate/up grouped GEMM stamped by its own dispatch ----
+    # ---- 3. the gate/up grouped GEMM stamped by its own dispatch, alone on
+    # the device (chunks one at a time, so no other kernel shares its time) ----
     moe.moe_profile_reset()
     moe.moe_profile_enable(1 << moe.K_GATEUP_GEMM)
     for i in range(a.steps):
-        step(i)
+        step_serial(i)
     torch.cuda.synchronize()
     moe.moe_profile_enable(0)
     tot, n = moe.moe_profile_read(moe.K_GATEUP_GEMM)
@@ -290,11 +323,12 @@ def main():
 
     def prefill_pass():
         for i in range(a.steps):
-            step(i)
+            step_serial(i)
 
     kern_all = breakdown(prefill_pass, [moe.K_LOGITS, moe.K_TOPK, moe.K_META, moe.K_DOWN_GEMM, moe.K_COMBINE])
     set_all(dequant_pass=1)
-    kern_dq = breakdown(prefill_pass, [moe.K_DEQUANT, moe.K_GATEUP_GEMM, moe.K_DOWN_GEMM])
+    # (the separate dequant pass always runs one chunk at a time)
+    kern_dq = breakdown(lambda: [step(i) for i in range(a.steps)], [moe.K_DEQUANT, moe.K_GATEUP_GEMM, moe.K_DOWN_GEMM])
     set_all(dequant_pass=0)
 
     Tc = 2048
@@ -508,10 +542,15 @@ def main():
         "headline_samples_us_per_step": leg_stats["headline"],
         "kernels_us": dict(kern, **kern_all),
         "down_gemm_tflops": round(down_tf, 2),
+        "ablation_serial_chunks": dict(leg_stats["serial_chunks"],
+                                       slowdown_p50=round(leg_stats["serial_chunks"]["p50"] / base50, 4)),
         "ablation_host_sync_routing": dict(leg_stats["host_sync_routing"],
-                                           slowdown_p50=round(leg_stats["host_sync_routing"]["p50"] / base50, 4)),
+                                           slowdown_p50=round(leg_stats["host_sync_routing"]["p50"] / base50, 4),
+                                           slowdown_vs_serial_chunks_p50=round(
+                                               leg_stats["host_sync_routing"]["p50"] / serial50, 4)),
         "ablation_dequant_pass": dict(leg_stats["dequant_pass"],
                                       slowdown_p50=round(leg_stats["dequant_pass"]["p50"] / base50, 4),
+                                      slowdown_vs_serial_chunks_p50=round(leg_stats["dequant_pass"]["p50"] / serial50, 4),
                                       kernels_us=kern_dq),
         "ablation_fixed_tiles": {str(bm): dict(leg_stats[f"fixed_tiles_{bm}"],
                                                slowdown_p50=round(leg_stats[f"fixed_tiles_{bm}"]["p50"] / base50, 4))

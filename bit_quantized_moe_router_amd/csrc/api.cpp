@@ -106,12 +106,18 @@ Blob blob_geom(const moe_layer_desc* d) {
 struct Ws {
   size_t logits, wnorm, xsum, x16, ids, tw, counts, offsets, sorted, inv, tiles, sched, n_tiles, active, n_active, segs,
       hbuf, obuf, dpart, wdq;
+  size_t span;     // bytes of one chunk's area (logits .. obuf)
+  int areas;       // 1, or 2: a second chunk area follows the first
   size_t total;
 };
 
 size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
-Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
+// Workspace of one chunk: routing outputs, gathered activations and the
+// GEMMs' intermediates.  With areas = 2 it is there twice, so two chunks can
+// be in flight at once (one per stream).  Offsets are relative to an area's
+// base, except wdq's, which is relative to the workspace.
+Ws ws_layout(const moe_layer_desc* d, int64_t Tc, int areas = 1) {
   const int64_t E = d->n_experts, k = d->top_k, H = d->hidden, Im = imax(d);
   const int64_t rows = Tc * k + Tc;
   Ws w;
@@ -140,6 +146,9 @@ Ws ws_layout(const moe_layer_desc* d, int64_t Tc) {
   w.obuf = o;
   w.dpart = o;
   o += al((Tc * k + Tc) * H * 2 > dpart_bytes ? (Tc * k + Tc) * H * 2 : dpart_bytes);
+  w.span = o;
+  w.areas = areas;
+  o *= areas;
   // Separate-dequant measurement only: an fp16 copy of the blob's blocks.
   w.wdq = o;
   if (d->dequant_pass) o += al(blob_geom(d).total / kBlockBytes * kDqBlockBytes);
@@ -298,6 +307,8 @@ moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, const fl
   return MOE_OK;
 }
 
+void* area_base(void* ws, const Ws& w, int area) { return static_cast<char*>(ws) + (area ? w.span : 0); }
+
 RouteOut ws_route(void* ws, const Ws& w) {
   RouteOut o;
   o.logits = at<float>(ws, w.logits);
@@ -359,11 +370,10 @@ moe_status forward_checks(const moe_layer_desc* d, const void* packed, const flo
   return MOE_OK;
 }
 
-moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_t* x, int Tc,
-                      const float* wr, const float* bias, float* y, void* ws, const Ws& w, hipStream_t s) {
-  const RouteOut o = ws_route(ws, w);
-  TRY(run_route(d, x, Tc, wr, bias, o, s));
-  const ChunkArgs C = chunk_args(d, x, Tc, o, ws, w, y);
+// The GEMMs and the combine of one routed chunk, on stream s.
+moe_status chunk_gemms(const moe_layer_desc* d, const LayerArgs& L, const uint16_t* x, int Tc, const RouteOut& o,
+                       float* y, void* area, void* ws, const Ws& w, hipStream_t s) {
+  const ChunkArgs C = chunk_args(d, x, Tc, o, area, w, y);
   LayerArgs Lc = L;
   if (d->dequant_pass) {
     Lc.wdq = at<uint8_t>(ws, w.wdq);
@@ -383,6 +393,66 @@ moe_status gemm_chunk(const moe_layer_desc* d, const LayerArgs& L, const uint16_
   TRY(timed(3, s, "gate/up GEMM", [&](const KTime& kt) { return launch_gateup_gemm(Lc, C, mt, s, kt); }));
   TRY(timed(4, s, "down GEMM", [&](const KTime& kt) { return launch_down_gemm(Lc, C, mt, s, kt); }));
   TRY(timed(7, s, "combine", [&](const KTime& kt) { return launch_combine(Lc, C, s, kt); }));
+  return MOE_OK;
+}
+
+// ---- the second stream ----------------------------------------------------------
+// Per device, a second stream (non-blocking, default priority) that runs every
+// other chunk beside the caller's stream.  Events without timing order the two
+// streams; they come from a per-device pool and go back to it once every wait
+// on them is enqueued (a wait takes the event's state at the time it is
+// enqueued).
+std::mutex g_side_mu;
+hipStream_t g_side[64];
+std::vector<hipEvent_t> g_sync_pool[64];
+
+struct SyncEvents {
+  int dev = 0;
+  std::vector<hipEvent_t> used;
+  ~SyncEvents() {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    for (hipEvent_t e : used) g_sync_pool[dev].push_back(e);
+  }
+  moe_status get(hipEvent_t* out) {
+    {
+      std::lock_guard<std::mutex> lk(g_side_mu);
+      if (!g_sync_pool[dev].empty()) {
+        *out = g_sync_pool[dev].back();
+        g_sync_pool[dev].pop_back();
+        used.push_back(*out);
+        return MOE_OK;
+      }
+    }
+    hipError_t e = hipEventCreateWithFlags(out, hipEventDisableTiming);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+    used.push_back(*out);
+    return MOE_OK;
+  }
+  // Stream `waiter` waits for what is enqueued on `src` so far.
+  moe_status order(hipStream_t src, hipStream_t waiter) {
+    hipEvent_t ev = nullptr;
+    TRY(get(&ev));
+    hipError_t e = hipEventRecord(ev, src);
+    if (e == hipSuccess) e = hipStreamWaitEvent(waiter, ev, 0);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream ordering: %s", hipGetErrorString(e));
+    return MOE_OK;
+  }
+};
+
+moe_status side_stream(int* dev_out, hipStream_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  if (!g_side[dev]) {
+    hipStream_t st = nullptr;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+    g_side[dev] = st;
+  }
+  *dev_out = dev;
+  *out = g_side[dev];
   return MOE_OK;
 }
 
@@ -416,17 +486,103 @@ moe_status static_scratch(void** out) {
   return MOE_OK;
 }
 
-// The grouped GEMM path over T tokens, max_chunk tokens at a time; the
-// workspace is carved for one chunk and reused (launches are stream-ordered).
+// The grouped GEMM path over T tokens, max_chunk tokens at a time.  With one
+// chunk area in the workspace every chunk is routed and run on the caller's
+// stream, one after the other.  With two (and more than one chunk), chunks
+// alternate between the caller's stream (even chunks, area 0) and the second
+// stream (odd chunks, area 1), so two chunks are in flight at once: the
+// routing of one runs beside the other's GEMMs, and the GEMMs of both share
+// the device.  The tokens of different chunks are independent, so the only
+// orderings are the call's inputs before the second stream's work, each
+// stream's own order for the reuse of its area, and the second stream's work
+// joined to the caller's stream before the call returns.
 moe_status prefill_loop(const moe_layer_desc* d, const void* packed, const float* wr, const float* bias,
-                        const uint16_t* x, int T, float* y, void* ws, hipStream_t s) {
+                        const uint16_t* x, int T, float* y, void* ws, size_t ws_bytes, bool may_overlap,
+                        hipStream_t s) {
   const LayerArgs L = layer_args(d, packed);
-  const int chunk = d->max_chunk;
-  const Ws w = ws_layout(d, T < chunk ? T : chunk);
-  for (int c0 = 0; c0 < T; c0 += chunk) {
-    const int Tc = T - c0 < chunk ? T - c0 : chunk;
-    TRY(gemm_chunk(d, L, x + (int64_t)c0 * d->hidden, Tc, wr, bias, y + (int64_t)c0 * d->hidden, ws, w, s));
+  const int chunk = d->max_chunk, H = d->hidden;
+  const int nch = (T + chunk - 1) / chunk;
+  const int64_t Tc0 = T < chunk ? T : chunk;
+  auto rows = [&](int c) { return T - c * chunk < chunk ? T - c * chunk : chunk; };
+  const Ws w2 = ws_layout(d, Tc0, 2);
+  const bool two = nch > 1 && may_overlap && !d->host_sync_routing && !d->dequant_pass && ws_bytes >= w2.total;
+  if (!two) {
+    const Ws w = ws_layout(d, Tc0);
+    const RouteOut o = ws_route(ws, w);
+    for (int c = 0; c < nch; c++) {
+      const int64_t off = (int64_t)c * chunk * H;
+      TRY(run_route(d, x + off, rows(c), wr, bias, o, s));
+      TRY(chunk_gemms(d, L, x + off, rows(c), o, y + off, ws, ws, w, s));
+    }
+    return MOE_OK;
   }
+  int dev = 0;
+  hipStream_t side = nullptr;
+  TRY(side_stream(&dev, &side));
+  SyncEvents ev;
+  ev.dev = dev;
+  TRY(ev.order(s, side));  // the inputs and the workspace's previous users come first
+  auto body = [&]() -> moe_status {
+    for (int c = 0; c < nch; c++) {
+      hipStream_t st = c & 1 ? side : s;
+      void* area = area_base(ws, w2, c & 1);
+      const RouteOut o = ws_route(area, w2);
+      const int64_t off = (int64_t)c * chunk * H;
+      TRY(run_route(d, x + off, rows(c), wr, bias, o, st));
+      TRY(chunk_gemms(d, L, x + off, rows(c), o, y + off, area, ws, w2, st));
+    }
+    return MOE_OK;
+  };
+  const moe_status st = body();
+  if (st != MOE_OK) {
+    // Best effort, keeping the first error: leave nothing of the call unjoined.
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess) {
+      if (hipEventRecord(e, side) == hipSuccess) (void)hipStreamWaitEvent(s, e, 0);
+      (void)hipEventDestroy(e);
+    }
+    return st;
+  }
+  return ev.order(side, s);
+}
+
+// Decode after the argument checks; may_overlap is false for the
+// static-scratch entry point, which must not create the routing stream.
+moe_status decode_impl(const moe_layer_desc* desc, const void* packed, const float* router_w,
+                       const float* logit_bias, const uint16_t* x, int32_t T, float* y, void* ws, size_t ws_bytes,
+                       bool may_overlap, void* stream) {
+  // T > R* (and always T > 8, the GEMV's largest row count) takes the grouped-GEMM path.
+  const int R = desc->gemv_max_rows >= 0 ? desc->gemv_max_rows
+                : desc->batch_invariant ? kDefaultGemvMaxRowsBi : kDefaultGemvMaxRows;
+  const bool gemv = T <= R && T <= desc->max_chunk && (int64_t)T * desc->hidden <= 32768;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!gemv) return prefill_loop(desc, packed, router_w, logit_bias, x, T, y, ws, ws_bytes, may_overlap, s);
+  const LayerArgs L = layer_args(desc, packed);
+  const Ws w = ws_layout(desc, T);
+  const RouteOut o = ws_route(ws, w);
+  // Exact logits; then the top-k, gate/up and split down projection; then the
+  // fixed-order sum of the partial outputs.
+  bool two = false;
+  float* part = at<float>(ws, w.dpart);
+  TRY(timed(0, s, "router logits", [&](const KTime& kt) {
+    return launch_route_logits(x, T, desc->hidden, router_w, logit_bias, desc->n_experts, desc->top_k, o.logits,
+                               o.wsq, o.ids, o.tw, nullptr, nullptr, nullptr, s, &two, kt);
+  }));
+  const ChunkArgs C = chunk_args(desc, x, T, o, ws, w, y);
+  if (desc->batch_invariant) {
+    // The grouped-GEMM path's arithmetic: gate/up into fp16 h rows, then down + combine.
+    TRY(timed(5, s, "top-k + gate/up GEMV (grouped-GEMM arithmetic)", [&](const KTime& kt) {
+      return launch_gemv_gateup_bi(L, C, o.logits, C.hbuf, o.ids, o.tw, s, kt);
+    }));
+    TRY(timed(6, s, "down GEMV + combine (grouped-GEMM arithmetic)", [&](const KTime& kt) {
+      return launch_gemv_down_bi(L, C, C.hbuf, o.ids, o.tw, s, kt);
+    }));
+    return MOE_OK;
+  }
+  TRY(timed(5, s, "top-k + gate/up + split down GEMV", [&](const KTime& kt) {
+    return launch_gemv_experts(L, C, o.logits, part, s, kt);
+  }));
+  TRY(timed(6, s, "partial-output sum", [&](const KTime& kt) { return launch_gemv_reduce(L, C, part, s, kt); }));
   return MOE_OK;
 }
 
@@ -446,7 +602,8 @@ moe_status moe_workspace_bytes(const moe_layer_desc* desc, int32_t max_tokens, s
   if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is null");
   if (max_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "max_tokens must be >= 0");
   const int64_t Tc = max_tokens < desc->max_chunk ? max_tokens : desc->max_chunk;
-  *bytes = ws_layout(desc, Tc > 0 ? Tc : 1).total;
+  // Beyond one chunk, room for a second chunk area (two chunks in flight).
+  *bytes = ws_layout(desc, Tc > 0 ? Tc : 1, max_tokens > desc->max_chunk ? 2 : 1).total;
   return MOE_OK;
 }
 
@@ -529,7 +686,8 @@ moe_status moe_forward_prefill(const moe_layer_desc* desc, const void* packed, c
   TRY(forward_checks(desc, packed, router_w, x, T, y, ws, ws_bytes));
   if (T == 0) return MOE_OK;
   TRY(check_device());
-  return prefill_loop(desc, packed, router_w, logit_bias, x, T, y, ws, static_cast<hipStream_t>(stream));
+  return prefill_loop(desc, packed, router_w, logit_bias, x, T, y, ws, ws_bytes, true,
+                      static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, const float* router_w,
@@ -538,39 +696,7 @@ moe_status moe_forward_decode(const moe_layer_desc* desc, const void* packed, co
   TRY(forward_checks(desc, packed, router_w, x, T, y, ws, ws_bytes));
   if (T == 0) return MOE_OK;
   TRY(check_device());
-  // T > R* (and always T > 8, the GEMV's largest row count) takes the grouped-GEMM path.
-  const int R = desc->gemv_max_rows >= 0 ? desc->gemv_max_rows
-                : desc->batch_invariant ? kDefaultGemvMaxRowsBi : kDefaultGemvMaxRows;
-  const bool gemv = T <= R && T <= desc->max_chunk && (int64_t)T * desc->hidden <= 32768;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!gemv) return prefill_loop(desc, packed, router_w, logit_bias, x, T, y, ws, s);
-  const LayerArgs L = layer_args(desc, packed);
-  const Ws w = ws_layout(desc, T);
-  const RouteOut o = ws_route(ws, w);
-  // Exact logits; then the top-k, gate/up and split down projection; then the
-  // fixed-order sum of the partial outputs.
-  bool two = false;
-  float* part = at<float>(ws, w.dpart);
-  TRY(timed(0, s, "router logits", [&](const KTime& kt) {
-    return launch_route_logits(x, T, desc->hidden, router_w, logit_bias, desc->n_experts, desc->top_k, o.logits,
-                               o.wsq, o.ids, o.tw, nullptr, nullptr, nullptr, s, &two, kt);
-  }));
-  const ChunkArgs C = chunk_args(desc, x, T, o, ws, w, y);
-  if (desc->batch_invariant) {
-    // The grouped-GEMM path's arithmetic: gate/up into fp16 h rows, then down + combine.
-    TRY(timed(5, s, "top-k + gate/up GEMV (grouped-GEMM arithmetic)", [&](const KTime& kt) {
-      return launch_gemv_gateup_bi(L, C, o.logits, C.hbuf, o.ids, o.tw, s, kt);
-    }));
-    TRY(timed(6, s, "down GEMV + combine (grouped-GEMM arithmetic)", [&](const KTime& kt) {
-      return launch_gemv_down_bi(L, C, C.hbuf, o.ids, o.tw, s, kt);
-    }));
-    return MOE_OK;
-  }
-  TRY(timed(5, s, "top-k + gate/up + split down GEMV", [&](const KTime& kt) {
-    return launch_gemv_experts(L, C, o.logits, part, s, kt);
-  }));
-  TRY(timed(6, s, "partial-output sum", [&](const KTime& kt) { return launch_gemv_reduce(L, C, part, s, kt); }));
-  return MOE_OK;
+  return decode_impl(desc, packed, router_w, logit_bias, x, T, y, ws, ws_bytes, true, stream);
 }
 
 moe_status moe_forward_decode_static(const moe_layer_desc* desc, const void* packed, const float* router_w,
@@ -589,7 +715,8 @@ moe_status moe_forward_decode_static(const moe_layer_desc* desc, const void* pac
   TRY(check_device());
   void* ws = nullptr;
   TRY(static_scratch(&ws));
-  return moe_forward_decode(desc, packed, router_w, logit_bias, x, T, y, ws, kStaticScratchBytes, stream);
+  TRY(forward_checks(desc, packed, router_w, x, T, y, ws, kStaticScratchBytes));
+  return decode_impl(desc, packed, router_w, logit_bias, x, T, y, ws, kStaticScratchBytes, false, stream);
 }
 
 const char* moe_status_str(moe_status s) {

@@ -161,7 +161,12 @@ moe_status moe_packed_bytes(const moe_layer_desc *desc, size_t *bytes);
  * call (host output).  The workspace holds one chunk's routing metadata and
  * intermediates; prefill reuses it chunk after chunk, so its size is bounded
  * by max_chunk whatever T is ("Optimizing on-device inference for Apple
- * Silicon", section "Bound temporary memory with prompt chunking").
+ * Silicon", section "Bound temporary memory with prompt chunking").  For
+ * max_tokens > max_chunk the size includes a second routing area (about 18 MB
+ * at H=2048, E=256, k=8 and 2048-token chunks), with which the forward calls
+ * route the next chunk while the current one's GEMMs run; a workspace of the
+ * one-chunk size (moe_workspace_bytes(desc, min(T, max_chunk))) is still
+ * valid for any T and runs the chunks one after the other.
  * Host-only; no device access.
  */
 moe_status moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens, size_t *bytes);
@@ -221,6 +226,13 @@ moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
  *   packed  blob from moe_pack_weights
  *   y       [T][H] float (written, not accumulated)
  *   ws      at least moe_workspace_bytes(desc, min(T, max_chunk)) bytes
+ * With more than one chunk and a workspace of moe_workspace_bytes(desc, T)
+ * bytes, chunk c + 1 is routed on a second stream of the library's (one per
+ * device, created on first use, default priority) while chunk c's GEMMs run on
+ * `stream`; events order the two streams, and the call returns with all of its
+ * work joined to `stream`, so stream order holds for the caller as with one
+ * stream (also under graph capture of `stream`).  The result is the same bits
+ * either way.
  */
 moe_status moe_forward_prefill(const moe_layer_desc *desc, const void *packed,
                                const float *router_w, const float *logit_bias,

@@ -48,8 +48,9 @@ def test_workspace_and_tile_bounds():
     assert moe.moe_max_tiles(d, 1) == 1 + 8 + 1
     w1 = moe.moe_workspace_bytes(d, 1)
     w2 = moe.moe_workspace_bytes(d, 2048)
-    w3 = moe.moe_workspace_bytes(d, 4096)  # capped at max_chunk
-    assert 0 < w1 < w2 == w3
+    w3 = moe.moe_workspace_bytes(d, 4096)  # two chunk areas: two chunks in flight
+    w4 = moe.moe_workspace_bytes(d, 1 << 20)  # still bounded by max_chunk
+    assert 0 < w1 < w2 < w3 == w4 == 2 * w2
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -442,6 +442,60 @@ def test_decode_graph_replays_match_eager(M, T, bi):
     check_close(y_static.cpu().numpy(), oracle_rows(sub), f"decode graph replay T={T}" + (" batch-invariant" if bi else ""))
 
 
+def test_prefill4096_two_chunks_in_flight_same_bits(M):
+    """A workspace sized for the whole call (two chunk areas) runs the second
+    2048-token chunk on the library's second stream beside the first; the output
+    equals the one-area (serial) call bit for bit, and sampled rows match the
+    oracle."""
+    case = mi.make_case("prefill4096")
+    ser = get_layer(M, case)
+    two = get_layer(M, case, max_tokens=case["T"])
+    assert two.ws.numel() > ser.ws.numel()
+    x, b = dev(M, case["x"]), dev(M, case["bias"])
+    y0 = ser.forward_prefill(x, b).clone()
+    y1 = two.forward_prefill(x, b).clone()
+    y2 = two.forward_prefill(x, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    assert torch.equal(y1, y2)
+    toks = _sample_tokens(case, 40, seed=13)
+    check_close(y1.cpu().numpy()[toks], oracle_rows(case, toks), "prefill4096 two chunks in flight")
+
+
+@pytest.mark.parametrize("T,chunk", [(300, 64), (129, 64), (200, 100)])
+def test_two_chunks_in_flight_many_chunks(M, T, chunk):
+    """3-5 chunks, the last one ragged, alternating between the caller's stream
+    and the second stream (chunk c + 2 reuses chunk c's area on the same
+    stream).  Every row against the oracle, and the same bits as the serial
+    call; then the call captured in a HIP graph and replayed with eager work in
+    between, each replay equal to the eager result."""
+    case = mi.small_layer(T, 256, 32, 8, 128, 64, 71, 72)
+    ser = M.MoELayer(case["w"], 8, max_tokens=chunk, max_chunk=chunk)
+    two = M.MoELayer(case["w"], 8, max_tokens=T, max_chunk=chunk)
+    assert two.ws.numel() > ser.ws.numel()
+    x, b = dev(M, case["x"]), dev(M, case["bias"])
+    y0 = ser.forward_prefill(x, b).clone()
+    y1 = two.forward_prefill(x, b).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    check_close(y1.cpu().numpy(), oracle_rows(case, chunk=chunk), f"two chunks in flight T={T} chunk={chunk}")
+    x_static = x.clone()
+    y_static = torch.empty_like(y1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        two.forward_prefill(x_static, b, y_static)
+    other = dev(M, mi.gen_x(T, 256, 7300))
+    y_other = two.forward_prefill(other, b).clone()
+    for rep in range(3):
+        y_static.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_static, y1), rep
+        y_o = two.forward_prefill(other, b)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y_o, y_other), rep
+
+
 @pytest.mark.parametrize("name", ["tiny", "prefill512"])
 def test_host_sync_routing_same_result(M, name):
     """The host-synchronised routing measurement (schedule size read back,
