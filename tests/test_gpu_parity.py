@@ -496,6 +496,45 @@ def test_two_chunks_in_flight_many_chunks(M, T, chunk):
         assert torch.equal(y_o, y_other), rep
 
 
+def test_two_chunks_in_flight_from_two_threads(M):
+    """Two host threads, each with its own layer workspace and torch stream,
+    enqueue multi-chunk calls at the same time: they share the library's second
+    stream and event pool, and every output equals the one-chunk-at-a-time
+    result bit for bit."""
+    import threading
+    T, chunk = 300, 64
+    case = mi.small_layer(T, 256, 32, 8, 128, 64, 75, 76)
+    ser = M.MoELayer(case["w"], 8, max_tokens=chunk, max_chunk=chunk)
+    lays = [M.MoELayer(case["w"], 8, max_tokens=T, max_chunk=chunk) for _ in range(2)]
+    xs = [dev(M, mi.gen_x(T, 256, 7400 + i)) for i in range(2)]
+    b = dev(M, case["bias"])
+    refs = [ser.forward_prefill(x, b).clone() for x in xs]
+    torch.cuda.synchronize()
+    outs = [[None] * 6 for _ in range(2)]
+    errs = []
+
+    def work(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for r in range(6):
+                    outs[i][r] = lays[i].forward_prefill(xs[i], b).clone()
+            st.synchronize()
+        except Exception as e:  # reported below
+            errs.append(e)
+
+    th = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t_ in th:
+        t_.start()
+    for t_ in th:
+        t_.join()
+    torch.cuda.synchronize()
+    assert not errs, errs
+    for i in range(2):
+        for r in range(6):
+            assert torch.equal(outs[i][r], refs[i]), (i, r)
+
+
 @pytest.mark.parametrize("name", ["tiny", "prefill512"])
 def test_host_sync_routing_same_result(M, name):
     """The host-synchronised routing measurement (schedule size read back,
