@@ -232,7 +232,9 @@ moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
  * `stream`; events order the two streams, and the call returns with all of its
  * work joined to `stream`, so stream order holds for the caller as with one
  * stream (also under graph capture of `stream`).  The result is the same bits
- * either way.
+ * either way.  The second stream and its events are created by the first such
+ * call on a device; make that call outside graph capture, as HIP may refuse to
+ * create a stream while one is being captured.
  */
 moe_status moe_forward_prefill(const moe_layer_desc *desc, const void *packed,
                                const float *router_w, const float *logit_bias,
