@@ -87,8 +87,10 @@ def source_digest(names=None):
 
 
 def gemm_source_digest():
-    """Digest of the grouped GEMM's sources (the kernel file, then the header of shared device helpers)."""
-    return source_digest(["gemm.hip", "common.h"])
+    """Digest of the sources that decide the grouped GEMM's memory traffic: the
+    kernel file, the header of shared device helpers, and the routing kernels,
+    which build the schedule that places its tiles on the XCDs."""
+    return source_digest(["gemm.hip", "common.h", "route.hip"])
 
 
 def traffic_from_profile():

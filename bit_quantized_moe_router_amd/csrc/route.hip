@@ -422,8 +422,9 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
                                int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                int32_t* __restrict__ sched) {
-  __shared__ int s_incl[3][kMaxE];         // inclusive scans: rows, tiles, active
-  __shared__ int s_wtot[kMaxE / 64][3];    // per-wave totals of those scans
+  __shared__ int s_incl[4][kMaxE];         // inclusive scans: rows, tiles, active, full tiles
+  __shared__ int s_wtot[kMaxE / 64][4];    // per-wave totals of those scans
+  __shared__ int s_nfull;                  // entries of the full-tile bin
   __shared__ int s_pbin[kMaxTileRows + 1]; // schedule entries per row count, then their next slots
   __shared__ int s_keep[kMaxTileRows + 1]; // long tiles per row count that stay whole
   __shared__ int s_extra[kMaxTileRows + 1];// pieces of cut tiles per row count
@@ -438,19 +439,19 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     npart = nt - nfull;
   }
   const int nwe = (E + 63) / 64;  // waves that cover the experts
-  int sc[3] = {tot, nt, act};
+  int sc[4] = {tot, nt, act, nfull};
   if (wave < nwe) {
 #pragma unroll
-    for (int q = 0; q < 3; q++) sc[q] = wave_incl_scan(sc[q]);
+    for (int q = 0; q < 4; q++) sc[q] = wave_incl_scan(sc[q]);
     if (lane == 63) {
 #pragma unroll
-      for (int q = 0; q < 3; q++) s_wtot[wave][q] = sc[q];
+      for (int q = 0; q < 4; q++) s_wtot[wave][q] = sc[q];
     }
   }
   __syncthreads();
   if (tid < E) {
 #pragma unroll
-    for (int q = 0; q < 3; q++) {
+    for (int q = 0; q < 4; q++) {
       int base = 0;
       for (int w = 0; w < wave; w++) base += s_wtot[w][q];
       s_incl[q][tid] = sc[q] + base;
@@ -474,8 +475,12 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
   // the device's compute units), the others are cut into a BM/2-row piece and
   // the rest, so that no long tile starts after the first round.  Each entry
   // holds (expert, first row, rows, first row in sorted order); entry 0 holds
-  // the number of entries.  The order among pieces of equal size is
-  // arbitrary; it changes no result.
+  // the number of entries.  The GEMMs run entry s on XCD s % 8, so the full
+  // tiles that stay whole are placed in expert order as 8 contiguous runs,
+  // run x on the entries of XCD x: the row tiles of a large expert then share
+  // one XCD's L2 and its weights are fetched there once, not once per XCD.
+  // The order among other pieces of equal size is arbitrary; no order changes
+  // a result.
   const int sfull = with_shared ? T / BM : 0;
   const int spart = with_shared && T % BM ? T % BM : 0;  // rows of the shared expert's partial tile
   const int half = (sched && max_long > 0 && BM >= 64) ? BM / 2 : 0;
@@ -519,13 +524,31 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     const int ta = lane_value(ia, 63), tb = lane_value(ib, 63);
     if (ra >= 1) s_pbin[ra] = 1 + ia - fa;
     if (rb >= 1) s_pbin[rb] = 1 + ta + ib - fb;
+    if (lane == 0) s_nfull = fa;  // ra = BM: the full tiles kept whole
     if (lane == 0 && sched) reinterpret_cast<int4*>(sched)[0] = make_int4(ta + tb, 0, 0, 0);
   }
   __syncthreads();
-  // One tile of e (rows at r0, sorted-order row rb) into the schedule.
-  auto place = [&](int e, int r0, int rows, int rb) {
+  // Entry (0-based, after the header) of the q-th full tile kept whole: the
+  // bin's entries [b0, b0 + n) enumerated XCD by XCD (residue of the entry
+  // mod 8), each XCD's in increasing order.
+  auto full_slot = [&](int q) {
+    const int b0 = s_pbin[BM] - 1, n = s_nfull;
+    int Q = 0, f = 0, c = 0;
+    for (int x = 0; x < 8; x++) {
+      f = (x - b0 % 8 + 8) % 8;
+      c = f < n ? (n - f + 7) / 8 : 0;
+      if (q < Q + c) break;
+      Q += c;
+    }
+    return b0 + f + 8 * (q - Q);
+  };
+  // One tile of e (rows at r0, sorted-order row rb; q: its position among the
+  // full tiles in expert order, for a full tile) into the schedule.
+  auto place = [&](int e, int r0, int rows, int rb, int q) {
     int4* sc = reinterpret_cast<int4*>(sched);
-    if (half && rows > half && atomicSub(&s_keep[rows], 1) <= 0) {
+    if (rows == BM && q < s_nfull) {
+      sc[1 + full_slot(q)] = make_int4(e, r0, rows, rb);
+    } else if (half && rows > half && (rows == BM || atomicSub(&s_keep[rows], 1) <= 0)) {
       sc[atomicAdd(&s_pbin[half], 1)] = make_int4(e, r0, half, rb);
       sc[atomicAdd(&s_pbin[rows - half], 1)] = make_int4(e, r0 + half, rows - half, rb + half);
     } else {
@@ -548,7 +571,7 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     tiles[3 * j + 0] = e;
     tiles[3 * j + 1] = r * BM;
     tiles[3 * j + 2] = rows;
-    if (sched) place(e, r * BM, rows, off_e + r * BM);
+    if (sched) place(e, r * BM, rows, off_e + r * BM, (e ? s_incl[3][e - 1] : 0) + r);
   }
   const int nshared = with_shared ? (T + BM - 1) / BM : 0;
   for (int r = tid; r < nshared; r += blockDim.x) {
@@ -556,7 +579,7 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     tiles[3 * (routed_tiles + r) + 0] = E;
     tiles[3 * (routed_tiles + r) + 1] = r * BM;
     tiles[3 * (routed_tiles + r) + 2] = rows;
-    if (sched) place(E, r * BM, rows, T * k + r * BM);
+    if (sched) place(E, r * BM, rows, T * k + r * BM, s_incl[3][E - 1] + r);
   }
   if (tid == 0) {
     n_tiles[0] = routed_tiles + nshared;
