@@ -417,13 +417,13 @@ constexpr int kMetaBatch = 8;   // chunks per wave whose ids are loaded together
 // holds tot for expert e; every thread of the 1024-thread workgroup calls
 // this): counts, offsets, active list, tile map and execution schedule.
 // Returns thread e's offset (its expert's first sorted position).
-__device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_shared, int max_long, bool out,
+__device__ __forceinline__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_shared, int max_long, bool out,
                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                int32_t* __restrict__ sched) {
   __shared__ int s_incl[4][kMaxE];         // inclusive scans: rows, tiles, active, full tiles
-  __shared__ int s_wtot[kMaxE / 64][4];    // per-wave totals of those scans
+  __shared__ int s_wtot[kMaxE / 64][2];    // per-wave totals of the two packed scans
   __shared__ int s_nfull;                  // entries of the full-tile bin
   __shared__ int s_pbin[kMaxTileRows + 1]; // schedule entries per row count, then their next slots
   __shared__ int s_keep[kMaxTileRows + 1]; // long tiles per row count that stay whole
@@ -439,23 +439,30 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     npart = nt - nfull;
   }
   const int nwe = (E + 63) / 64;  // waves that cover the experts
-  int sc[4] = {tot, nt, act, nfull};
+  // Two packed scans carry the four: rows | active << 18 (rows <= 8192 * 16 =
+  // 2^17, active <= 512) and tiles | full tiles << 16 (each <= 8192 + 512),
+  // so no field's sum reaches the next field.
+  int sc[2] = {tot | (act << 18), nt | (nfull << 16)};
   if (wave < nwe) {
 #pragma unroll
-    for (int q = 0; q < 4; q++) sc[q] = wave_incl_scan(sc[q]);
+    for (int q = 0; q < 2; q++) sc[q] = wave_incl_scan(sc[q]);
     if (lane == 63) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) s_wtot[wave][q] = sc[q];
+      for (int q = 0; q < 2; q++) s_wtot[wave][q] = sc[q];
     }
   }
   __syncthreads();
   if (tid < E) {
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      int base = 0;
-      for (int w = 0; w < wave; w++) base += s_wtot[w][q];
-      s_incl[q][tid] = sc[q] + base;
+    int base0 = 0, base1 = 0;
+    for (int w = 0; w < wave; w++) {
+      base0 += s_wtot[w][0];
+      base1 += s_wtot[w][1];
     }
+    const int v0 = sc[0] + base0, v1 = sc[1] + base1;
+    s_incl[0][tid] = v0 & ((1 << 18) - 1);
+    s_incl[2][tid] = v0 >> 18;
+    s_incl[1][tid] = v1 & 0xFFFF;
+    s_incl[3][tid] = v1 >> 16;
   }
   __syncthreads();
   const int routed_tiles = s_incl[1][E - 1];
@@ -528,26 +535,15 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     if (lane == 0 && sched) reinterpret_cast<int4*>(sched)[0] = make_int4(ta + tb, 0, 0, 0);
   }
   __syncthreads();
-  // Entry (0-based, after the header) of the q-th full tile kept whole: the
-  // bin's entries [b0, b0 + n) enumerated XCD by XCD (residue of the entry
-  // mod 8), each XCD's in increasing order.
-  auto full_slot = [&](int q) {
-    const int b0 = s_pbin[BM] - 1, n = s_nfull;
-    int Q = 0, f = 0, c = 0;
-    for (int x = 0; x < 8; x++) {
-      f = (x - b0 % 8 + 8) % 8;
-      c = f < n ? (n - f + 7) / 8 : 0;
-      if (q < Q + c) break;
-      Q += c;
-    }
-    return b0 + f + 8 * (q - Q);
-  };
-  // One tile of e (rows at r0, sorted-order row rb; q: its position among the
-  // full tiles in expert order, for a full tile) into the schedule.
+  // Full tiles kept whole: the bin's entries [b0, b0 + n) as 8 runs, run i
+  // holding entries b0 + i + 8 j for j < n / 8 + (i < n % 8) (so each run is
+  // one XCD's, residue b0 + i mod 8) and, in expert order, the full tiles
+  // q = i n/8 + min(i, n%8) + j.  One thread per entry, so the writes are
+  // contiguous; the other tiles go through the bins' LDS counters.
   auto place = [&](int e, int r0, int rows, int rb, int q) {
     int4* sc = reinterpret_cast<int4*>(sched);
     if (rows == BM && q < s_nfull) {
-      sc[1 + full_slot(q)] = make_int4(e, r0, rows, rb);
+      // written by the entry loop below
     } else if (half && rows > half && (rows == BM || atomicSub(&s_keep[rows], 1) <= 0)) {
       sc[atomicAdd(&s_pbin[half], 1)] = make_int4(e, r0, half, rb);
       sc[atomicAdd(&s_pbin[rows - half], 1)] = make_int4(e, r0 + half, rows - half, rb + half);
@@ -580,6 +576,31 @@ __device__ int meta_scan_tiles(int tot, int T, int k, int E, int BM, int with_sh
     tiles[3 * (routed_tiles + r) + 1] = r * BM;
     tiles[3 * (routed_tiles + r) + 2] = rows;
     if (sched) place(E, r * BM, rows, T * k + r * BM, s_incl[3][E - 1] + r);
+  }
+  if (sched) {
+    const int b0 = s_pbin[BM] - 1, n = s_nfull, a = n >> 3, b = n & 7;
+    const int routed_full = s_incl[3][E - 1];
+    for (int d = tid; d < n; d += blockDim.x) {
+      const int i = d & 7, jj = d >> 3;  // entry b0 + d: run (d mod 8), its jj-th tile
+      const int q = i * a + min(i, b) + jj;
+      int e, r, rb;
+      if (q < routed_full) {
+        int lo = 0, hi = E - 1;  // the expert whose full tiles hold q
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_incl[3][mid] > q) hi = mid;
+          else lo = mid + 1;
+        }
+        e = lo;
+        r = q - (e ? s_incl[3][e - 1] : 0);
+        rb = (e ? s_incl[0][e - 1] : 0) + r * BM;  // the expert's first sorted row + the tile's
+      } else {
+        e = E;
+        r = q - routed_full;
+        rb = T * k + r * BM;
+      }
+      reinterpret_cast<int4*>(sched)[1 + b0 + d] = make_int4(e, r * BM, BM, rb);
+    }
   }
   if (tid == 0) {
     n_tiles[0] = routed_tiles + nshared;
