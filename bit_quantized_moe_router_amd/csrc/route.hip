@@ -538,12 +538,16 @@ __device__ __forceinline__ int meta_scan_tiles(int tot, int T, int k, int E, int
   // Full tiles kept whole: the bin's entries [b0, b0 + n) as 8 runs, run i
   // holding entries b0 + i + 8 j for j < n / 8 + (i < n % 8) (so each run is
   // one XCD's, residue b0 + i mod 8) and, in expert order, the full tiles
-  // q = i n/8 + min(i, n%8) + j.  One thread per entry, so the writes are
-  // contiguous; the other tiles go through the bins' LDS counters.
+  // q = i n/8 + min(i, n%8) + j.  The other tiles go through the bins' LDS
+  // counters.
   auto place = [&](int e, int r0, int rows, int rb, int q) {
     int4* sc = reinterpret_cast<int4*>(sched);
     if (rows == BM && q < s_nfull) {
-      // written by the entry loop below
+      const int b0 = s_pbin[BM] - 1, n = s_nfull, a = n >> 3, b = n & 7;
+      int i = 0;  // the run of q: run x starts at q = x a + min(x, b)
+#pragma unroll
+      for (int x = 1; x < 8; x++) i += q >= x * a + min(x, b) ? 1 : 0;
+      sc[1 + b0 + i + 8 * (q - i * a - min(i, b))] = make_int4(e, r0, rows, rb);
     } else if (half && rows > half && (rows == BM || atomicSub(&s_keep[rows], 1) <= 0)) {
       sc[atomicAdd(&s_pbin[half], 1)] = make_int4(e, r0, half, rb);
       sc[atomicAdd(&s_pbin[rows - half], 1)] = make_int4(e, r0 + half, rows - half, rb + half);
@@ -576,31 +580,6 @@ __device__ __forceinline__ int meta_scan_tiles(int tot, int T, int k, int E, int
     tiles[3 * (routed_tiles + r) + 1] = r * BM;
     tiles[3 * (routed_tiles + r) + 2] = rows;
     if (sched) place(E, r * BM, rows, T * k + r * BM, s_incl[3][E - 1] + r);
-  }
-  if (sched) {
-    const int b0 = s_pbin[BM] - 1, n = s_nfull, a = n >> 3, b = n & 7;
-    const int routed_full = s_incl[3][E - 1];
-    for (int d = tid; d < n; d += blockDim.x) {
-      const int i = d & 7, jj = d >> 3;  // entry b0 + d: run (d mod 8), its jj-th tile
-      const int q = i * a + min(i, b) + jj;
-      int e, r, rb;
-      if (q < routed_full) {
-        int lo = 0, hi = E - 1;  // the expert whose full tiles hold q
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (s_incl[3][mid] > q) hi = mid;
-          else lo = mid + 1;
-        }
-        e = lo;
-        r = q - (e ? s_incl[3][e - 1] : 0);
-        rb = (e ? s_incl[0][e - 1] : 0) + r * BM;  // the expert's first sorted row + the tile's
-      } else {
-        e = E;
-        r = q - routed_full;
-        rb = T * k + r * BM;
-      }
-      reinterpret_cast<int4*>(sched)[1 + b0 + d] = make_int4(e, r * BM, BM, rb);
-    }
   }
   if (tid == 0) {
     n_tiles[0] = routed_tiles + nshared;
