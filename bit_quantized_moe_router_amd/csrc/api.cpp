@@ -370,7 +370,7 @@ moe_status forward_checks(const moe_layer_desc* d, const void* packed, const flo
   return MOE_OK;
 }
 
-// The GEMMs and the combine of one routed chunk, on stream s.
+// The GEMMs of one routed chunk, on stream s (chunk_combine follows them).
 moe_status chunk_gemms(const moe_layer_desc* d, const LayerArgs& L, const uint16_t* x, int Tc, const RouteOut& o,
                        float* y, void* area, void* ws, const Ws& w, hipStream_t s) {
   const ChunkArgs C = chunk_args(d, x, Tc, o, area, w, y);
@@ -392,7 +392,14 @@ moe_status chunk_gemms(const moe_layer_desc* d, const LayerArgs& L, const uint16
   }
   TRY(timed(3, s, "gate/up GEMM", [&](const KTime& kt) { return launch_gateup_gemm(Lc, C, mt, s, kt); }));
   TRY(timed(4, s, "down GEMM", [&](const KTime& kt) { return launch_down_gemm(Lc, C, mt, s, kt); }));
-  TRY(timed(7, s, "combine", [&](const KTime& kt) { return launch_combine(Lc, C, s, kt); }));
+  return MOE_OK;
+}
+
+// The per-token combine of one chunk whose down GEMM is ordered before it on stream s.
+moe_status chunk_combine(const moe_layer_desc* d, const LayerArgs& L, const uint16_t* x, int Tc, const RouteOut& o,
+                         float* y, void* area, const Ws& w, hipStream_t s) {
+  const ChunkArgs C = chunk_args(d, x, Tc, o, area, w, y);
+  TRY(timed(7, s, "combine", [&](const KTime& kt) { return launch_combine(L, C, s, kt); }));
   return MOE_OK;
 }
 
@@ -513,6 +520,7 @@ moe_status prefill_loop(const moe_layer_desc* d, const void* packed, const float
       const int64_t off = (int64_t)c * chunk * H;
       TRY(run_route(d, x + off, rows(c), wr, bias, o, s));
       TRY(chunk_gemms(d, L, x + off, rows(c), o, y + off, ws, ws, w, s));
+      TRY(chunk_combine(d, L, x + off, rows(c), o, y + off, ws, w, s));
     }
     return MOE_OK;
   }
@@ -522,6 +530,12 @@ moe_status prefill_loop(const moe_layer_desc* d, const void* packed, const float
   SyncEvents ev;
   ev.dev = dev;
   TRY(ev.order(s, side));  // the inputs and the workspace's previous users come first
+  // When the last chunk runs on the second stream, its combine runs on the
+  // caller's stream after an event that follows that chunk's down GEMM: the
+  // wait then overlaps the other chunk's combine, and it orders all of the
+  // second stream's work before the call's end on the caller's stream, so no
+  // separate join is needed.
+  const bool last_on_side = (nch - 1) & 1;
   auto body = [&]() -> moe_status {
     for (int c = 0; c < nch; c++) {
       hipStream_t st = c & 1 ? side : s;
@@ -530,6 +544,12 @@ moe_status prefill_loop(const moe_layer_desc* d, const void* packed, const float
       const int64_t off = (int64_t)c * chunk * H;
       TRY(run_route(d, x + off, rows(c), wr, bias, o, st));
       TRY(chunk_gemms(d, L, x + off, rows(c), o, y + off, area, ws, w2, st));
+      hipStream_t cs = st;
+      if (c == nch - 1 && last_on_side) {
+        TRY(ev.order(side, s));
+        cs = s;
+      }
+      TRY(chunk_combine(d, L, x + off, rows(c), o, y + off, area, w2, cs));
     }
     return MOE_OK;
   };
@@ -543,7 +563,7 @@ moe_status prefill_loop(const moe_layer_desc* d, const void* packed, const float
     }
     return st;
   }
-  return ev.order(side, s);
+  return last_on_side ? MOE_OK : ev.order(side, s);
 }
 
 // Decode after the argument checks; may_overlap is false for the

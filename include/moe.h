@@ -227,9 +227,10 @@ moe_status moe_route(const moe_layer_desc *desc, const uint16_t *x, int32_t T,
  *   y       [T][H] float (written, not accumulated)
  *   ws      at least moe_workspace_bytes(desc, min(T, max_chunk)) bytes
  * With more than one chunk and a workspace of moe_workspace_bytes(desc, T)
- * bytes, chunk c + 1 is routed on a second stream of the library's (one per
- * device, created on first use, default priority) while chunk c's GEMMs run on
- * `stream`; events order the two streams, and the call returns with all of its
+ * bytes, two chunks are in flight at once: even chunks run on `stream` and odd
+ * chunks on a second stream of the library's (one per device, created on first
+ * use, default priority), except that the combine of a last odd chunk runs on
+ * `stream`.  Events order the two streams, and the call returns with all of its
  * work joined to `stream`, so stream order holds for the caller as with one
  * stream (also under graph capture of `stream`).  The result is the same bits
  * either way.  The second stream and its events are created by the first such
