@@ -89,7 +89,7 @@ int64_t max_sched_for(const moe_layer_desc* d, int64_t T) {
 }
 
 struct Blob {
-  int64_t expert_bytes, gateup_bytes, shared_base, shared_gateup_bytes, total;
+  int64_t expert_bytes, gateup_bytes, shared_base, shared_gateup_bytes, trailer, total;
 };
 
 Blob blob_geom(const moe_layer_desc* d) {
@@ -99,7 +99,8 @@ Blob blob_geom(const moe_layer_desc* d) {
   b.expert_bytes = b.gateup_bytes + (H / 32) * (I / 64) * kBlockBytes;
   b.shared_base = E * b.expert_bytes;
   b.shared_gateup_bytes = (Is / 32) * (H / 64) * 2 * kBlockBytes;
-  b.total = b.shared_base + (Is ? b.shared_gateup_bytes + (H / 32) * (Is / 64) * kBlockBytes : 0);
+  b.trailer = b.shared_base + (Is ? b.shared_gateup_bytes + (H / 32) * (Is / 64) * kBlockBytes : 0);
+  b.total = b.trailer + kTrailerBytes;
   return b;
 }
 
@@ -269,6 +270,7 @@ LayerArgs layer_args(const moe_layer_desc* d, const void* packed) {
   L.gateup_bytes = b.gateup_bytes;
   L.shared_base = b.shared_base;
   L.shared_gateup_bytes = b.shared_gateup_bytes;
+  L.small_scales = reinterpret_cast<const int32_t*>(L.blob + b.trailer);
   L.wdq = nullptr;
   return L;
 }
@@ -656,11 +658,16 @@ moe_status moe_pack_weights(const moe_layer_desc* desc, moe_qmatrix gate, moe_qm
   uint8_t* dst = static_cast<uint8_t*>(packed);
   auto pack = [&](const moe_qmatrix& m, int M, int N, int K, int64_t base, int64_t stride_m,
                   int64_t stride_nb, int64_t stride_g) -> moe_status {
-    PackArgs P{m.codes, m.scales, m.biases, dst, M, N, K, base, stride_m, stride_nb, stride_g};
+    PackArgs P{m.codes, m.scales, m.biases, dst, M, N, K, base, stride_m, stride_nb, stride_g,
+               reinterpret_cast<int32_t*>(dst + b.trailer)};
     hipError_t e = launch_pack(P, s);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
     return MOE_OK;
   };
+  {
+    hipError_t e = launch_pack_trailer(dst + b.trailer, s);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
+  }
   const int64_t gu_nb = (int64_t)(H / 64) * 2 * kBlockBytes, gu_g = 2 * kBlockBytes;
   TRY(pack(gate, E, I, H, 0, b.expert_bytes, gu_nb, gu_g));
   TRY(pack(up, E, I, H, kBlockBytes, b.expert_bytes, gu_nb, gu_g));

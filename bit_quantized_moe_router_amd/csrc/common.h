@@ -31,7 +31,10 @@
 //   gate/up block (nb, g, which) at ((nb * H/64 + g) * 2 + which) * 1152
 //   down block (nb, g)           at gateup_bytes + (nb * I/64 + g) * 1152
 // Routed experts follow each other with stride expert_bytes; the shared expert
-// (width Is) follows the last routed expert.
+// (width Is) follows the last routed expert.  A trailer of kTrailerBytes ends
+// the blob; its first int32 is 1 when every stored scale s has |s| < 2^-4
+// (the packer clears it otherwise), which lets the grouped GEMM rebuild
+// weights with the subnormal form (gemm.hip), and the rest is zero.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,6 +46,9 @@ constexpr int kGroup = 64;
 constexpr int kBlockRows = 32;
 constexpr int kCodeBytes = 1024;
 constexpr int kBlockBytes = 1152;
+constexpr int kTrailerBytes = 256;
+// fp16 bits of 2^-4: stored scales below it in magnitude allow the subnormal rebuild.
+constexpr uint32_t kSmallScaleBits = 0x2C00u;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -57,6 +63,7 @@ struct LayerArgs {
   int64_t gateup_bytes;         // routed gate/up region
   int64_t shared_base;          // byte offset of the shared expert
   int64_t shared_gateup_bytes;  // shared gate/up region
+  const int32_t* small_scales;  // the trailer's flag: 1 = every |s| < 2^-4
   // Separate-dequant measurement only (else null): fp16 weights, each 1152-byte
   // block of the blob expanded to 4096 bytes at the same block index; in a
   // block, the 8 weights of lane l for MFMA k-step c sit at c * 1024 + l * 16.

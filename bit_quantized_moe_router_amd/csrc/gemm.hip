@@ -19,7 +19,9 @@
 // so a wave loads its blocks with one 16-byte load per block and K group,
 // rebuilds w = s*q + b in registers (fp16, one rounding) and feeds them to the
 // MFMAs of the same group.  Codes are prefetched four groups ahead, starting
-// before the token indices of the tile are known.
+// before the token indices of the tile are known.  When the blob's trailer says
+// every scale is below 2^-4 in magnitude, the rebuild takes the subnormal form
+// (rebuild16_small), which gives the same bits with fewer instructions.
 //
 // Activations (gathered token rows for gate/up, the expert's contiguous rows
 // of the intermediate for down) are shared by the 4 waves through LDS: per K
@@ -106,6 +108,34 @@ __device__ __forceinline__ f16x8_t dequant8(uint32_t d, f16x2v_t s2, f16x2v_t b2
                           __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q3, s2, b2))));
 }
 
+// The same rebuild for two dwords of codes d0, d1 (one per weight block),
+// valid while |s| < 2^-4.  A nibble in bits 4..7 of an fp16 whose exponent
+// field is zero is the subnormal q * 2^-20, exact; with s20 = s * 2^20 (exact
+// in fp16 for |s| < 2^-4) one packed FMA forms s20 * (q * 2^-20) + b = s*q + b
+// exactly before its single rounding, so the result equals dequant8's bit for
+// bit.  Pair i sits in nibbles i and 4+i, so pair 1 is in place and pairs 0, 2
+// and 3 need shifts of 4 left, 4 right and 8 right; the shifts run on the two
+// dwords as one 64-bit value (a bit that crosses from one dword into the other
+// lands outside the mask), so 8 codes cost 1.5 shifts, 4 ANDs and 4 FMAs
+// instead of 13 instructions.
+__device__ __forceinline__ void rebuild16_small(uint32_t d0, uint32_t d1, f16x2v_t s0, f16x2v_t b0, f16x2v_t s1,
+                                                f16x2v_t b1, f16x8_t& o0, f16x8_t& o1) {
+  constexpr uint32_t m = 0x00F000F0u;
+  const uint64_t dd = ((uint64_t)d1 << 32) | d0;
+  uint64_t l4, r4, r8;
+  // One VALU op each (the compiler would split a 64-bit shift into two 32-bit ones).
+  asm("v_lshlrev_b64 %0, 4, %1" : "=v"(l4) : "v"(dd));
+  asm("v_lshrrev_b64 %0, 4, %1" : "=v"(r4) : "v"(dd));
+  asm("v_lshrrev_b64 %0, 8, %1" : "=v"(r8) : "v"(dd));
+  auto w2 = [](uint32_t v, f16x2v_t sc, f16x2v_t bc) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2v_t, v & m), sc, bc));
+  };
+  o0 = __builtin_bit_cast(f16x8_t, make_uint4(w2((uint32_t)l4, s0, b0), w2(d0, s0, b0), w2((uint32_t)r4, s0, b0),
+                                              w2((uint32_t)r8, s0, b0)));
+  o1 = __builtin_bit_cast(f16x8_t, make_uint4(w2((uint32_t)(l4 >> 32), s1, b1), w2(d1, s1, b1),
+                                              w2((uint32_t)(r4 >> 32), s1, b1), w2((uint32_t)(r8 >> 32), s1, b1)));
+}
+
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
@@ -128,7 +158,7 @@ struct Tile {
   bool shared;
 };
 
-template <bool kGateUp, int NF, bool kPre>
+template <bool kGateUp, int NF, bool kPre, bool kSmall>
 __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C, const Tile& T, uint8_t* smem) {
   const int H = L.H;
   const int G = T.G;
@@ -235,10 +265,21 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
   // Scale and bias of one block (the blob's fp16 pair) broadcast to both
   // halves, which the packed FMA takes by operand selection; zero (weights
   // rebuild to 0) for groups padded past G.
+  // With the subnormal rebuild the scale is taken times 2^20 (exact: |s| < 2^-4).
   auto sbpair = [&](uint32_t sb, bool live, f16x2v_t& s2, f16x2v_t& b2) {
-    const f16x2v_t v = __builtin_bit_cast(f16x2v_t, live ? sb : 0u);
+    f16x2v_t v = __builtin_bit_cast(f16x2v_t, live ? sb : 0u);
+    if constexpr (kSmall) v.x = __builtin_ldexpf16(v.x, 20);
     s2 = __builtin_shufflevector(v, v, 0, 0);
     b2 = __builtin_shufflevector(v, v, 1, 1);
+  };
+  auto rebuild2 = [&](uint32_t d0, uint32_t d1, f16x2v_t s0, f16x2v_t b0, f16x2v_t s1, f16x2v_t b1, f16x8_t& o0,
+                      f16x8_t& o1) {
+    if constexpr (kSmall) {
+      rebuild16_small(d0, d1, s0, b0, s1, b1, o0, o1);
+    } else {
+      o0 = dequant8(d0, s0, b0);
+      o1 = dequant8(d1, s1, b1);
+    }
   };
   // B operands of k-step 0 of the current group, rebuilt during the last
   // k-step of the previous group.
@@ -271,16 +312,14 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
           bn0 = __builtin_bit_cast(f16x8_t, q.b0[c + 1]);
           bn1 = __builtin_bit_cast(f16x8_t, q.b1[c + 1]);
         } else {
-          bn0 = dequant8(cw0[c + 1], s20, b20);
-          bn1 = dequant8(cw1[c + 1], s21, b21);
+          rebuild2(cw0[c + 1], cw1[c + 1], s20, b20, s21, b21, bn0, bn1);
         }
       } else {
         if constexpr (kPre) {
           bn0 = __builtin_bit_cast(f16x8_t, qn.b0[0]);
           bn1 = __builtin_bit_cast(f16x8_t, qn.b1[0]);
         } else {
-          bn0 = dequant8(qn.c0.x, n20, m20);
-          bn1 = dequant8(qn.c1.x, n21, m21);
+          rebuild2(qn.c0.x, qn.c1.x, n20, m20, n21, m21, bn0, bn1);
         }
       }
 #pragma unroll
@@ -329,8 +368,7 @@ __device__ __forceinline__ void gemm_tile(const LayerArgs& L, const ChunkArgs& C
       f16x2v_t s20, b20, s21, b21;
       sbpair(q0.s0, true, s20, b20);
       sbpair(q0.s1, true, s21, b21);
-      bc0 = dequant8(q0.c0.x, s20, b20);
-      bc1 = dequant8(q0.c1.x, s21, b21);
+      rebuild2(q0.c0.x, q0.c1.x, s20, b20, s21, b21, bc0, bc1);
     }
   }
   __syncthreads();
@@ -417,6 +455,7 @@ void k_expert_gemm(LayerArgs L, ChunkArgs C, int n_ct) {
   const int4* sc = reinterpret_cast<const int4*>(C.sched);
   const int nt = sc[0].x;
   const int4 d = sc[1 + (slot < nt ? slot : 0)];
+  const bool small_scales = !kPre && *L.small_scales != 0;
   if (slot >= nt) return;
   Tile T;
   T.e = d.x;
@@ -434,14 +473,25 @@ void k_expert_gemm(LayerArgs L, ChunkArgs C, int n_ct) {
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int nf = (T.rows + 31) >> 5;
-  if (nf <= 1)
-    gemm_tile<kGateUp, 1, kPre>(L, C, T, smem);
-  else if (nf == 2)
-    gemm_tile<kGateUp, 2, kPre>(L, C, T, smem);
-  else if (nf == 3)
-    gemm_tile<kGateUp, 3, kPre>(L, C, T, smem);
-  else
-    gemm_tile<kGateUp, 4, kPre>(L, C, T, smem);
+  if (kPre || !small_scales) {
+    if (nf <= 1)
+      gemm_tile<kGateUp, 1, kPre, false>(L, C, T, smem);
+    else if (nf == 2)
+      gemm_tile<kGateUp, 2, kPre, false>(L, C, T, smem);
+    else if (nf == 3)
+      gemm_tile<kGateUp, 3, kPre, false>(L, C, T, smem);
+    else
+      gemm_tile<kGateUp, 4, kPre, false>(L, C, T, smem);
+  } else if constexpr (!kPre) {
+    if (nf <= 1)
+      gemm_tile<kGateUp, 1, false, true>(L, C, T, smem);
+    else if (nf == 2)
+      gemm_tile<kGateUp, 2, false, true>(L, C, T, smem);
+    else if (nf == 3)
+      gemm_tile<kGateUp, 3, false, true>(L, C, T, smem);
+    else
+      gemm_tile<kGateUp, 4, false, true>(L, C, T, smem);
+  }
 }
 
 // y[t] = 256 * obuf[T k + t] (the shared expert's row) + sum_j w_tj * 256 * obuf[pos(t, j)]

@@ -53,9 +53,12 @@ struct PackArgs {
   int64_t stride_m;
   int64_t stride_nb;
   int64_t stride_g;
+  int32_t* small_scales;  // the blob trailer's flag, cleared by a scale with |s| >= 2^-4
 };
 
 hipError_t launch_pack(const PackArgs& P, hipStream_t s);
+// Writes the blob trailer (flag = 1, rest zero) before the matrices are packed.
+hipError_t launch_pack_trailer(uint8_t* trailer, hipStream_t s);
 // Router logits: exact float64 ones for T <= 8, otherwise bf16-MFMA screened
 // partial sums over 4 slices of h (and partial squared router row norms);
 // *two_launches tells which.

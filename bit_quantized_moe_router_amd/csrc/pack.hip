@@ -4,7 +4,8 @@
 // the scale/bias dword of row j, both converted from bf16 to fp16 (round to
 // nearest even, the conversion every kernel would otherwise make on every
 // load).  Reads of the canonical rows are 4-byte aligned because K is a
-// multiple of 64.
+// multiple of 64.  A scale of magnitude 2^-4 or more clears the trailer's flag
+// (common.h), which k_pack_trailer sets before the matrices are packed.
 #include "launch.h"
 
 namespace moe {
@@ -42,10 +43,22 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs P) {
 
   if (j < kBlockRows) {
     const int64_t gi = ((int64_t)m * P.N + nb * kBlockRows + j) * G + g;
-    const uint32_t sb = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(P.scales[gi])) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(P.biases[gi])) << 16);
+    const uint32_t s16 = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(P.scales[gi]));
+    const uint32_t sb = s16 | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(P.biases[gi])) << 16);
     reinterpret_cast<uint32_t*>(out + kCodeBytes)[j] = sb;
+    // Every writer stores the same 0, so the unordered stores need no atomics.
+    if ((s16 & 0x7FFFu) >= kSmallScaleBits) *P.small_scales = 0;
   }
+}
+
+__global__ __launch_bounds__(64) void k_pack_trailer(uint8_t* trailer) {
+  reinterpret_cast<int32_t*>(trailer)[threadIdx.x] = threadIdx.x == 0 ? 1 : 0;
+}
+
+hipError_t launch_pack_trailer(uint8_t* trailer, hipStream_t s) {
+  static_assert(kTrailerBytes == 64 * 4, "one int32 per thread");
+  k_pack_trailer<<<dim3(1), dim3(64), 0, s>>>(trailer);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const PackArgs& P, hipStream_t s) {

@@ -152,7 +152,8 @@ typedef struct {
  * Size in bytes of the packed weight blob for `desc` (host output): the
  * canonical 4-bit codes plus one bf16 scale and one bf16 bias per 64 weights,
  * 0.5625 bytes per parameter (the Laya page's quantisation section gives this
- * storage cost of the group-64 4-bit format).  Host-only; no device access.
+ * storage cost of the group-64 4-bit format), plus a 256-byte trailer (a flag
+ * the packer writes for the kernels).  Host-only; no device access.
  */
 moe_status moe_packed_bytes(const moe_layer_desc *desc, size_t *bytes);
 
@@ -190,7 +191,10 @@ moe_status moe_max_tiles(const moe_layer_desc *desc, int32_t T, int32_t *n);
  * biases are stored converted to fp16 (round to nearest even), the type the
  * kernels rebuild weights in.  The conversion is exact for magnitudes in
  * [2^-14, 65504]; smaller values lose bits as fp16 subnormals and larger
- * ones become infinity, so the supported scale and bias range is fp16's.  sh_* are ignored when
+ * ones become infinity, so the supported scale and bias range is fp16's.  The
+ * blob's last 256 bytes are a trailer whose first int32 the packer sets to 1
+ * when every scale is below 2^-4 in magnitude (0 otherwise); the grouped GEMM
+ * then rebuilds weights with fewer instructions, to the same bits.  sh_* are ignored when
  * shared_inter == 0.  One-time preparation; not part of the forward path.
  */
 moe_status moe_pack_weights(const moe_layer_desc *desc, moe_qmatrix gate, moe_qmatrix up,

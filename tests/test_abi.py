@@ -32,14 +32,17 @@ def _desc(**kw):
     return moe.make_desc(**base)
 
 
+TRAILER = 256  # the blob's last bytes: the small-scale flag of the grouped GEMM's rebuild
+
+
 def test_packed_bytes_is_0p5625_bytes_per_param():
     d = _desc()
     params = 3 * 2048 * 512 * (256 + 1)
-    assert moe.moe_packed_bytes(d) == params * 9 // 16 == 257 * 1769472
+    assert moe.moe_packed_bytes(d) == params * 9 // 16 + TRAILER == 257 * 1769472 + TRAILER
     d0 = _desc(shared_inter=0)
-    assert moe.moe_packed_bytes(d0) == 256 * 1769472
+    assert moe.moe_packed_bytes(d0) == 256 * 1769472 + TRAILER
     tiny = _desc(hidden=256, n_experts=16, top_k=2, inter=128, shared_inter=128)
-    assert moe.moe_packed_bytes(tiny) == 17 * 3 * 256 * 128 * 9 // 16
+    assert moe.moe_packed_bytes(tiny) == 17 * 3 * 256 * 128 * 9 // 16 + TRAILER
 
 
 def test_workspace_and_tile_bounds():

@@ -116,7 +116,10 @@ def test_pack_roundtrip(M, name):
     H, E, I, Is = w["H"], w["E"], w["I"], w["Is"]
     gu = (I // 32) * (H // 64) * 2 * 1152
     ex = gu + (H // 32) * (I // 64) * 1152
-    assert blob.size == E * ex + 3 * H * Is * 9 // 16
+    assert blob.size == E * ex + 3 * H * Is * 9 // 16 + 256
+    # The trailer: the small-scale flag (every scale of these layers is below 2^-4), then zeros.
+    trailer = blob[-256:].view(np.int32)
+    assert trailer[0] == 1 and not trailer[1:].any()
     experts = range(E) if E <= 16 else [0, 1, 77, E - 1]
     for e in experts:
         for which, m in ((0, "gate"), (1, "up")):
@@ -143,6 +146,50 @@ def test_pack_roundtrip(M, name):
             normal = np.abs(f) >= 2.0 ** -14
             assert np.array_equal(g[normal], f[normal])
             assert np.all(np.abs(g - f) <= 2.0 ** -25)
+
+
+def _with_scales_times(w, factor, mats=("gate", "up", "down")):
+    """A copy of layer weights with the listed matrices' scales multiplied by factor (bf16 bits)."""
+    w2 = dict(w)
+    for m in mats:
+        q = dict(w[m])
+        q["scales"] = mi.f32_to_bf16_bits(mi.bf16_bits_to_f32(q["scales"]) * factor)
+        w2[m] = q
+    return w2
+
+
+def test_pack_clears_small_scale_flag(M):
+    """A layer with scales of 2^-4 and more: the packer clears the trailer's
+    flag, the grouped GEMM rebuilds weights with the general form, and the
+    output matches the oracle."""
+    case = mi.small_layer(300, 256, 16, 4, 128, 128, 71, 72)
+    case["w"] = _with_scales_times(case["w"], 8.0, ("up", "down"))  # U(0.04, 0.16)
+    lay = M.MoELayer(case["w"], case["k"], max_tokens=300)
+    assert lay.packed[-256:].cpu().numpy().view(np.int32)[0] == 0
+    y = lay.forward_prefill(dev(M, case["x"]), dev(M, case["bias"]))
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), oracle_rows(case), "scales up to 0.16 (general rebuild)")
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 64), ("prefill4096", 2048)])
+def test_rebuild_forms_same_bits(M, name, T):
+    """The grouped GEMM's two weight rebuilds (the subnormal form taken when
+    every scale is below 2^-4, and the general form) give the same bits: the
+    same blob with its trailer flag cleared by hand takes the general form."""
+    case = mi.make_case(name)
+    lay = get_layer(M, case)
+    assert lay.packed[-256:].cpu().numpy().view(np.int32)[0] == 1
+    x, b = dev(M, case["x"])[:T].contiguous(), dev(M, case["bias"])
+    y_small = lay.forward_prefill(x, b).clone()
+    saved = lay.packed.clone()
+    try:
+        lay.packed[-256:-252].zero_()
+        y_general = lay.forward_prefill(x, b).clone()
+        torch.cuda.synchronize()
+    finally:
+        lay.packed.copy_(saved)
+        torch.cuda.synchronize()
+    assert torch.equal(y_small, y_general)
 
 
 # ---- routing ------------------------------------------------------------------
