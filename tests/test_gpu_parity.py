@@ -192,6 +192,39 @@ def test_rebuild_forms_same_bits(M, name, T):
     assert torch.equal(y_small, y_general)
 
 
+def test_rebuild_forms_same_bits_edge_scales(M):
+    """Scales at the edges of the subnormal rebuild's range (just below 2^-4,
+    negative, zero, fp16-subnormal after the packer's conversion) and biases of
+    many magnitudes: the packer keeps the small-scale flag, both rebuild forms
+    give the same bits, and the output matches the oracle."""
+    case = mi.small_layer(300, 256, 16, 4, 128, 128, 73, 74)
+    rng = np.random.default_rng(75)
+    edge = np.array([0.0625 - 2.0 ** -12, -(0.0625 - 2.0 ** -12), 0.0, 2.0 ** -15, -(2.0 ** -18), 2.0 ** -24,
+                     0.03, -0.011, 1e-4], np.float32)
+    w = dict(case["w"])
+    for m in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+        q = dict(w[m])
+        sc = mi.bf16_bits_to_f32(q["scales"]).copy()
+        pick = rng.random(sc.shape) < 0.5
+        sc[pick] = rng.choice(edge, size=int(pick.sum()))
+        q["scales"] = mi.f32_to_bf16_bits(sc)
+        bi = mi.bf16_bits_to_f32(q["biases"]).copy()
+        pick = rng.random(bi.shape) < 0.3
+        bi[pick] *= rng.choice(np.array([1e-5, 1e-3, 30.0, -30.0], np.float32), size=int(pick.sum()))
+        q["biases"] = mi.f32_to_bf16_bits(bi)
+        w[m] = q
+    case["w"] = w
+    lay = M.MoELayer(w, case["k"], max_tokens=300)
+    assert lay.packed[-256:].cpu().numpy().view(np.int32)[0] == 1
+    x, b = dev(M, case["x"]), dev(M, case["bias"])
+    y_small = lay.forward_prefill(x, b).clone()
+    lay.packed[-256:-252].zero_()
+    y_general = lay.forward_prefill(x, b).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y_small, y_general)
+    check_close(y_small.cpu().numpy(), oracle_rows(case), "edge scales (subnormal rebuild)")
+
+
 # ---- routing ------------------------------------------------------------------
 
 ROUTE_CASES = ["tiny", "decode", "smallrow2", "smallrow3", "smallrow4", "smallrow5", "smallrow8", "prefill512",
