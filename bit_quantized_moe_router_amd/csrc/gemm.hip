@@ -117,7 +117,9 @@ __device__ __forceinline__ f16x8_t dequant8(uint32_t d, f16x2v_t s2, f16x2v_t b2
 // and 3 need shifts of 4 left, 4 right and 8 right; the shifts run on the two
 // dwords as one 64-bit value (a bit that crosses from one dword into the other
 // lands outside the mask), so 8 codes cost 1.5 shifts, 4 ANDs and 4 FMAs
-// instead of 13 instructions.
+// instead of 13 instructions.  It needs fp16 subnormal inputs kept, not
+// flushed: the kernels run in the compiler's default fp16/fp64 denormal mode
+// (preserve), which a build that flushes fp16 denormals would break.
 __device__ __forceinline__ void rebuild16_small(uint32_t d0, uint32_t d1, f16x2v_t s0, f16x2v_t b0, f16x2v_t s1,
                                                 f16x2v_t b1, f16x8_t& o0, f16x8_t& o1) {
   constexpr uint32_t m = 0x00F000F0u;
