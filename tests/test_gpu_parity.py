@@ -419,6 +419,23 @@ def test_prefill_sampled_rows(M, name):
     check_close(yn[toks], oracle_rows(case, toks), f"{name} sampled {len(toks)} rows")
 
 
+def test_prefill_full_layer_ragged_second_chunk(M):
+    """The full-size layer at T = 2048 + 37: a whole 2048-token chunk and a
+    37-token chunk in flight together (the second on the library's stream).
+    Every token of the short chunk and a sample of the long one against the
+    oracle."""
+    base = mi.make_case("prefill4096")
+    T = mi.CHUNK + 37
+    case = dict(base, x=base["x"][:T], T=T)
+    lay = get_layer(M, base)
+    y = lay.forward_prefill(dev(M, case["x"]), dev(M, case["bias"]))
+    torch.cuda.synchronize()
+    yn = y.cpu().numpy()
+    assert yn.shape == (T, base["w"]["H"]) and np.all(np.isfinite(yn))
+    toks = np.union1d(_sample_tokens(case, 24, seed=11), np.arange(mi.CHUNK, T)).astype(np.int32)
+    check_close(yn[toks], oracle_rows(case, toks), f"prefill4096[:{T}] sampled {len(toks)} rows")
+
+
 # ---- edge cases -------------------------------------------------------------------
 
 EDGE = [
